@@ -1,0 +1,185 @@
+"""tree_verify_attn on the GPU against the oracle, within the stated
+tolerance (max |gpu - ref| / RMS(ref): 2e-2 for bf16, 1e-4 for fp32)."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import np64, rel_err, say, tol_for
+from oracle import attn as OA
+from oracle import mask as OM
+from synth import configs as CF
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def gpu_attn(lib, x, window=None, mask=None, out_dtype=None):
+    w = x.window if window is None else window
+    if mask is None:
+        parent = torch.from_numpy(x.trees.parent).to(DEV)
+        mask = lib.tree_mask_build(parent, x.ctx_len)
+    out = lib.tree_verify_attn(x.q, x.k_node, x.v_node, x.k_cache, x.v_cache, x.block_table,
+                               x.ctx_len, x.max_ctx_len, mask["anc"], mask["pos"], w, x.scale,
+                               out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, mask
+
+
+def gpu_attn_checked(lib, x, window):
+    """fp32 output for the tolerance check; for bf16 inputs also the bf16
+    output, which must be exactly the round-to-nearest-even of the fp32 one."""
+    out32, mask = gpu_attn(lib, x, window, out_dtype=torch.float32)
+    if x.q.dtype == torch.bfloat16:
+        out16, _ = gpu_attn(lib, x, window, mask)
+        assert out16.dtype == torch.bfloat16
+        assert torch.equal(out16, out32.to(torch.bfloat16))
+    return out32
+
+
+def oracle_full(x, window):
+    m = OM.tree_mask(x.trees.parent, x.ctx_len.cpu().numpy())
+    return OA.tree_attn(np64(x.q), np64(x.k_node), np64(x.v_node), np64(x.k_cache), np64(x.v_cache),
+                        x.block_table.cpu().numpy(), x.ctx_len.cpu().numpy(), m["vis"], m["pos"],
+                        window, x.scale)
+
+
+def make(config, device=DEV, **over):
+    c = CF.reduced(config, **over)
+    win = c.pop("windows")
+    c.pop("vocab")
+    return W.attn_inputs(config, device=device, **c), win
+
+
+def check_full(lib, x, window, tag):
+    say(f"attn {tag} B={x.B} N={x.N} Hq={x.Hq} Hkv={x.Hkv} D={x.D} W={window} "
+        f"ctx={x.ctx_len.cpu().tolist()}")
+    out = gpu_attn_checked(lib, x, window)
+    ref = oracle_full(x, window)
+    err = rel_err(np64(out), ref)
+    say(f"   err={err:.3e}")
+    assert err <= tol_for(x.q.dtype), err
+    return err
+
+
+def test_c1_full(lib):
+    x, wins = make(1)
+    check_full(lib, x, wins[0], "c1")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_dims_and_dtypes(lib, dtype, D):
+    x, _ = make(1, B=2, N=20, Hq=4, Hkv=2, D=D, ctx_lo=700, ctx_hi=2500, dtype=dtype)
+    for w in (0, 300):
+        check_full(lib, x, w, f"dims {dtype} D={D}")
+
+
+def test_c2_reduced(lib):
+    x, _ = make(2, B=2, ctx_lo=2000, ctx_hi=3100)
+    check_full(lib, x, 0, "c2-reduced")
+
+
+@pytest.mark.parametrize("window", [512, 0])
+def test_c3_reduced(lib, window):
+    x, _ = make(3, B=3, ctx_lo=600, ctx_hi=5000)
+    check_full(lib, x, window, "c3-reduced")
+
+
+def test_c4_reduced(lib):
+    x, _ = make(4, B=2, ctx_lo=1500, ctx_hi=2100, tree="ddtree")
+    check_full(lib, x, 0, "c4-reduced")
+
+
+@pytest.mark.parametrize("window", [1, 2, 5, 9, 16, 100])
+def test_windows(lib, window):
+    x, _ = make(3, B=2, N=24, ctx_lo=150, ctx_hi=300, Hq=4, Hkv=2, D=64, tree="random_parent",
+                dtype=torch.float32)
+    check_full(lib, x, window, "window")
+
+
+def test_window_one_is_own_value(lib):
+    x, _ = make(1, B=2, N=16, ctx_lo=40, ctx_hi=90)
+    out, _ = gpu_attn(lib, x, 1)
+    G = x.Hq // x.Hkv
+    for h in range(x.Hq):
+        assert torch.equal(out[:, :, h].cpu(), x.v_node[:, :, h // G].cpu())
+
+
+@pytest.mark.parametrize("tree,N", [("chain", 64), ("star", 64), ("random_parent", 1),
+                                    ("random_parent", 63), ("random_parent", 33)])
+def test_tree_shapes(lib, tree, N):
+    x, _ = make(1, B=2, N=N, Hq=4, Hkv=1, D=64, ctx_lo=17, ctx_hi=150, tree=tree, dtype=torch.bfloat16)
+    check_full(lib, x, 0, f"tree {tree}")
+    check_full(lib, x, 20, f"tree {tree}")
+
+
+def test_short_and_empty_context(lib):
+    """ctx 0 (nodes only), 1, 15, 16, 17: ragged page tails."""
+    trees = W.make_trees(50, "random_parent", 5, 12, 100)
+    x, _ = make(1, B=5, N=12, Hq=4, Hkv=2, D=64, trees=trees,
+                ctx_len=np.array([0, 1, 15, 16, 17], dtype=np.int32))
+    check_full(lib, x, 0, "short ctx")
+    check_full(lib, x, 3, "short ctx")
+
+
+def test_gqa_group_of_one_and_many(lib):
+    for Hq, Hkv in ((8, 8), (16, 1)):
+        x, _ = make(1, B=1, N=9, Hq=Hq, Hkv=Hkv, D=128, ctx_lo=300, ctx_hi=300, dtype=torch.bfloat16)
+        check_full(lib, x, 0, f"gqa {Hq}/{Hkv}")
+
+
+def test_deterministic(lib):
+    x, _ = make(3, B=2, ctx_lo=3000, ctx_hi=4000)
+    a, m = gpu_attn(lib, x, 0)
+    b, _ = gpu_attn(lib, x, 0, m)
+    assert torch.equal(a, b)
+
+
+def _sampled_check(lib, x, window, units, nodes):
+    """Oracle on sampled (sequence, kv head) units and nodes, fetching only
+    the pages those units read."""
+    out = gpu_attn_checked(lib, x, window)
+    m = OM.tree_mask(x.trees.parent, x.ctx_len.cpu().numpy())
+    G = x.Hq // x.Hkv
+    got_all, ref_all = [], []
+    for (b, g) in units:
+        ctx = int(x.ctx_len[b])
+        pages = x.block_table[b, :(ctx + 15) // 16].long()
+        kc = x.k_cache[pages, g].reshape(-1, x.D)[:ctx].double().cpu().numpy()
+        vc = x.v_cache[pages, g].reshape(-1, x.D)[:ctx].double().cpu().numpy()
+        ref = OA.tree_attn_group(np64(x.q[b, :, g * G:(g + 1) * G]), kc, vc, np64(x.k_node[b, :, g]),
+                                 np64(x.v_node[b, :, g]), m["vis"][b], m["pos"][b], window, x.scale,
+                                 nodes=nodes)
+        got = np64(out[b, :, g * G:(g + 1) * G])
+        got_all.append(got[nodes])
+        ref_all.append(ref[nodes])
+    err = rel_err(np.concatenate(got_all), np.concatenate(ref_all))
+    say(f"   sampled err={err:.3e}")
+    assert err <= tol_for(x.q.dtype), err
+    return err
+
+
+@pytest.mark.parametrize("window", [512, 0])
+def test_c3_full_size_sampled(lib, window):
+    """The mixed batch at full size (B=32, ctx in [1024, 32768]), in the launch
+    configuration the benchmark times; the oracle checks sampled units."""
+    x, _ = make(3, kv_on_device=True)
+    ctx = x.ctx_len.cpu().numpy()
+    rng = np.random.default_rng(8)
+    bs = [int(np.argmax(ctx)), int(np.argmin(ctx))] + rng.integers(0, x.B, size=2).tolist()
+    units = [(b, int(rng.integers(0, x.Hkv))) for b in bs]
+    say(f"attn c3 full W={window} units={units}")
+    _sampled_check(lib, x, window, units, nodes=[0, 7, 8, 19, 31])
+
+
+def test_c2_full_size_sampled(lib):
+    x, _ = make(2, kv_on_device=True)
+    say("attn c2 full")
+    _sampled_check(lib, x, 0, [(0, 0), (7, 7), (3, 4)], nodes=[0, 1, 5, 28, 31])
+
+
+def test_c4_full_size_sampled(lib):
+    x, _ = make(4, kv_on_device=True)
+    say("attn c4 full")
+    _sampled_check(lib, x, 0, [(0, 0), (63, 7)], nodes=[0, 1, 30, 63])

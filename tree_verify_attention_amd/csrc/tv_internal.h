@@ -1,0 +1,64 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tree_verify.h"
+
+namespace tv {
+
+// bf16 <-> fp32 (bf16 is carried as its 16 raw bits)
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// round to nearest, ties to even; NaN stays a (quiet) NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// 64-bit lane shuffle as two 32-bit ones
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = __shfl(static_cast<uint32_t>(v), src, 64);
+  uint32_t hi = __shfl(static_cast<uint32_t>(v >> 32), src, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// ---- launchers (one per kernel family); return the launch error
+hipError_t launch_mask(const int32_t* parent, const int32_t* depth_in, const int32_t* ctx_len,
+                       int B, int N, uint64_t* anc, int32_t* depth_out, int32_t* pos,
+                       float* dense_bias, int32_t* status, hipStream_t stream);
+
+hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void* logits, int B,
+                       int N, int V, tv_dtype dtype, int32_t* acc_tok, int32_t* acc_node,
+                       int32_t* num_acc, int32_t* argmax_ws, hipStream_t stream);
+
+struct AttnPlan {
+  int G;            // query heads per kv head
+  int rows;         // G * N query rows per (sequence, kv head)
+  int row_groups;   // ceil(rows / rows per workgroup)
+  int nsplit;       // maximum context splits per (sequence, kv head)
+  int split_tokens; // nominal tokens per split (multiple of the key tile)
+  size_t ws_bytes;  // partials
+};
+
+AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int window);
+
+hipError_t launch_attn(const AttnPlan& plan, const void* q, const void* k_node,
+                       const void* v_node, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int max_blocks, int num_blocks,
+                       const int32_t* ctx_len, int max_ctx_len, const uint64_t* anc,
+                       const int32_t* pos, int B, int N, int Hq, int Hkv, int D, int window,
+                       float scale, tv_dtype dtype, tv_dtype out_dtype, void* out, void* ws,
+                       hipStream_t stream);
+
+hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                      int H, int Dk, int Dv, tv_dtype dtype, tv_dtype out_dtype, void* out,
+                      hipStream_t stream);
+
+}  // namespace tv

@@ -1,0 +1,176 @@
+// Greedy tree walk with the bonus token.
+//
+// Serve-integration spec, sections "What's proven" and "3. Rejection
+// sampler: tree walk": from the root follow the child whose token equals the
+// target argmax at the current node, then emit the argmax where no child
+// matches.  Two kernels: a row argmax over the vocabulary (an HBM stream, one
+// workgroup per logits row), then one wave per tree that walks the parent
+// pointers (lane = node; a ballot finds the matching child each step).
+#include "tv_internal.h"
+
+namespace tv {
+
+namespace {
+
+constexpr int kArgmaxThreads = 256;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kUnroll = 4;
+
+struct Best {
+  float v;
+  int i;
+};
+
+// larger value wins; on equal values the lower index wins
+__device__ __forceinline__ Best better(Best a, Best b) {
+  return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+__device__ __forceinline__ Best wave_best(Best x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Best y;
+    y.v = __shfl_xor(x.v, off, 64);
+    y.i = __shfl_xor(x.i, off, 64);
+    x = better(x, y);
+  }
+  return x;
+}
+
+__device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T>
+__device__ __forceinline__ void scan_chunk(const u32x4_t& c, int first, Best& best) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo = __uint_as_float(w[k] << 16);
+      float hi = __uint_as_float(w[k] & 0xffff0000u);
+      if (lo > best.v) { best.v = lo; best.i = first + 2 * k; }
+      if (hi > best.v) { best.v = hi; best.i = first + 2 * k + 1; }
+    }
+  } else {
+    const float f[4] = {__uint_as_float(c[0]), __uint_as_float(c[1]), __uint_as_float(c[2]),
+                        __uint_as_float(c[3])};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (f[k] > best.v) { best.v = f[k]; best.i = first + k; }
+  }
+}
+
+// am[row] = argmax_v logits[row, v]; rows are V elements long.
+template <typename T>
+__global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const T* __restrict__ logits,
+                                                                int V, int32_t* __restrict__ am) {
+  const size_t row = blockIdx.x;
+  const T* p = logits + row * static_cast<size_t>(V);
+  const int tid = threadIdx.x;
+  // strict '>' while a thread scans increasing indices keeps its first maximum;
+  // the start value lets the first element (even -inf) win
+  Best best{-INFINITY, 0x7fffffff};
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
+  const bool vec = ((static_cast<size_t>(V) * sizeof(T)) % 16 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  if (vec) {
+    const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(p);
+    const int nchunk = V / E;
+    int c = tid;
+    for (; c + (kUnroll - 1) * kArgmaxThreads < nchunk; c += kUnroll * kArgmaxThreads) {
+      u32x4_t r[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) r[u] = __builtin_nontemporal_load(pc + c + u * kArgmaxThreads);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        Best cand{-INFINITY, 0x7fffffff};
+        scan_chunk<T>(r[u], (c + u * kArgmaxThreads) * E, cand);
+        best = better(best, cand);
+      }
+    }
+    for (; c < nchunk; c += kArgmaxThreads) {
+      Best cand{-INFINITY, 0x7fffffff};
+      scan_chunk<T>(pc[c], c * E, cand);
+      best = better(best, cand);
+    }
+  } else {
+    for (int v = tid; v < V; v += kArgmaxThreads) {
+      Best cand{load_elem(p, v), v};
+      best = better(best, cand);
+    }
+  }
+  // an all -inf chunk leaves its candidate index at the sentinel; -inf rows
+  // are outside the contract, so any in-range index is acceptable there
+  best = wave_best(best);
+  __shared__ float sv[kArgmaxThreads / 64];
+  __shared__ int si[kArgmaxThreads / 64];
+  const int w = tid / 64;
+  if ((tid & 63) == 0) { sv[w] = best.v; si[w] = best.i; }
+  __syncthreads();
+  if (tid == 0) {
+    Best r{sv[0], si[0]};
+    for (int k = 1; k < kArgmaxThreads / 64; ++k) r = better(r, Best{sv[k], si[k]});
+    if (r.i < 0 || r.i >= V) r.i = 0;
+    am[row] = r.i;
+  }
+}
+
+__global__ __launch_bounds__(64) void walk_kernel(const int32_t* __restrict__ tokens,
+                                                  const int32_t* __restrict__ parent,
+                                                  const int32_t* __restrict__ am, int N,
+                                                  int32_t* __restrict__ acc_tok,
+                                                  int32_t* __restrict__ acc_node,
+                                                  int32_t* __restrict__ num_acc) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const bool act = t < N;
+  const size_t base = static_cast<size_t>(b) * N;
+  const int tok = act ? tokens[base + t] : -1;
+  const int par = act ? parent[base + t] : -2;
+  const bool valid = act && par >= -1 && par < t;
+  const int32_t* amb = am + static_cast<size_t>(b) * (N + 1);
+
+  int cur = -1, row = 0, a = 0;
+  int my_node = -1, my_tok = -1;
+  int pred = amb[0];
+  // a matched child always has a larger index than its parent, so the walk
+  // ends within N steps
+  for (int step = 0; step < N; ++step) {
+    const uint64_t m = __ballot(valid && par == cur && tok == pred);
+    if (m == 0ull) break;
+    const int i = __ffsll(static_cast<unsigned long long>(m)) - 1;
+    if (t == a) { my_node = i; my_tok = pred; }
+    ++a;
+    cur = i;
+    row = 1 + i;
+    pred = amb[row];
+  }
+  // pred is now the bonus token (argmax at the last accepted node)
+  int32_t* ot = acc_tok + static_cast<size_t>(b) * (N + 1);
+  if (act) acc_node[base + t] = t < a ? my_node : -1;
+  if (t < N + 1) ot[t] = t < a ? my_tok : (t == a ? pred : -1);
+  if (t == 0 && N + 1 > 64) ot[64] = (64 == a) ? pred : -1;  // N == 64: slot 64
+  if (t == 0) num_acc[b] = a;
+}
+
+}  // namespace
+
+hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void* logits, int B,
+                       int N, int V, tv_dtype dtype, int32_t* acc_tok, int32_t* acc_node,
+                       int32_t* num_acc, int32_t* argmax_ws, hipStream_t stream) {
+  const unsigned rows = static_cast<unsigned>(B) * static_cast<unsigned>(N + 1);
+  if (dtype == TV_BF16)
+    hipLaunchKernelGGL(argmax_kernel<uint16_t>, dim3(rows), dim3(kArgmaxThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), V, argmax_ws);
+  else
+    hipLaunchKernelGGL(argmax_kernel<float>, dim3(rows), dim3(kArgmaxThreads), 0, stream,
+                       static_cast<const float*>(logits), V, argmax_ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(64), 0, stream, tokens, parent, argmax_ws, N,
+                     acc_tok, acc_node, num_acc);
+  return hipGetLastError();
+}
+
+}  // namespace tv
