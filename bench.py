@@ -1,0 +1,263 @@
+"""Benchmark of one tree-verify step on one MI355X.
+
+A step is one pass of the whole verify path over one batch: tree_mask_build,
+tree_verify_attn for a 512-token sliding-window layer and for a global layer,
+tree_walk_accept and tree_gdn_verify.  The batch is the mixed workload: 32
+sequences with context lengths uniform in [1024, 32768], random spine-first
+trees of N = 32 nodes (max depth 8), Hq = 16, Hkv = 8, D = 256, bf16, paged
+KV in 16-token pages under a random block table.  That workload states no
+vocabulary or GDN shape, so the walk runs over [32, 33, 262144] bf16 logits
+(the DDTree workload's vocabulary) and the GDN layer uses H = 16,
+Dk = Dv = 128 over the same trees.
+
+Prints one JSON line: verified tree nodes per second (B * N per step), the
+roofline of the dominant kernel (the global-layer attention: context K/V bytes
+over its event-timed duration against 8 TB/s) and the CPU oracle on a bounded
+sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch of the dominant kernel (rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+class Step:
+    """Inputs resident in HBM, preallocated outputs and workspaces."""
+
+    def __init__(self, dev):
+        import tree_verify_attention_amd as tv
+        from synth import configs as CF
+        from synth import workloads as W
+        self.tv = tv
+        tv.load()
+        c = dict(CF.ATTN[3])
+        wins = c.pop("windows")
+        c.pop("vocab")
+        self.B, self.N = c["B"], c["N"]
+        self.layers = []
+        trees = None
+        ctx = None
+        for li, w in enumerate(wins):
+            x = W.attn_inputs(3, device=dev, kv_on_device=True, layer=li, window=w,
+                              trees=trees, ctx_len=ctx, **c)
+            trees, ctx = x.trees, x.ctx_len.cpu().numpy()
+            self.layers.append(x)
+        self.trees = trees
+        self.parent = torch.from_numpy(trees.parent).to(dev)
+        self.tokens = torch.from_numpy(trees.tokens).to(dev)
+        self.ctx_len = self.layers[0].ctx_len
+        self.V = 262144
+        self.logits = W.walk_inputs(3, trees, self.V, torch.bfloat16, device=dev, on_device=True).logits
+        g = CF.GDN[5]
+        self.gdn = W.gdn_inputs(3, B=self.B, N=self.N, H=g["H"], Dk=g["Dk"], Dv=g["Dv"], tree="spine_first",
+                                dtype=torch.bfloat16, trees=trees, device=dev)
+        B, N = self.B, self.N
+        self.mask_out = dict(anc=torch.empty(B, N, dtype=torch.int64, device=dev),
+                             depth=torch.empty(B, N, dtype=torch.int32, device=dev),
+                             pos=torch.empty(B, N, dtype=torch.int32, device=dev),
+                             status=torch.empty(B, dtype=torch.int32, device=dev), dense_bias=None)
+        self.attn_out = [torch.empty_like(x.q) for x in self.layers]
+        self.attn_ws = []
+        for x in self.layers:
+            n = tv.tree_verify_attn_workspace_size(B, N, x.Hq, x.Hkv, x.D, x.max_ctx_len, x.window)
+            self.attn_ws.append(torch.empty(max(n, 1), dtype=torch.uint8, device=dev))
+        self.walk_out = dict(accepted_tokens=torch.empty(B, N + 1, dtype=torch.int32, device=dev),
+                             accepted_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
+                             num_accepted=torch.empty(B, dtype=torch.int32, device=dev))
+        self.walk_ws = torch.empty(tv.tree_walk_accept_workspace_size(B, N), dtype=torch.uint8, device=dev)
+        self.gdn_out = torch.empty(B, N, g["H"], g["Dv"], dtype=torch.bfloat16, device=dev)
+
+    def kv_bytes(self, li):
+        x = self.layers[li]
+        ctx = x.ctx_len.cpu().numpy().astype(np.int64)
+        per_tok = 2 * x.Hkv * x.D * x.k_cache.element_size()
+        if x.window > 0:
+            # the union of keys the nodes can see: the last window - 1 positions
+            seen = np.minimum(ctx, x.window - 1)
+        else:
+            seen = ctx
+        return int(seen.sum() * per_tok)
+
+    def run(self, events=None):
+        tv = self.tv
+        ev = events or {}
+
+        def mark(name, i):
+            if name in ev:
+                ev[name][i].record()
+
+        mark("mask", 0)
+        tv.tree_mask_build(self.parent, self.ctx_len, out=self.mask_out)
+        mark("mask", 1)
+        m = self.mask_out
+        for li, x in enumerate(self.layers):
+            nm = f"attn{li}"
+            mark(nm, 0)
+            tv.tree_verify_attn(x.q, x.k_node, x.v_node, x.k_cache, x.v_cache, x.block_table, x.ctx_len,
+                                x.max_ctx_len, m["anc"], m["pos"], x.window, x.scale,
+                                out=self.attn_out[li], workspace=self.attn_ws[li])
+            mark(nm, 1)
+        mark("walk", 0)
+        tv.tree_walk_accept(self.tokens, self.parent, self.logits, out=self.walk_out, workspace=self.walk_ws)
+        mark("walk", 1)
+        g = self.gdn
+        mark("gdn", 0)
+        tv.tree_gdn_verify(g.q, g.k, g.v, g.alpha, g.beta, g.S0, m["anc"], out=self.gdn_out)
+        mark("gdn", 1)
+
+
+def cpu_baseline(step: Step, nseq: int):
+    """The oracle on the first `nseq` sequences of the same step (mask, both
+    attention layers, walk, GDN), timed on this host's cores."""
+    from oracle import attn as OA, gdn as OG, mask as OM, walk as OW
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    b_idx = list(range(nseq))
+    par = step.trees.parent[b_idx]
+    toks = step.trees.tokens[b_idx]
+    # bring the sample's inputs to the host (outside the timed region)
+    host = []
+    for x in step.layers:
+        G = x.Hq // x.Hkv
+        per = []
+        for b in b_idx:
+            ctx = int(x.ctx_len[b])
+            pages = x.block_table[b, :(ctx + 15) // 16].long()
+            kc = x.k_cache[pages].double().cpu().numpy()   # [pages, Hkv, 16, D]
+            vc = x.v_cache[pages].double().cpu().numpy()
+            table = np.arange(len(pages), dtype=np.int64)
+            per.append((ctx, kc, vc, table, x.q[b].double().cpu().numpy(), x.k_node[b].double().cpu().numpy(),
+                        x.v_node[b].double().cpu().numpy()))
+        host.append((x, G, per))
+    logits = step.logits[b_idx].double().cpu().numpy()
+    g = step.gdn
+    gin = [t[b_idx].double().cpu().numpy() for t in (g.q, g.k, g.v, g.alpha, g.beta, g.S0)]
+    ctx_np = step.ctx_len.cpu().numpy()[b_idx]
+
+    t0 = time.perf_counter()
+    m = OM.tree_mask(par, ctx_np)
+    for x, G, per in host:
+        for i, (ctx, kc, vc, table, q, kn, vn) in enumerate(per):
+            OA.tree_attn(q[None], kn[None], vn[None], kc, vc, table[None], np.array([ctx]),
+                         m["vis"][i:i + 1], m["pos"][i:i + 1], x.window, x.scale)
+    OW.tree_walk(toks, par, logits)
+    OG.gdn_tree(*gin, par)
+    dt = time.perf_counter() - t0
+    nodes = nseq * step.N
+    return dict(value=nodes / dt, unit="nodes/s", cores=int(threads), kind="oracle",
+                sample=f"first {nseq} of {step.B} sequences of the step (all {step.N} nodes; mask, "
+                       f"window and global attention, walk over 262144-entry rows, GDN), "
+                       f"{dt:.1f} s on {len(os.sched_getaffinity(0))} host cores")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
+              f"described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    step = Step(dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    names = ["mask", "attn0", "attn1", "walk", "gdn"]
+    per_call = {n: 0.0 for n in names}
+    # timed region: exactly K steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step.run()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    # per-call durations: the same steps again with events around each call
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step.run(evs[i])
+    torch.cuda.synchronize()
+    for e in evs:
+        for n in names:
+            per_call[n] += e[n][0].elapsed_time(e[n][1]) / args.steps
+
+    nodes_per_s = step.B * step.N / (ms_per_step * 1e-3)
+    kv_global = step.kv_bytes(1)
+    kv_window = step.kv_bytes(0)
+    achieved = kv_global / (per_call["attn1"] * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    out = {
+        "metric": "verified tree nodes/sec + KV-stream HBM GB/s (% of peak), 1x MI355X",
+        "value": round(nodes_per_s, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mixed batch: B=32, N=32 spine-first trees (depth<=8), ctx U[1024,32768], "
+                               "Hq=16, Hkv=8, D=256, bf16, 16-token pages; W=512 layer + global layer; "
+                               "walk over [32,33,262144] bf16 logits; GDN H=16 Dk=Dv=128",
+                   "global_batch": step.B, "nodes_per_tree": step.N,
+                   "sum_ctx": int(step.ctx_len.sum().item()), "parallelism": "single GPU"},
+        "kv_stream": {"global_layer_GBps": round(achieved, 1),
+                      "global_layer_frac_of_8TBps": round(achieved / HBM_PEAK_GBS, 4),
+                      "window_layer_GBps": round(kv_window / (per_call["attn0"] * 1e-3) / 1e9, 1),
+                      "pair_GBps": round((kv_global + kv_window) / ((per_call["attn0"] + per_call["attn1"]) * 1e-3) / 1e9, 1)},
+        "calls_ms": {n: round(v, 4) for n, v in per_call.items()},
+        "roofline": {"kernel": "tree_verify_attn (global layer: split + merge kernels)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": kv_global},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_seqs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,17 +8,31 @@
 // Work unit = (sequence b, kv head g, row group, context split).  The query
 // tile is the G*N rows (node, query head of the group) that share kv head g,
 // 64 rows per workgroup (4 waves x 16 rows).  The split's keys stream through
-// LDS in tiles of 32: K row-major, V row-major, both padded by 16 bytes per
-// row to spread LDS banks; the next tile's global loads are in flight while
-// the current one is computed.  Scores are formed transposed (S^T = K Q^T) so
-// that each lane's MFMA result holds keys of a single query row: the online
-// softmax then needs only two cross-lane steps per row, and the probabilities
-// feed the P.V MFMA (O^T = V^T P^T) straight from registers.  The split that
-// holds the end of the context also takes the node keys, masked by the
-// ancestor word of each row's node.  A split writes fp32 partials (acc, m, l);
-// a second kernel merges them by log-sum-exp.  A sequence whose keys fit one
-// split writes its output directly.
+// a ring of LDS stages, 32 keys per stage, filled by LDS DMA straight from
+// HBM (no register staging), several stages in flight while one is computed.
+// The split's page indices are cached in LDS first, so no load waits on a
+// page-table lookup.
+//
+// Scores are formed transposed (S^T = K Q^T, K rows as the MFMA A operand
+// read straight from the row-major stage) so that each lane's MFMA result
+// holds keys of a single query row: the online softmax then needs two
+// cross-lane steps per row, and the probabilities feed the P.V MFMA
+// (O^T = V^T P^T) straight from registers.  V^T comes out of the row-major
+// stage through the LDS transpose read.  Granules of 16 bytes are XOR
+// swizzled by row so both operand reads spread over the LDS banks.
+//
+// The split that holds the end of the context also takes the node keys,
+// masked by the ancestor word of each row's node.  A split writes fp32
+// partials (acc, m, l); a second kernel merges them by log-sum-exp.  A
+// sequence whose keys fit one split writes its output directly.
 #include "tv_internal.h"
+
+#ifndef TV_ATTN_LDS_BUDGET
+#define TV_ATTN_LDS_BUDGET 65536  // bytes of LDS for the K and V rings of a workgroup
+#endif
+#ifndef TV_ATTN_MIN_WG
+#define TV_ATTN_MIN_WG 2  // workgroups per CU the register budget is sized for
+#endif
 
 namespace tv {
 
@@ -26,23 +40,89 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kRows = kWaves * 16;  // query rows per workgroup
-constexpr int kTile = 32;           // keys per LDS tile
+constexpr int kTile = 32;           // keys per LDS stage
 constexpr int kThreads = kWaves * 64;
+constexpr int kMaxPages = 1024;     // page indices of one split cached in LDS
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T, int D>
 struct Cfg {
   static constexpr int kEsz = sizeof(T);
-  static constexpr int kRowBytes = D * kEsz;
-  static constexpr int kPitch = kRowBytes + 16;  // LDS row pitch in bytes
-  static constexpr int kChunksPerRow = kRowBytes / 16;
-  static constexpr int kChunksPerThread = kTile * kChunksPerRow / kThreads;
+  static constexpr int kRowBytes = D * kEsz;           // one key (or value) row
+  static constexpr int kGran = kRowBytes / 16;          // 16-byte granules per row
+  static constexpr int kSwz = (kGran < 16 ? kGran : 16) - 1;
+  static constexpr int kTileBytes = kTile * kRowBytes;  // K (or V) of one tile
+  // K and V of a tile live in separate rings of kSlots slots each
+  static constexpr int kFit = TV_ATTN_LDS_BUDGET / (2 * kTileBytes);
+  static constexpr int kSlots = kFit < 2 ? 2 : (kFit > 4 ? 4 : kFit);
+  static constexpr int kInstPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave DMA
   static constexpr int kDT = D / 16;  // 16-wide output column tiles
-  static_assert(kTile * kChunksPerRow % kThreads == 0, "tile must split evenly over threads");
+  static_assert(kInstPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile must split over waves");
+  static_assert(kInstPerWave * (2 * kSlots - 1) <= 63, "vmcnt range");
 };
+
+// Byte offset of (row, byte) in a stage: the 16-byte granules of a row are
+// XOR-swizzled with the row index.
+template <typename T, int D>
+__device__ __forceinline__ int swz(int row, int byte) {
+  using C = Cfg<T, D>;
+  return row * C::kRowBytes + ((((byte >> 4) ^ (row & C::kSwz))) << 4) + (byte & 15);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (LDS DMA; the LDS base goes in M0 and must be wave-uniform).  Issued through
+// asm so that the compiler's wait insertion does not drain the whole ring
+// before each LDS read; completion is tracked with explicit vmcnt waits.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
+  const uint32_t la = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               ::"s"(la), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS transpose read of four bf16: within each 16-lane group, lane i receives
+// element (i & 3) of the 8-byte rows addressed by lanes 4j + (i >> 2), j = 0..3.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
+  auto lp = (__attribute__((address_space(3))) bf16x4_t*)(p);
+  return __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that does not drain outstanding global loads (the
+// __syncthreads fence would wait for every in-flight stage); LDS reads issued
+// before it have completed.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wait until at most n load groups (kG loads each) issued later are in flight
+template <int kG>
+__device__ __forceinline__ void wait_groups_after(int n) {
+  switch (n) {
+    case 0: wait_vmem<0>(); break;
+    case 1: wait_vmem<kG>(); break;
+    case 2: wait_vmem<2 * kG>(); break;
+    case 3: wait_vmem<3 * kG>(); break;
+    case 4: wait_vmem<4 * kG>(); break;
+    case 5: wait_vmem<5 * kG>(); break;
+    case 6: wait_vmem<6 * kG>(); break;
+    default: wait_vmem<7 * kG>(); break;
+  }
+}
 
 struct SeqPlan {
   int start, end, split_len, nsplit;
@@ -71,62 +151,79 @@ __device__ __forceinline__ SeqPlan seq_plan(int ctx_raw, int max_ctx, int window
   return p;
 }
 
-// smallest position id of the tree (N <= 64 nodes, read by wave 0)
-__device__ __forceinline__ int tree_min_pos(const int32_t* pos_b, int N, int* s_min) {
+// smallest and largest position id of the tree (N <= 64 nodes, read by wave 0)
+__device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2* s_rng) {
   const int tid = threadIdx.x;
   if (tid < 64) {
-    int v = tid < N ? pos_b[tid] : 0x7fffffff;
+    int lo = tid < N ? pos_b[tid] : 0x7fffffff;
+    int hi = tid < N ? pos_b[tid] : -0x7fffffff;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-    if (tid == 0) *s_min = v;
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off, 64));
+      hi = max(hi, __shfl_xor(hi, off, 64));
+    }
+    if (tid == 0) *s_rng = make_int2(lo, hi);
   }
   __syncthreads();
-  return *s_min;
+  return *s_rng;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T, typename TO, int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(
+__global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
     const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
     int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
     const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int N, int Hq, int Hkv,
     int G, int rows, int row_groups, int nsplit_max, int split_tokens, int window,
-    float scale_log2, int total_units, TO* __restrict__ out, float* __restrict__ ws_acc,
+    float scale_log2, int units, TO* __restrict__ out, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
   using C = Cfg<T, D>;
-  __shared__ __align__(16) unsigned char Ks[kTile * C::kPitch];
-  __shared__ __align__(16) unsigned char Vs[kTile * C::kPitch];
+  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
+  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
+  __shared__ int s_pages[kMaxPages];
   __shared__ int s_pos[64];
-  __shared__ int s_min;
+  __shared__ int2 s_rng;
 
-  // blocks are dispatched round-robin over the 8 XCDs; give each XCD a
-  // contiguous range of work units so that row groups sharing a KV stream
-  // share an L2
-  const int nwg = gridDim.x;
-  const int logical = (blockIdx.x % 8) * (nwg / 8) + (blockIdx.x / 8);
-  if (logical >= total_units) return;
-  const int rg = logical % row_groups;
-  int rest = logical / row_groups;
-  const int s = rest % nsplit_max;
-  rest /= nsplit_max;
-  const int g = rest % Hkv;
-  const int b = rest / Hkv;
+  // Blocks are dealt round-robin to the 8 XCDs.  Work units are numbered
+  // split-major, u = s * (B * Hkv) + b * Hkv + g, and consecutive units go to
+  // different XCDs, so each XCD gets the same share of every sequence (with 8
+  // kv heads, one head of each): a ragged batch loads the XCDs evenly.  The
+  // row groups of one unit, which stream the same keys, share an XCD and its L2.
+  const int xcd = blockIdx.x % 8;
+  const int slot = blockIdx.x / 8;
+  const int u = (slot / row_groups) * 8 + xcd;
+  if (u >= units) return;
+  const int rg = slot % row_groups;
+  const int n_bg = units / nsplit_max;  // B * Hkv
+  const int s = u / n_bg;
+  const int g = (u % n_bg) % Hkv;
+  const int b = (u % n_bg) / Hkv;
 
   const int tid = threadIdx.x;
   const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
   if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
-  const int min_pos = tree_min_pos(pos_b, N, &s_min);
-  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, min_pos, nsplit_max, split_tokens);
+  const int2 prng = tree_pos_range(pos_b, N, &s_rng);
+  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, prng.x, nsplit_max, split_tokens);
   if (s >= sp.nsplit) return;  // uniform over the workgroup
   const int k0 = sp.start + s * sp.split_len;
   const int k1 = min(k0 + sp.split_len, sp.end);
   const bool last = s == sp.nsplit - 1;
   const int nctx_tiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
   const int ntiles = nctx_tiles + (last ? (N + kTile - 1) / kTile : 0);
+  // context keys in [win_all, min_pos] are inside every row's window
+  const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
 
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  // page indices of this split, clamped into the pool
+  const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
+  const int p0 = k0 >> 4;
+  const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
+  for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
+    s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int R = rg * kRows + wave * 16 + lr;
   const bool row_ok = R < rows;
   const int t = row_ok ? R / G : 0;
@@ -150,69 +247,78 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(
 #pragma unroll
     for (int ks = 0; ks < kQ; ++ks) qf_f[ks] = row_ok ? q[qoff + ks * 4 + lg] : 0.0f;
   }
+  // make the query and row loads complete here, so that the compiler's wait
+  // bookkeeping does not place a full drain inside the key loop
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < kQ; ++ks) asm volatile("" ::"v"(qf_b[ks]));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < kQ; ++ks) asm volatile("" ::"v"(qf_f[ks]));
+  }
+  asm volatile("" ::"v"(row_pos), "v"(row_anc));
 
   f32x4_t acc[C::kDT];
 #pragma unroll
   for (int dt = 0; dt < C::kDT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
   const unsigned char* kcb = reinterpret_cast<const unsigned char*>(kc);
   const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc);
   const unsigned char* knb = reinterpret_cast<const unsigned char*>(kn);
   const unsigned char* vnb = reinterpret_cast<const unsigned char*>(vn);
+  __syncthreads();  // page cache ready; every earlier global load has returned
 
-  uint4 rk[C::kChunksPerThread], rv[C::kChunksPerThread];
-  auto load_tile = [&](int it) {
+  // Enqueue the loads of one tile's keys (or values) straight into its LDS
+  // slot.  Each wave fills kInstPerWave 1 KB blocks; lane i of a block lands
+  // at block + 16 i, so the lane picks the global granule that belongs there
+  // under the swizzle.  Keys past the end of the range read a valid key
+  // instead (masked later), so that LDS never holds non-finite garbage.
+  auto issue = [&](int it, bool values) {
+    unsigned char* dst = (values ? vring : kring) + (it % C::kSlots) * C::kTileBytes;
     const bool is_node = it >= nctx_tiles;
     const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
     const int lim = is_node ? N : k1;
+    const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
 #pragma unroll
-    for (int c = 0; c < C::kChunksPerThread; ++c) {
-      const int chunk = tid + c * kThreads;
-      const int j = chunk / C::kChunksPerRow;
-      const int part = chunk % C::kChunksPerRow;
-      const int key = base + j;
-      if (key < lim) {
-        size_t off;
-        const unsigned char *ksrc, *vsrc;
-        if (is_node) {
-          off = ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes + part * 16;
-          ksrc = knb;
-          vsrc = vnb;
-        } else {
-          int page = bt_b[key >> 4];
-          page = min(max(page, 0), num_blocks - 1);
-          off = ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes + part * 16;
-          ksrc = kcb;
-          vsrc = vcb;
-        }
-        rk[c] = *reinterpret_cast<const uint4*>(ksrc + off);
-        rv[c] = *reinterpret_cast<const uint4*>(vsrc + off);
+    for (int j = 0; j < C::kInstPerWave; ++j) {
+      const int blk = wave * C::kInstPerWave + j;
+      const int gl = blk * 64 + lane;
+      const int row = gl / C::kGran;
+      const int gp = gl % C::kGran;
+      const int part = gp ^ (row & C::kSwz);
+      const int key = min(base + row, lim - 1);
+      size_t off;
+      if (is_node) {
+        off = ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes;
       } else {
-        rk[c] = make_uint4(0, 0, 0, 0);
-        rv[c] = make_uint4(0, 0, 0, 0);
+        const int pi = (key >> 4) - p0;
+        const int page = pi < kMaxPages ? s_pages[pi] : min(max(bt_b[key >> 4], 0), num_blocks - 1);
+        off = ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes;
       }
+      lds_dma16(src + off + part * 16, dst + blk * 1024);
     }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int c = 0; c < C::kChunksPerThread; ++c) {
-      const int chunk = tid + c * kThreads;
-      const int j = chunk / C::kChunksPerRow;
-      const int part = chunk % C::kChunksPerRow;
-      *reinterpret_cast<uint4*>(Ks + j * C::kPitch + part * 16) = rk[c];
-      *reinterpret_cast<uint4*>(Vs + j * C::kPitch + part * 16) = rv[c];
-    }
+    asm volatile("" ::: "memory");
   };
 
-  if (ntiles > 0) load_tile(0);
+  // Loads go out in the order K(0) V(0) K(1) V(1) ...: the prologue fills
+  // every slot, then K(it + kSlots) goes out once all waves are done with the
+  // keys of tile it and V(it + kSlots) once they are done with its values, so
+  // that while one tile's keys or values are in use, the next 2 kSlots - 1
+  // groups are in flight.
+  for (int i = 0; i < C::kSlots && i < ntiles; ++i) {
+    issue(i, false);
+    issue(i, true);
+  }
+
   for (int it = 0; it < ntiles; ++it) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(it + 1);
+    const int last_ahead = min(it + C::kSlots - 1, ntiles - 1);  // newest tile issued
+    // groups issued after K(it): V(it), then K and V of it+1 .. last_ahead
+    wait_groups_after<C::kInstPerWave>(1 + 2 * (last_ahead - it));
+    lds_barrier();  // every wave's key loads of tile `it` have landed
 
+    const unsigned char* Kt = kring + (it % C::kSlots) * C::kTileBytes;
+    const unsigned char* Vt = vring + (it % C::kSlots) * C::kTileBytes;
     const bool is_node = it >= nctx_tiles;
     const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
     const int lim = is_node ? N : k1;
@@ -222,70 +328,78 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       S[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const unsigned char* krow = Ks + (16 * j + lr) * C::kPitch;
+      const int krow = 16 * j + lr;
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int ks = 0; ks < kQ; ++ks) {
-          bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(krow + ks * 64 + lg * 16));
+          bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(Kt + swz<T, D>(krow, ks * 64 + lg * 16)));
           S[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf_b[ks], S[j], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int ks = 0; ks < kQ; ++ks) {
-          float a = *reinterpret_cast<const float*>(krow + (ks * 4 + lg) * 4);
+          float a = *reinterpret_cast<const float*>(Kt + swz<T, D>(krow, (ks * 4 + lg) * 4));
           S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf_f[ks], S[j], 0, 0, 0);
         }
       }
     }
 
-    // mask, scale into the log2 domain, row max
+    // scale into the log2 domain and mask; a context tile that lies wholly
+    // inside the range and inside every row's window needs no mask
     float x[2][4];
-    float mt = -INFINITY;
+    const bool full = !is_node && base + kTile <= lim &&
+                      (window <= 0 || (base >= win_all && base + kTile - 1 <= prng.x));
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = base + 16 * j + 4 * lg + i;
-        bool vis = row_ok && key < lim;
-        if (is_node) {
-          vis = vis && ((row_anc >> (key & 63)) & 1ull);
-          if (window > 0) {
-            const int dpos = row_pos - s_pos[key & 63];
-            vis = vis && dpos >= 0 && dpos < window;
-          }
-        } else if (window > 0) {
-          const int dpos = row_pos - key;
-          vis = vis && dpos >= 0 && dpos < window;
+        for (int i = 0; i < 4; ++i) x[j][i] = S[j][i] * scale_log2;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = base + 16 * j + 4 * lg + i;
+          const int kpos = is_node ? s_pos[key & 63] : key;
+          const int dpos = row_pos - kpos;
+          bool vis = row_ok & (key < lim);
+          vis &= !is_node | (((row_anc >> (key & 63)) & 1ull) != 0ull);
+          vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+          x[j][i] = vis ? S[j][i] * scale_log2 : -INFINITY;
         }
-        x[j][i] = vis ? S[j][i] * scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[j][i]);
       }
     }
+    float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
+    // reference point for the exponentials (0 while the row has seen nothing)
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     float p[2][4];
-    float alpha = 1.0f;
-    if (m_new == -INFINITY) {
+    float ps = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[j][i] = 0.0f;
-    } else {
-      alpha = fast_exp2(m_run - m_new);
-      float ps = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[j][i] = fast_exp2(x[j][i] - m_new);
-          ps += p[j][i];
-        }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
+      for (int i = 0; i < 4; ++i) {
+        p[j][i] = fast_exp2(x[j][i] - m_use);
+        ps += p[j][i];
+      }
+    // rescale only when some row's running max moved
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0ull) {
+      const float alpha = fast_exp2(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::kDT; ++dt) acc[dt] *= alpha;
     }
+    l_run += ps;
+    m_run = m_new;
+
+    // groups issued after V(it): K and V of it+1 .. last_ahead
+    wait_groups_after<C::kInstPerWave>(2 * (last_ahead - it));
+    lds_barrier();  // values of tile `it` have landed; every wave is done with its keys
+    if (it + C::kSlots < ntiles) issue(it + C::kSlots, false);
 
     // O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
@@ -296,22 +410,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(
         pb16[4 + i] = static_cast<short>(f32_to_bf16(p[1][i]));
       }
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pb16);
-      const uint16_t* V16 = reinterpret_cast<const uint16_t*>(Vs);
-      constexpr int P16 = C::kPitch / 2;
+      // lane (lr, lg) addresses value row 4lg + (lr >> 2) (and 16 + that),
+      // columns 16 dt + 4 (lr & 3) .. +3; the transpose read hands lane lr
+      // column 16 dt + lr of rows 4lg + 0..3 (and 16 + 4lg + 0..3)
+      const int vrow = 4 * lg + (lr >> 2);
+      const int vcol = 8 * (lr & 3);
 #pragma unroll
       for (int dt = 0; dt < C::kDT; ++dt) {
-        s16x8_t av;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          av[i] = static_cast<short>(V16[(4 * lg + i) * P16 + dt * 16 + lr]);
-          av[4 + i] = static_cast<short>(V16[(16 + 4 * lg + i) * P16 + dt * 16 + lr]);
-        }
+        const s16x4_t lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
+        const s16x4_t hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+        const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb,
                                                           acc[dt], 0, 0, 0);
       }
     } else {
-      const float* VF = reinterpret_cast<const float*>(Vs);
-      constexpr int PF = C::kPitch / 4;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -319,10 +431,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_split_kernel(
           const int krow = 16 * j + 4 * lg + i;
 #pragma unroll
           for (int dt = 0; dt < C::kDT; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(VF[krow * PF + dt * 16 + lr], p[j][i],
-                                                           acc[dt], 0, 0, 0);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                *reinterpret_cast<const float*>(Vt + swz<T, D>(krow, (dt * 16 + lr) * 4)), p[j][i],
+                acc[dt], 0, 0, 0);
         }
     }
+    lds_barrier();  // every wave is done with the values of tile `it`
+    if (it + C::kSlots < ntiles) issue(it + C::kSlots, true);
   }
 
   // row sum over the four lanes that share the row
@@ -366,36 +481,40 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     const int32_t* __restrict__ ctx_len, int max_ctx, const int32_t* __restrict__ pos, int N,
     int Hq, int Hkv, int G, int rows, int nsplit_max, int split_tokens, int window,
     const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml, TO* __restrict__ out) {
-  constexpr int kTpr = D / 4;              // threads per row
-  constexpr int kRpb = 256 / kTpr;         // rows per block
-  __shared__ int s_min;
+  constexpr int kTpr = D / 4;       // threads per row
+  constexpr int kRpb = 256 / kTpr;  // rows per block
+  __shared__ int2 s_rng;
   const int chunks = (rows + kRpb - 1) / kRpb;
   const int bg = blockIdx.x / chunks;
   const int chunk = blockIdx.x % chunks;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
   const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
-  const int min_pos = tree_min_pos(pos_b, N, &s_min);
-  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, min_pos, nsplit_max, split_tokens);
+  const int2 prng = tree_pos_range(pos_b, N, &s_rng);
+  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, prng.x, nsplit_max, split_tokens);
   if (sp.nsplit == 1) return;
   const int R = chunk * kRpb + threadIdx.x / kTpr;
   if (R >= rows) return;
   const int d0 = (threadIdx.x % kTpr) * 4;
   const size_t ub0 = (static_cast<size_t>(b) * Hkv + g) * nsplit_max * rows + R;
-  float mx = -INFINITY;
-  for (int s = 0; s < sp.nsplit; ++s) mx = fmaxf(mx, ws_ml[ub0 + static_cast<size_t>(s) * rows].x);
-  float L = 0.f;
+  // one pass: running max, rescaling the running sums when it moves
+  float mx = -INFINITY, L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int s = 0; s < sp.nsplit; ++s) {
     const size_t ub = ub0 + static_cast<size_t>(s) * rows;
     const float2 ml = ws_ml[ub];
-    const float w = ml.x == -INFINITY ? 0.0f : fast_exp2(ml.x - mx);
-    L += w * ml.y;
     const float4 a = *reinterpret_cast<const float4*>(ws_acc + ub * D + d0);
-    o.x += w * a.x;
-    o.y += w * a.y;
-    o.z += w * a.z;
-    o.w += w * a.w;
+    if (ml.x == -INFINITY) continue;  // this split saw no key of the row
+    const float m_new = fmaxf(mx, ml.x);
+    const float c_old = fast_exp2(mx - m_new);  // 0 while mx is still -inf
+    const float c_new = fast_exp2(ml.x - m_new);
+    L = L * c_old + ml.y * c_new;
+    o.x = o.x * c_old + a.x * c_new;
+    o.y = o.y * c_old + a.y * c_new;
+    o.z = o.z * c_old + a.z * c_new;
+    o.w = o.w * c_old + a.w * c_new;
+    mx = m_new;
   }
   const float inv = 1.0f / L;
   const int t = R / G, hl = R % G;
@@ -416,8 +535,8 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                         int max_blocks, int num_blocks, const int32_t* ctx_len, int max_ctx,
                         const uint64_t* anc, const int32_t* pos, int B, int N, int Hq, int Hkv,
                         int window, float scale, void* out, void* ws, hipStream_t stream) {
-  const long long units = static_cast<long long>(B) * Hkv * pl.nsplit * pl.row_groups;
-  const long long grid = (units + 7) / 8 * 8;
+  const long long units = static_cast<long long>(B) * Hkv * pl.nsplit;
+  const long long grid = (units + 7) / 8 * 8 * pl.row_groups;
   float* ws_acc = nullptr;
   float2* ws_ml = nullptr;
   if (pl.nsplit > 1) {
@@ -426,8 +545,8 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                                       static_cast<size_t>(B) * Hkv * pl.nsplit * pl.rows * D * 4);
   }
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                     stream, static_cast<const T*>(q), static_cast<const T*>(k_node),
+  hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                     0, stream, static_cast<const T*>(q), static_cast<const T*>(k_node),
                      static_cast<const T*>(v_node), static_cast<const T*>(k_cache),
                      static_cast<const T*>(v_cache), block_table, max_blocks, num_blocks, ctx_len,
                      max_ctx, anc, pos, N, Hq, Hkv, pl.G, pl.rows, pl.row_groups, pl.nsplit,
@@ -445,6 +564,13 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
 
 }  // namespace
 
+#ifndef TV_ATTN_MIN_SPLIT
+#define TV_ATTN_MIN_SPLIT 2048  // keys per split at least (partials stay small)
+#endif
+#ifndef TV_ATTN_TARGET_WG
+#define TV_ATTN_TARGET_WG 4096  // workgroups the split plan aims for
+#endif
+
 AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int window) {
   AttnPlan p{};
   p.G = Hq / Hkv;
@@ -454,8 +580,8 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int wi
   // aim for a few thousand workgroups, but keep each split long enough that
   // its fp32 partials stay small next to the keys it streams
   const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  long long want = (4096 + units - 1) / units;
-  const int min_split = 1024;
+  long long want = (TV_ATTN_TARGET_WG + units - 1) / units;
+  const int min_split = TV_ATTN_MIN_SPLIT;
   long long cap = (range + min_split - 1) / min_split;
   if (cap < 1) cap = 1;
   if (want > cap) want = cap;
@@ -481,7 +607,7 @@ hipError_t launch_attn(const AttnPlan& plan, const void* q, const void* k_node, 
   return launch_typed<TYPE, OTYPE, DIM>(plan, q, k_node, v_node, k_cache, v_cache, block_table, \
                                         max_blocks, num_blocks, ctx_len, max_ctx_len, anc, pos, \
                                         B, N, Hq, Hkv, window, scale, out, ws, stream)
-#define TV_ATTN_DIMS(TYPE, OTYPE)            \
+#define TV_ATTN_DIMS(TYPE, OTYPE)               \
   if (D == 64) TV_ATTN_CASE(TYPE, OTYPE, 64);   \
   if (D == 128) TV_ATTN_CASE(TYPE, OTYPE, 128); \
   if (D == 256) TV_ATTN_CASE(TYPE, OTYPE, 256);
