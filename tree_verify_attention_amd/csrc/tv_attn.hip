@@ -66,12 +66,21 @@ struct Cfg {
   static_assert(kInstPerWave * (2 * kSlots - 1) <= 63, "vmcnt range");
 };
 
-// Byte offset of (row, byte) in a stage: the 16-byte granules of a row are
-// XOR-swizzled with the row index.
+// XOR key of a row's 16-byte granules.  Rows 0..7 of every 16 get the even
+// keys 0, 2, .., 14 and rows 8..15 the odd ones: the K operand reads (16 rows,
+// one granule each) and the V transpose reads (4 rows, two adjacent granules
+// each, per 16 lanes) then fall on distinct LDS banks.
+template <typename T, int D>
+__device__ __forceinline__ int swz_key(int row) {
+  using C = Cfg<T, D>;
+  return ((((row & 7) << 1) | ((row >> 3) & 1))) & C::kSwz;
+}
+
+// Byte offset of (row, byte) in a tile slot under that swizzle.
 template <typename T, int D>
 __device__ __forceinline__ int swz(int row, int byte) {
   using C = Cfg<T, D>;
-  return row * C::kRowBytes + ((((byte >> 4) ^ (row & C::kSwz))) << 4) + (byte & 15);
+  return row * C::kRowBytes + (((byte >> 4) ^ swz_key<T, D>(row)) << 4) + (byte & 15);
 }
 
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
@@ -86,6 +95,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                ::"s"(la), "v"(src) : "memory", "m0");
 }
+
 #pragma clang diagnostic pop
 
 // LDS transpose read of four bf16: within each 16-lane group, lane i receives
@@ -109,18 +119,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// wait until at most n load groups (kG loads each) issued later are in flight
-template <int kG>
-__device__ __forceinline__ void wait_groups_after(int n) {
-  switch (n) {
-    case 0: wait_vmem<0>(); break;
-    case 1: wait_vmem<kG>(); break;
-    case 2: wait_vmem<2 * kG>(); break;
-    case 3: wait_vmem<3 * kG>(); break;
-    case 4: wait_vmem<4 * kG>(); break;
-    case 5: wait_vmem<5 * kG>(); break;
-    case 6: wait_vmem<6 * kG>(); break;
-    default: wait_vmem<7 * kG>(); break;
+// wait until at most n vector-memory instructions issued later are in flight
+// (n above 31 waits for 31, which is only stricter)
+template <int M = 0>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (M < 31) {
+    if (n == M) {
+      wait_vmem<M>();
+      return;
+    }
+    wait_vm_upto<M + 1>(n);
+  } else {
+    wait_vmem<31>();
   }
 }
 
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
       const int gl = blk * 64 + lane;
       const int row = gl / C::kGran;
       const int gp = gl % C::kGran;
-      const int part = gp ^ (row & C::kSwz);
+      const int part = gp ^ swz_key<T, D>(row);
       const int key = min(base + row, lim - 1);
       size_t off;
       if (is_node) {
@@ -302,20 +312,24 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
   };
 
   // Loads go out in the order K(0) V(0) K(1) V(1) ...: the prologue fills
-  // every slot, then K(it + kSlots) goes out once all waves are done with the
-  // keys of tile it and V(it + kSlots) once they are done with its values, so
-  // that while one tile's keys or values are in use, the next 2 kSlots - 1
-  // groups are in flight.
+  // every slot; afterwards K(it + kSlots) goes out once every wave is done
+  // with the keys of tile it (second barrier of iteration it) and
+  // V(it + kSlots) once every wave is done with its values (first barrier of
+  // iteration it + 1).  While one tile's keys or values are in use, the next
+  // 2 kSlots - 1 groups are in flight; two barriers per tile.
   for (int i = 0; i < C::kSlots && i < ntiles; ++i) {
     issue(i, false);
     issue(i, true);
   }
 
   for (int it = 0; it < ntiles; ++it) {
-    const int last_ahead = min(it + C::kSlots - 1, ntiles - 1);  // newest tile issued
-    // groups issued after K(it): V(it), then K and V of it+1 .. last_ahead
-    wait_groups_after<C::kInstPerWave>(1 + 2 * (last_ahead - it));
-    lds_barrier();  // every wave's key loads of tile `it` have landed
+    const int newest = min(it + C::kSlots - 1, ntiles - 1);  // newest tile whose keys are out
+    // values issued so far reach tile newest (prologue) or newest - 1
+    const int v_out = it == 0 ? newest : min(it + C::kSlots - 2, ntiles - 1);
+    // loads issued after K(it): V(it .. v_out) and K(it + 1 .. newest)
+    wait_vm_upto(C::kInstPerWave * ((v_out - it + 1) + (newest - it)));
+    lds_barrier();  // keys of tile `it` have landed; every wave is done with tile it - 1
+    if (it > 0 && it + C::kSlots - 1 < ntiles) issue(it + C::kSlots - 1, true);
 
     const unsigned char* Kt = kring + (it % C::kSlots) * C::kTileBytes;
     const unsigned char* Vt = vring + (it % C::kSlots) * C::kTileBytes;
@@ -396,20 +410,24 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
     l_run += ps;
     m_run = m_new;
 
-    // groups issued after V(it): K and V of it+1 .. last_ahead
-    wait_groups_after<C::kInstPerWave>(2 * (last_ahead - it));
+    // loads issued after V(it): K and V of it + 1 .. newest
+    wait_vm_upto(C::kInstPerWave * 2 * (newest - it));
     lds_barrier();  // values of tile `it` have landed; every wave is done with its keys
     if (it + C::kSlots < ntiles) issue(it + C::kSlots, false);
 
     // O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
-      s16x8_t pb16;
+      // P = P_hi + P_lo, both bf16: the two products keep P to ~16 mantissa
+      // bits, so the bf16 MFMA adds no visible error to the weights
+      bf16x8_t ph, pl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb16[i] = static_cast<short>(f32_to_bf16(p[0][i]));
-        pb16[4 + i] = static_cast<short>(f32_to_bf16(p[1][i]));
-      }
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pb16);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const __bf16 h = static_cast<__bf16>(p[j][i]);
+          ph[4 * j + i] = h;
+          pl[4 * j + i] = static_cast<__bf16>(p[j][i] - static_cast<float>(h));
+        }
       // lane (lr, lg) addresses value row 4lg + (lr >> 2) (and 16 + that),
       // columns 16 dt + 4 (lr & 3) .. +3; the transpose read hands lane lr
       // column 16 dt + lr of rows 4lg + 0..3 (and 16 + 4lg + 0..3)
@@ -420,8 +438,9 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
         const s16x4_t lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
         const s16x4_t hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
         const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb,
-                                                          acc[dt], 0, 0, 0);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, acc[dt], 0, 0, 0);
       }
     } else {
 #pragma unroll
@@ -436,8 +455,6 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
                 acc[dt], 0, 0, 0);
         }
     }
-    lds_barrier();  // every wave is done with the values of tile `it`
-    if (it + C::kSlots < ntiles) issue(it + C::kSlots, true);
   }
 
   // row sum over the four lanes that share the row

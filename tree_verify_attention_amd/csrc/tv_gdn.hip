@@ -34,11 +34,46 @@ __device__ __forceinline__ void store_f(float* p, size_t i, float v) { p[i] = v;
 __device__ __forceinline__ void store_f(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
 size_t gdn_lds_bytes(int N) {
-  // s_k, s_q [N][128]; s_x, s_y [N][N]; s_u, s_ks, s_qs [N][32]; gamma, beta,
-  // alpha [N] (+1 pad); anc [N] (u64)
-  return sizeof(float) * (static_cast<size_t>(N) * kDk * 2 + static_cast<size_t>(N) * N * 2 +
-                          static_cast<size_t>(N) * kCB * 3 + 3 * N + 1) +
+  // s_s0 [128][32]; s_k, s_q [N][128]; s_x, s_y [N][N]; s_u, s_ks, s_qs
+  // [N][32]; gamma, beta, alpha [N] (+1 pad); anc [N] (u64)
+  return sizeof(float) * (static_cast<size_t>(kDk) * kCB + static_cast<size_t>(N) * kDk * 2 +
+                          static_cast<size_t>(N) * N * 2 + static_cast<size_t>(N) * kCB * 3 +
+                          3 * N + 1) +
          sizeof(uint64_t) * N + 16;
+}
+
+// 8 consecutive elements of an input row, loaded with 16-byte accesses
+template <typename T>
+struct Chunk8 {
+  uint4 w[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ Chunk8<T> load8(const T* p) {
+  Chunk8<T> c;
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(T) / 2); ++i) c.w[i] = reinterpret_cast<const uint4*>(p)[i];
+  return c;
+}
+
+__device__ __forceinline__ void store8(float* dst, const Chunk8<uint16_t>& c) {
+  const uint32_t w[4] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w};
+  float4 lo, hi;
+  lo.x = __uint_as_float(w[0] << 16);
+  lo.y = __uint_as_float(w[0] & 0xffff0000u);
+  lo.z = __uint_as_float(w[1] << 16);
+  lo.w = __uint_as_float(w[1] & 0xffff0000u);
+  hi.x = __uint_as_float(w[2] << 16);
+  hi.y = __uint_as_float(w[2] & 0xffff0000u);
+  hi.z = __uint_as_float(w[3] << 16);
+  hi.w = __uint_as_float(w[3] & 0xffff0000u);
+  reinterpret_cast<float4*>(dst)[0] = lo;
+  reinterpret_cast<float4*>(dst)[1] = hi;
+}
+
+__device__ __forceinline__ void store8(float* dst, const Chunk8<float>& c) {
+  reinterpret_cast<uint4*>(dst)[0] = c.w[0];
+  reinterpret_cast<uint4*>(dst)[1] = c.w[1];
 }
 
 template <typename T, typename TO>
@@ -47,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     const uint64_t* __restrict__ anc, int N, int H, int Dv, TO* __restrict__ out) {
   extern __shared__ __align__(16) float lds[];
-  float* s_k = lds;                // [N][kDk]
+  float* s_s0 = lds;                // [kDk][kCB]  this block's columns of S0
+  float* s_k = s_s0 + kDk * kCB;    // [N][kDk]
   float* s_q = s_k + N * kDk;      // [N][kDk]
   float* s_x = s_q + N * kDk;      // [N][N]
   float* s_y = s_x + N * N;        // [N][N]
@@ -80,11 +116,39 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
     const uint64_t below = t >= 63 ? ~0ull >> 1 : ((1ull << t) - 1ull);
     s_anc[t] = (anc[static_cast<size_t>(b) * N + t] & live & below) | (1ull << t);
   }
-  for (int e = tid; e < N * kDk; e += kThreads) {
-    const int t = e / kDk, d = e % kDk;
-    const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + d;
-    s_k[e] = load_f(k, off);
-    s_q[e] = load_f(q, off);
+  {
+    // keys and queries, 8 elements per chunk: every thread issues all of its
+    // loads before converting any (N * 128 / 8 <= 1024 chunks, 4 per thread)
+    constexpr int kPer = 4;
+    const int nchunk = N * kDk / 8;
+    Chunk8<T> ck[kPer], cq[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < nchunk) {
+        const int t = e / (kDk / 8), d = (e % (kDk / 8)) * 8;
+        const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + d;
+        ck[u] = load8(k + off);
+        cq[u] = load8(q + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < nchunk) {
+        store8(s_k + e * 8, ck[u]);
+        store8(s_q + e * 8, cq[u]);
+      }
+    }
+  }
+  {
+    // the 128 x 32 column block of S0, as float4 (all loads in flight at once)
+    const float* s0 = S0 + (static_cast<size_t>(b) * H + h) * kDk * Dv + cb * kCB;
+    for (int e = tid; e < kDk * kCB / 4; e += kThreads) {
+      const int d = e / (kCB / 4), c4 = e % (kCB / 4);
+      reinterpret_cast<float4*>(s_s0)[e] =
+          *reinterpret_cast<const float4*>(s0 + static_cast<size_t>(d) * Dv + 4 * c4);
+    }
   }
   __syncthreads();
 
@@ -121,10 +185,13 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
       const float* ki = s_k + i * kDk;
       const float* qt = s_q + t * kDk;
       float kk = 0.0f, qk = 0.0f;
-#pragma unroll 8
-      for (int d = 0; d < kDk; ++d) {
-        kk = fmaf(kt[d], ki[d], kk);
-        qk = fmaf(qt[d], ki[d], qk);
+#pragma unroll 4
+      for (int d = 0; d < kDk; d += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(kt + d);
+        const float4 c = *reinterpret_cast<const float4*>(ki + d);
+        const float4 e = *reinterpret_cast<const float4*>(qt + d);
+        kk = fmaf(a.x, c.x, fmaf(a.y, c.y, fmaf(a.z, c.z, fmaf(a.w, c.w, kk))));
+        qk = fmaf(e.x, c.x, fmaf(e.y, c.y, fmaf(e.z, c.z, fmaf(e.w, c.w, qk))));
       }
       yv = r * qk;
       if (i != t) xv = s_beta[t] * r * kk;
@@ -134,20 +201,26 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
   }
 
   {
-    // K S0 and Q S0 for this column block: thread = (column c, node group)
+    // K S0 and Q S0 for this column block: thread = (column c, node group),
+    // four nodes per pass, four head dimensions per LDS read
     constexpr int kGroups = kThreads / kCB;
     const int c = tid % kCB;
     const int grp = tid / kCB;
-    const float* s0 = S0 + (static_cast<size_t>(b) * H + h) * kDk * Dv + cb * kCB + c;
     for (int t0 = grp; t0 < N; t0 += 4 * kGroups) {
       float ak[4] = {0.f, 0.f, 0.f, 0.f}, aq[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int d = 0; d < kDk; ++d) {
-        const float sv = s0[static_cast<size_t>(d) * Dv];
+      int tt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) tt[u] = min(t0 + u * kGroups, N - 1);
+#pragma unroll 4
+      for (int d = 0; d < kDk; d += 4) {
+        const float s0a = s_s0[(d + 0) * kCB + c], s0b = s_s0[(d + 1) * kCB + c];
+        const float s0c = s_s0[(d + 2) * kCB + c], s0d = s_s0[(d + 3) * kCB + c];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int t = min(t0 + u * kGroups, N - 1);
-          ak[u] = fmaf(s_k[t * kDk + d], sv, ak[u]);
-          aq[u] = fmaf(s_q[t * kDk + d], sv, aq[u]);
+          const float4 kv = *reinterpret_cast<const float4*>(s_k + tt[u] * kDk + d);
+          const float4 qv = *reinterpret_cast<const float4*>(s_q + tt[u] * kDk + d);
+          ak[u] = fmaf(kv.x, s0a, fmaf(kv.y, s0b, fmaf(kv.z, s0c, fmaf(kv.w, s0d, ak[u]))));
+          aq[u] = fmaf(qv.x, s0a, fmaf(qv.y, s0b, fmaf(qv.z, s0c, fmaf(qv.w, s0d, aq[u]))));
         }
       }
 #pragma unroll

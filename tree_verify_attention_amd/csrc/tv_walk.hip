@@ -15,7 +15,7 @@ namespace {
 constexpr int kArgmaxThreads = 256;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 struct Best {
   float v;
