@@ -91,8 +91,11 @@ def test_attn_workspace_sizes(lib):
     assert ws(1, 32, 12, 8, 256, 4096, 0) == 0        # Hq % Hkv != 0
     # a window shorter than one split needs no partials
     assert ws(32, 32, 16, 8, 256, 32768, 512) == 0
+    # global layer: fp32 partials (D values + max + sum) of 64 rows per slot,
+    # at least one slot per (sequence, kv head)
     big = ws(32, 32, 16, 8, 256, 32768, 0)
-    assert big > 0 and big % (32 * 8 * 64) == 0
+    slot = 64 * (256 * 4 + 8)
+    assert big > 0 and big % slot == 0 and big // slot >= 32 * 8
 
 
 def test_gdn_validation(lib):

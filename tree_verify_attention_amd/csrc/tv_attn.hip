@@ -180,58 +180,29 @@ __device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One segment of the key stream of one (sequence, kv head, row group): the
+// context keys [k0, k1) and the node tiles [node_t0, node_t1) (32 nodes each),
+// accumulated with an online softmax.  With final_out the normalised rows go
+// to `out`; otherwise the unnormalised partial (acc, m, l) goes to partial
+// slot `pslot`.  s_pos holds the tree's position ids and s_pages the page
+// indices of pages k0 / 16 onwards, both filled by the caller before a
+// barrier that this routine also relies on for its own LDS.
 template <typename T, typename TO, int D>
-__global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
+__device__ __forceinline__ void attn_segment(
     const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
-    const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
-    int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
-    const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int N, int Hq, int Hkv,
-    int G, int rows, int row_groups, int nsplit_max, int split_tokens, int window,
-    float scale_log2, int units, TO* __restrict__ out, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml) {
+    const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt_b,
+    int num_blocks, const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos_b, int N,
+    int Hq, int Hkv, int G, int rows, int window, float scale_log2, int b, int g, int rg, int k0,
+    int k1, int node_t0, int node_t1, int2 prng, bool final_out, size_t pslot,
+    TO* __restrict__ out, float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
+    unsigned char* kring, unsigned char* vring, const int* s_pages, const int* s_pos) {
   using C = Cfg<T, D>;
-  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
-  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
-  __shared__ int s_pages[kMaxPages];
-  __shared__ int s_pos[64];
-  __shared__ int2 s_rng;
-
-  // Blocks are dealt round-robin to the 8 XCDs.  Work units are numbered
-  // split-major, u = s * (B * Hkv) + b * Hkv + g, and consecutive units go to
-  // different XCDs, so each XCD gets the same share of every sequence (with 8
-  // kv heads, one head of each): a ragged batch loads the XCDs evenly.  The
-  // row groups of one unit, which stream the same keys, share an XCD and its L2.
-  const int xcd = blockIdx.x % 8;
-  const int slot = blockIdx.x / 8;
-  const int u = (slot / row_groups) * 8 + xcd;
-  if (u >= units) return;
-  const int rg = slot % row_groups;
-  const int n_bg = units / nsplit_max;  // B * Hkv
-  const int s = u / n_bg;
-  const int g = (u % n_bg) % Hkv;
-  const int b = (u % n_bg) / Hkv;
-
   const int tid = threadIdx.x;
-  const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
-  if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
-  const int2 prng = tree_pos_range(pos_b, N, &s_rng);
-  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, prng.x, nsplit_max, split_tokens);
-  if (s >= sp.nsplit) return;  // uniform over the workgroup
-  const int k0 = sp.start + s * sp.split_len;
-  const int k1 = min(k0 + sp.split_len, sp.end);
-  const bool last = s == sp.nsplit - 1;
   const int nctx_tiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
-  const int ntiles = nctx_tiles + (last ? (N + kTile - 1) / kTile : 0);
+  const int ntiles = nctx_tiles + (node_t1 - node_t0);
   // context keys in [win_all, min_pos] are inside every row's window
   const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
-
-  // page indices of this split, clamped into the pool
-  const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
   const int p0 = k0 >> 4;
-  const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-  for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
-    s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
-
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int R = rg * kRows + wave * 16 + lr;
@@ -277,7 +248,11 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
   const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc);
   const unsigned char* knb = reinterpret_cast<const unsigned char*>(kn);
   const unsigned char* vnb = reinterpret_cast<const unsigned char*>(vn);
-  __syncthreads();  // page cache ready; every earlier global load has returned
+  // every earlier global access (query, row data, an earlier segment's stores)
+  // completes here, so the counted waits below see only this segment's loads
+  wait_vmem<0>();
+  __syncthreads();  // page cache ready
+  if (ntiles == 0) return;
 
   // Enqueue the loads of one tile's keys (or values) straight into its LDS
   // slot.  Each wave fills kInstPerWave 1 KB blocks; lane i of a block lands
@@ -287,7 +262,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
   auto issue = [&](int it, bool values) {
     unsigned char* dst = (values ? vring : kring) + (it % C::kSlots) * C::kTileBytes;
     const bool is_node = it >= nctx_tiles;
-    const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
+    const int base = is_node ? (node_t0 + it - nctx_tiles) * kTile : k0 + it * kTile;
     const int lim = is_node ? N : k1;
     const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
 #pragma unroll
@@ -334,7 +309,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
     const unsigned char* Kt = kring + (it % C::kSlots) * C::kTileBytes;
     const unsigned char* Vt = vring + (it % C::kSlots) * C::kTileBytes;
     const bool is_node = it >= nctx_tiles;
-    const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
+    const int base = is_node ? (node_t0 + it - nctx_tiles) * kTile : k0 + it * kTile;
     const int lim = is_node ? N : k1;
 
     // S^T for two 16-key halves: lane holds keys 16j + 4lg + i of row lr
@@ -462,7 +437,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
   l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
   if (!row_ok) return;
 
-  if (sp.nsplit == 1) {
+  if (final_out) {
     const float inv = 1.0f / l_tot;
     TO* o = out + qoff;
 #pragma unroll
@@ -481,13 +456,250 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
       }
     }
   } else {
-    const size_t ub = ((static_cast<size_t>(b) * Hkv + g) * nsplit_max + s) * rows + R;
+    const size_t ub = pslot * rows + R;
     float* pa = ws_acc + ub * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt)
       *reinterpret_cast<float4*>(pa + dt * 16 + 4 * lg) =
           make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
     if (lg == 0) ws_ml[ub] = make_float2(m_run, l_tot);
+  }
+}
+
+
+template <typename T, typename TO, int D>
+__global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
+    const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
+    int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
+    const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int N, int Hq, int Hkv,
+    int G, int rows, int row_groups, int nsplit_max, int split_tokens, int window,
+    float scale_log2, int units, TO* __restrict__ out, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
+  using C = Cfg<T, D>;
+  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
+  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
+  __shared__ int s_pages[kMaxPages];
+  __shared__ int s_pos[64];
+  __shared__ int2 s_rng;
+
+  // Blocks are dealt round-robin to the 8 XCDs.  Work units are numbered
+  // split-major, u = s * (B * Hkv) + b * Hkv + g, and consecutive units go to
+  // different XCDs, so each XCD gets the same share of every sequence (with 8
+  // kv heads, one head of each): a ragged batch loads the XCDs evenly.  The
+  // row groups of one unit, which stream the same keys, share an XCD and its L2.
+  const int xcd = blockIdx.x % 8;
+  const int slot = blockIdx.x / 8;
+  const int u = (slot / row_groups) * 8 + xcd;
+  if (u >= units) return;
+  const int rg = slot % row_groups;
+  const int n_bg = units / nsplit_max;  // B * Hkv
+  const int s = u / n_bg;
+  const int g = (u % n_bg) % Hkv;
+  const int b = (u % n_bg) / Hkv;
+
+  const int tid = threadIdx.x;
+  const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
+  if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
+  const int2 prng = tree_pos_range(pos_b, N, &s_rng);
+  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, prng.x, nsplit_max, split_tokens);
+  if (s >= sp.nsplit) return;  // uniform over the workgroup
+  const int k0 = sp.start + s * sp.split_len;
+  const int k1 = min(k0 + sp.split_len, sp.end);
+  const bool last = s == sp.nsplit - 1;
+
+  // page indices of this split, clamped into the pool
+  const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
+  const int p0 = k0 >> 4;
+  const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
+  for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
+    s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
+
+  attn_segment<T, TO, D>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
+                         window, scale_log2, b, g, rg, k0, k1, 0, last ? (N + kTile - 1) / kTile : 0,
+                         prng, sp.nsplit == 1,
+                         (static_cast<size_t>(b) * Hkv + g) * nsplit_max + s, out, ws_acc, ws_ml,
+                         kring, vring, s_pages, s_pos);
+}
+
+// Stream decomposition of a layer without a window.  The tiles of every
+// (sequence, kv head) unit -- its context keys in tiles of 32, then its node
+// tiles -- are laid end to end in unit order j = b * Hkv + g, and workgroup w
+// takes the contiguous share [w * per, (w + 1) * per) of that sequence.  Every
+// workgroup streams the same number of tiles, whatever the mix of context
+// lengths, so the grid ends together.  A workgroup walks the units its share
+// touches as segments; a unit covered by one segment is written out directly,
+// otherwise each segment leaves a partial in slot w + j (unique, because
+// shares are disjoint and ordered) for the merge.
+constexpr int kMaxSeqs = 4 * kThreads - 1;  // sequences the stream prefix covers
+
+struct StreamLayout {
+  int total;  // tiles over all units
+  int per;    // tiles per workgroup
+};
+
+// tiles of sequence b's units and their start offsets: s_pref[b] = tiles of
+// sequences before b (one kv head each), filled for b = 0..B
+__device__ __forceinline__ void stream_prefix(const int32_t* ctx_len, int max_ctx, int B, int N,
+                                              int* s_pref) {
+  const int tid = threadIdx.x;
+  const int ntn = (N + kTile - 1) / kTile;
+  // each thread owns up to 4 consecutive sequences
+  int own[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = tid * 4 + i;
+    int tl = 0;
+    if (b < B) {
+      const int ctx = min(max(ctx_len[b], 0), max_ctx);
+      tl = (ctx + kTile - 1) / kTile + ntn;
+    }
+    own[i] = tl;
+    sum += tl;
+  }
+  // inclusive scan of the per-thread sums over the workgroup
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if ((tid & 63) >= off) incl += v;
+  }
+  __shared__ int s_wave[kWaves];
+  if ((tid & 63) == 63) s_wave[tid >> 6] = incl;
+  __syncthreads();
+  int before = incl - sum;
+  for (int w = 0; w < (tid >> 6); ++w) before += s_wave[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = tid * 4 + i;
+    if (b <= B) s_pref[b] = before;
+    before += own[i];
+  }
+  __syncthreads();
+}
+
+template <typename T, typename TO, int D>
+__global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
+    const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
+    const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
+    int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
+    const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int B, int N, int Hq,
+    int Hkv, int G, int rows, float scale_log2, TO* __restrict__ out, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
+  using C = Cfg<T, D>;
+  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
+  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
+  __shared__ int s_pages[kMaxPages];
+  __shared__ int s_pos[64];
+  __shared__ int2 s_rng;
+  __shared__ int s_pref[kMaxSeqs + 1];
+
+  const int tid = threadIdx.x;
+  const int ntn = (N + kTile - 1) / kTile;
+  stream_prefix(ctx_len, max_ctx, B, N, s_pref);
+  const int total = s_pref[B] * Hkv;
+  const int per = (total + gridDim.x - 1) / gridDim.x;
+  const int w = blockIdx.x;
+  int cur = w * per;
+  const int r1 = min(total, cur + per);
+
+  // first sequence whose units reach past `cur`
+  int b = 0;
+  {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] * Hkv <= cur) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+  }
+  while (cur < r1) {
+    while (cur >= s_pref[b + 1] * Hkv) ++b;
+    const int tiles_b = s_pref[b + 1] - s_pref[b];
+    const int g = (cur - s_pref[b] * Hkv) / tiles_b;
+    const int us = s_pref[b] * Hkv + g * tiles_b;  // first tile of unit (b, g)
+    const int t0 = cur - us;
+    const int t1 = min(tiles_b, r1 - us);
+    const int ctx = min(max(ctx_len[b], 0), max_ctx);
+    const int nct = tiles_b - ntn;  // context tiles of the unit
+    const int k0 = min(min(t0, nct) * kTile, ctx);
+    const int k1 = min(min(t1, nct) * kTile, ctx);
+    const int n0 = max(t0, nct) - nct;
+    const int n1 = max(t1, nct) - nct;
+
+    __syncthreads();  // the previous segment is done with every LDS buffer
+    const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
+    if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
+    const int2 prng = tree_pos_range(pos_b, N, &s_rng);
+    const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
+    const int p0 = k0 >> 4;
+    const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
+    for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
+      s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
+
+    attn_segment<T, TO, D>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
+                           0, scale_log2, b, g, 0, k0, k1, n0, n1, prng,
+                           t0 == 0 && t1 == tiles_b, static_cast<size_t>(w) + b * Hkv + g, out,
+                           ws_acc, ws_ml, kring, vring, s_pages, s_pos);
+    cur = us + t1;
+  }
+}
+
+// Merge of the stream layout: unit (b, g) covers tiles [us, us + tiles_b);
+// its segments belong to workgroups us / per .. (us + tiles_b - 1) / per and
+// sit in slots w + j.  A unit with one segment was written out directly.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void attn_merge_stream_kernel(
+    const int32_t* __restrict__ ctx_len, int max_ctx, int B, int N, int Hq, int Hkv, int G,
+    int rows, int nwg, const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
+    TO* __restrict__ out) {
+  constexpr int kTpr = D / 4;       // threads per row
+  constexpr int kRpb = 256 / kTpr;  // rows per block
+  __shared__ int s_pref[kMaxSeqs + 1];
+  const int chunks = (rows + kRpb - 1) / kRpb;
+  const int j = blockIdx.x / chunks;
+  const int chunk = blockIdx.x % chunks;
+  const int g = j % Hkv;
+  const int b = j / Hkv;
+  stream_prefix(ctx_len, max_ctx, B, N, s_pref);
+  const int total = s_pref[B] * Hkv;
+  const int per = (total + nwg - 1) / nwg;
+  const int tiles_b = s_pref[b + 1] - s_pref[b];
+  const int us = s_pref[b] * Hkv + g * tiles_b;
+  const int w_lo = us / per, w_hi = (us + tiles_b - 1) / per;
+  if (w_lo == w_hi) return;
+  const int R = chunk * kRpb + threadIdx.x / kTpr;
+  if (R >= rows) return;
+  const int d0 = (threadIdx.x % kTpr) * 4;
+  float mx = -INFINITY, L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int w = w_lo; w <= w_hi; ++w) {
+    const size_t ub = (static_cast<size_t>(w) + j) * rows + R;
+    const float2 ml = ws_ml[ub];
+    const float4 a = *reinterpret_cast<const float4*>(ws_acc + ub * D + d0);
+    if (ml.x == -INFINITY) continue;  // this segment saw no key of the row
+    const float m_new = fmaxf(mx, ml.x);
+    const float c_old = fast_exp2(mx - m_new);
+    const float c_new = fast_exp2(ml.x - m_new);
+    L = L * c_old + ml.y * c_new;
+    o.x = o.x * c_old + a.x * c_new;
+    o.y = o.y * c_old + a.y * c_new;
+    o.z = o.z * c_old + a.z * c_new;
+    o.w = o.w * c_old + a.w * c_new;
+    mx = m_new;
+  }
+  const float inv = 1.0f / L;
+  const int t = R / G, hl = R % G;
+  TO* op = out + ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D + d0;
+  if constexpr (sizeof(TO) == 2) {
+    uint2 wv;
+    wv.x = static_cast<uint32_t>(f32_to_bf16(o.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(o.y * inv)) << 16);
+    wv.y = static_cast<uint32_t>(f32_to_bf16(o.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(o.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(op) = wv;
+  } else {
+    *reinterpret_cast<float4*>(op) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   }
 }
 
@@ -562,6 +774,25 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                                       static_cast<size_t>(B) * Hkv * pl.nsplit * pl.rows * D * 4);
   }
   const float scale_log2 = scale * 1.4426950408889634f;
+  constexpr int kRpb = 256 / (D / 4);
+  const unsigned merge_grid = static_cast<unsigned>(B) * Hkv * ((pl.rows + kRpb - 1) / kRpb);
+  if (pl.stream_wg > 0) {
+    ws_acc = static_cast<float*>(ws);
+    const size_t slots = static_cast<size_t>(pl.stream_wg) + static_cast<size_t>(B) * Hkv - 1;
+    ws_ml = reinterpret_cast<float2*>(static_cast<char*>(ws) + slots * pl.rows * D * 4);
+    hipLaunchKernelGGL((attn_stream_kernel<T, TO, D>), dim3(pl.stream_wg), dim3(kThreads), 0,
+                       stream, static_cast<const T*>(q), static_cast<const T*>(k_node),
+                       static_cast<const T*>(v_node), static_cast<const T*>(k_cache),
+                       static_cast<const T*>(v_cache), block_table, max_blocks, num_blocks,
+                       ctx_len, max_ctx, anc, pos, B, N, Hq, Hkv, pl.G, pl.rows, scale_log2,
+                       static_cast<TO*>(out), ws_acc, ws_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_merge_stream_kernel<TO, D>), dim3(merge_grid), dim3(256), 0, stream,
+                       ctx_len, max_ctx, B, N, Hq, Hkv, pl.G, pl.rows, pl.stream_wg, ws_acc, ws_ml,
+                       static_cast<TO*>(out));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
                      0, stream, static_cast<const T*>(q), static_cast<const T*>(k_node),
                      static_cast<const T*>(v_node), static_cast<const T*>(k_cache),
@@ -571,9 +802,7 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                      static_cast<TO*>(out), ws_acc, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  constexpr int kRpb = 256 / (D / 4);
-  const unsigned mgrid = static_cast<unsigned>(B) * Hkv * ((pl.rows + kRpb - 1) / kRpb);
-  hipLaunchKernelGGL((attn_merge_kernel<TO, D>), dim3(mgrid), dim3(256), 0, stream, ctx_len, max_ctx,
+  hipLaunchKernelGGL((attn_merge_kernel<TO, D>), dim3(merge_grid), dim3(256), 0, stream, ctx_len, max_ctx,
                      pos, N, Hq, Hkv, pl.G, pl.rows, pl.nsplit, pl.split_tokens, window, ws_acc,
                      ws_ml, static_cast<TO*>(out));
   return hipGetLastError();
@@ -588,16 +817,58 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
 #define TV_ATTN_TARGET_WG 4096  // workgroups the split plan aims for
 #endif
 
+#ifndef TV_ATTN_STREAM_WG_PER_CU
+#define TV_ATTN_STREAM_WG_PER_CU 2  // resident workgroups per CU in the stream layout
+#endif
+#ifndef TV_ATTN_STREAM_MIN_TILES
+#define TV_ATTN_STREAM_MIN_TILES 16  // key tiles per stream workgroup at least
+#endif
+
+namespace {
+// compute units of the current device (256 on an MI355X; that value also
+// when no device can be queried, e.g. for a size query on a host without one)
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+}  // namespace
+
 AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int window) {
   AttnPlan p{};
   p.G = Hq / Hkv;
   p.rows = p.G * N;
   p.row_groups = (p.rows + kRows - 1) / kRows;
+  // Global layers whose rows fit one workgroup use the stream layout: every
+  // workgroup streams the same number of key tiles, so batches of mixed
+  // context length end together.  Partials: one slot per (workgroup, unit)
+  // pair a share touches, at most workgroups + units - 1.
+  const long long units = static_cast<long long>(B) * Hkv;
+  const long long tiles =
+      units * ((static_cast<long long>(max_ctx_len) + kTile - 1) / kTile + (N + kTile - 1) / kTile);
+  if (TV_ATTN_STREAM_WG_PER_CU > 0 && window <= 0 && p.row_groups == 1 && B >= 1 && B <= kMaxSeqs && tiles < (1ll << 30)) {
+    long long wg = static_cast<long long>(TV_ATTN_STREAM_WG_PER_CU) * device_cus();
+    const long long by_work = (tiles + TV_ATTN_STREAM_MIN_TILES - 1) / TV_ATTN_STREAM_MIN_TILES;
+    if (wg > by_work) wg = by_work;
+    if (wg < 1) wg = 1;
+    p.stream_wg = static_cast<int>(wg);
+    p.nsplit = 1;
+    p.split_tokens = kTile;
+    p.ws_bytes = static_cast<size_t>(wg + units - 1) * p.rows * (static_cast<size_t>(D) * 4 + 8);
+    return p;
+  }
   const int range = window > 0 ? (max_ctx_len < window ? max_ctx_len : window) : max_ctx_len;
   // aim for a few thousand workgroups, but keep each split long enough that
   // its fp32 partials stay small next to the keys it streams
-  const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  long long want = (TV_ATTN_TARGET_WG + units - 1) / units;
+  const long long units_rg = units * p.row_groups;
+  long long want = (TV_ATTN_TARGET_WG + units_rg - 1) / units_rg;
   const int min_split = TV_ATTN_MIN_SPLIT;
   long long cap = (range + min_split - 1) / min_split;
   if (cap < 1) cap = 1;

@@ -43,6 +43,7 @@ struct AttnPlan {
   int row_groups;   // ceil(rows / rows per workgroup)
   int nsplit;       // maximum context splits per (sequence, kv head)
   int split_tokens; // nominal tokens per split (multiple of the key tile)
+  int stream_wg;    // > 0: stream layout over this many workgroups, no splits
   size_t ws_bytes;  // partials
 };
 
