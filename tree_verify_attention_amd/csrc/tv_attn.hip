@@ -314,24 +314,48 @@ __device__ __forceinline__ void attn_segment(
 
     // S^T for two 16-key halves: lane holds keys 16j + 4lg + i of row lr
     f32x4_t S[2];
+    if constexpr (sizeof(T) == 2) {
+      // the two halves' products interleave (independent accumulators); key
+      // fragments are read two k-steps ahead, and scheduling fences keep the
+      // compiler from sinking the reads next to their use
+      S[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      S[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      constexpr int kAh = kQ < 2 ? kQ : 2;
+      uint4 ka[kAh + 1][2];
+      auto kread = [&](int ks, int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
+      };
+#pragma unroll
+      for (int ks = 0; ks < kAh; ++ks) {
+        ka[ks][0] = kread(ks, 0);
+        ka[ks][1] = kread(ks, 1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kQ; ++ks) {
+        if (ks + kAh < kQ) {
+          ka[(ks + kAh) % (kAh + 1)][0] = kread(ks + kAh, 0);
+          ka[(ks + kAh) % (kAh + 1)][1] = kread(ks + kAh, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][0]), qf_b[ks], S[0], 0, 0, 0);
+        S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][1]), qf_b[ks], S[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       S[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int krow = 16 * j + lr;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int ks = 0; ks < kQ; ++ks) {
-          bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(Kt + swz<T, D>(krow, ks * 64 + lg * 16)));
-          S[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf_b[ks], S[j], 0, 0, 0);
-        }
-      } else {
+      {
 #pragma unroll
         for (int ks = 0; ks < kQ; ++ks) {
           float a = *reinterpret_cast<const float*>(Kt + swz<T, D>(krow, (ks * 4 + lg) * 4));
           S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf_f[ks], S[j], 0, 0, 0);
         }
       }
+    }
     }
 
     // scale into the log2 domain and mask; a context tile that lies wholly
@@ -408,14 +432,29 @@ __device__ __forceinline__ void attn_segment(
       // column 16 dt + lr of rows 4lg + 0..3 (and 16 + 4lg + 0..3)
       const int vrow = 4 * lg + (lr >> 2);
       const int vcol = 8 * (lr & 3);
+      // value reads run two column tiles ahead of the products (fenced as above)
+      constexpr int kVA = C::kDT < 2 ? C::kDT : 2;
+      s16x4_t vlo[kVA + 1], vhi[kVA + 1];
+#pragma unroll
+      for (int dt = 0; dt < kVA; ++dt) {
+        vlo[dt] = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
+        vhi[dt] = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+      }
 #pragma unroll
       for (int dt = 0; dt < C::kDT; ++dt) {
-        const s16x4_t lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
-        const s16x4_t hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+        if (dt + kVA < C::kDT) {
+          vlo[(dt + kVA) % (kVA + 1)] = lds_read_tr16(Vt + swz<T, D>(vrow, (dt + kVA) * 32 + vcol));
+          vhi[(dt + kVA) % (kVA + 1)] =
+              lds_read_tr16(Vt + swz<T, D>(16 + vrow, (dt + kVA) * 32 + vcol));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const s16x4_t lo = vlo[dt % (kVA + 1)];
+        const s16x4_t hi = vhi[dt % (kVA + 1)];
         const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph, acc[dt], 0, 0, 0);
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, acc[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
