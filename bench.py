@@ -39,10 +39,36 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=1)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured HBM bytes per launch of the dominant kernel (rocprofv3 --pmc)")
+                    help="measured HBM bytes per global-layer attention call (rocprofv3 --pmc)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device copy of this many MiB "
+                         "(the known-size reference for HBM byte counters)")
     return ap.parse_args()
+
+
+ATTN_SRC = os.path.join(ROOT, "tree_verify_attention_amd", "csrc", "tv_attn.hip")
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
+
+
+def measured_traffic(path: str):
+    """HBM bytes per global-layer call from counter runs, if they were taken
+    on the attention source as it is now (else None)."""
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha1") != source_digest(ATTN_SRC):
+        return None
+    return t.get("bytes_per_launch")
 
 
 class Step:
@@ -220,12 +246,7 @@ def main():
     kv_global = step.kv_bytes(1)
     kv_window = step.kv_bytes(0)
     achieved = kv_global / (per_call["attn1"] * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic):
-        try:
-            traffic = json.load(open(args.traffic)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(args.traffic)
     out = {
         "metric": "verified tree nodes/sec + KV-stream HBM GB/s (% of peak), 1x MI355X",
         "value": round(nodes_per_s, 1),
@@ -249,11 +270,23 @@ def main():
                       "window_layer_GBps": round(kv_window / (per_call["attn0"] * 1e-3) / 1e9, 1),
                       "pair_GBps": round((kv_global + kv_window) / ((per_call["attn0"] + per_call["attn1"]) * 1e-3) / 1e9, 1)},
         "calls_ms": {n: round(v, 4) for n, v in per_call.items()},
-        "roofline": {"kernel": "tree_verify_attn (global layer: split + merge kernels)",
+        "roofline": {"kernel": "tree_verify_attn on the global layer: attn_stream_kernel + "
+                               "attn_merge_stream_kernel (one call, event-timed)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": kv_global},
+                     "algorithmic_bytes": kv_global,
+                     "bytes_per_unit": "8192 B of K+V per (context token, sequence): 2 x Hkv 8 x D 256 x 2 B",
+                     "call_ms": round(per_call["attn1"], 4)},
     }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_seqs)
     print(json.dumps(out), flush=True)

@@ -180,6 +180,37 @@ __device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The values of lanes l and l ^ S (S = 16 or 32), through the gfx950 lane-swap
+// instructions (VALU, no LDS round trip): the two results hold exactly that
+// pair, in an order that depends on the lane, so max and sum over them are the
+// same in both lanes of the pair.
+template <int S>
+__device__ __forceinline__ void lane_pair(float v, float& a, float& b) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    static_assert(S == 32, "lane pairs are 16 or 32 apart");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+template <int S>
+__device__ __forceinline__ float pair_max(float v) {
+  float a, b;
+  lane_pair<S>(v, a, b);
+  return fmaxf(a, b);
+}
+template <int S>
+__device__ __forceinline__ float pair_sum(float v) {
+  float a, b;
+  lane_pair<S>(v, a, b);
+  return a + b;
+}
+
 // One segment of the key stream of one (sequence, kv head, row group): the
 // context keys [k0, k1) and the node tiles [node_t0, node_t1) (32 nodes each),
 // accumulated with an online softmax.  With final_out the normalised rows go
@@ -385,8 +416,7 @@ __device__ __forceinline__ void attn_segment(
     }
     float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                      fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = pair_max<32>(pair_max<16>(mt));
     const float m_new = fmaxf(m_run, mt);
     // reference point for the exponentials (0 while the row has seen nothing)
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -472,8 +502,7 @@ __device__ __forceinline__ void attn_segment(
   }
 
   // row sum over the four lanes that share the row
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot = l_tot + __shfl_xor(l_tot, 32, 64);
+  const float l_tot = pair_sum<32>(pair_sum<16>(l_run));
   if (!row_ok) return;
 
   if (final_out) {
