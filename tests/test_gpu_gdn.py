@@ -57,9 +57,11 @@ def test_trees(lib, dtype, tree, N):
     check(lib, x, tree)
 
 
-def test_strong_state_and_gates(lib):
-    """Larger committed state and gates spread over (0, 1]."""
-    x = W.gdn_inputs(52, B=2, N=32, H=3, Dk=128, Dv=128, tree="random_parent", dtype=torch.float32,
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_strong_state_and_gates(lib, dtype):
+    """Larger committed state and gates spread over (0, 1] on deep random trees
+    (gate products far below 1, so the gate ratios of distant ancestors matter)."""
+    x = W.gdn_inputs(52, B=2, N=64, H=3, Dk=128, Dv=128, tree="random_parent", dtype=dtype,
                      device=DEV, s0_std=1.0)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(7)

@@ -14,10 +14,13 @@
 //
 // The section's (I + X) U = beta V carries the committed-state term in the
 // same system.  Node t depends only on rows of smaller depth, so the solve
-// runs level by level over depth.  Workgroup = (sequence, head, 32 output
-// columns): the columns of U and O are independent, so the state S0 is read
-// once in total while the (small) Gram terms are recomputed per column block.
-// All arithmetic is fp32.
+// runs level by level over depth.
+//
+// Two kernels.  bf16 inputs: one workgroup per (sequence, head), with the
+// dense products on MFMA (below).  fp32 inputs: workgroup = (sequence, head,
+// 32 output columns), every product as fp32 FMAs from LDS; the columns of U
+// and O are independent, so the state S0 is read once in total while the
+// (small) Gram terms are recomputed per column block.
 #include "tv_internal.h"
 
 namespace tv {
@@ -29,9 +32,7 @@ constexpr int kCB = 32;  // output columns per workgroup
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ float load_f(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float load_f(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ void store_f(float* p, size_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void store_f(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
 size_t gdn_lds_bytes(int N) {
   // s_s0 [128][32]; s_k, s_q [N][128]; s_x, s_y [N][N]; s_u, s_ks, s_qs
@@ -54,21 +55,6 @@ __device__ __forceinline__ Chunk8<T> load8(const T* p) {
 #pragma unroll
   for (int i = 0; i < static_cast<int>(sizeof(T) / 2); ++i) c.w[i] = reinterpret_cast<const uint4*>(p)[i];
   return c;
-}
-
-__device__ __forceinline__ void store8(float* dst, const Chunk8<uint16_t>& c) {
-  const uint32_t w[4] = {c.w[0].x, c.w[0].y, c.w[0].z, c.w[0].w};
-  float4 lo, hi;
-  lo.x = __uint_as_float(w[0] << 16);
-  lo.y = __uint_as_float(w[0] & 0xffff0000u);
-  lo.z = __uint_as_float(w[1] << 16);
-  lo.w = __uint_as_float(w[1] & 0xffff0000u);
-  hi.x = __uint_as_float(w[2] << 16);
-  hi.y = __uint_as_float(w[2] & 0xffff0000u);
-  hi.z = __uint_as_float(w[3] << 16);
-  hi.w = __uint_as_float(w[3] & 0xffff0000u);
-  reinterpret_cast<float4*>(dst)[0] = lo;
-  reinterpret_cast<float4*>(dst)[1] = hi;
 }
 
 __device__ __forceinline__ void store8(float* dst, const Chunk8<float>& c) {
@@ -277,6 +263,360 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: the dense products on MFMA, one workgroup per (sequence, head).
+//
+// K S0 and Q S0 are one product [Q; K] S0, formed transposed (S0^T [Q; K]^T)
+// so that S0's rows come out of LDS through the transpose read, as the value
+// tile does in the attention kernel.  S0 is fp32; it is split into two bf16
+// parts S0 = hi + lo (hi its round-to-nearest bf16, lo that of the remainder),
+// so two bf16 products with fp32 accumulation carry S0 to ~16 mantissa bits
+// while q and k are used exactly.  The Gram products [Q; K] K^T are exact bf16
+// products.  Their masks and gate ratios are applied in registers; the small
+// forward substitution and the outputs then run as vectorised LDS loops.
+constexpr int kMThreads = 512;
+constexpr int kRowB = kDk * 2;  // bytes of one bf16 row of 128
+
+typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 mbf16x4_t __attribute__((ext_vector_type(4)));
+typedef short ms16x4_t __attribute__((ext_vector_type(4)));
+typedef short ms16x8_t __attribute__((ext_vector_type(8)));
+typedef float mf32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte granules of a 256-byte bf16 row are XOR-swizzled by row, so reads
+// of one granule column from 16 rows (and transpose reads of 4 rows) spread
+// over the LDS banks
+__device__ __forceinline__ int gswz(int row, int byte) {
+  const int key = ((row & 7) << 1) | ((row >> 3) & 1);
+  return row * kRowB + (((byte >> 4) ^ key) << 4) + (byte & 15);
+}
+
+__device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
+  auto lp = (__attribute__((address_space(3))) mbf16x4_t*)(p);
+  return __builtin_bit_cast(ms16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+size_t gdn_mfma_lds_bytes(int N) {
+  const size_t np = (static_cast<size_t>(N) + 15) / 16 * 16;
+  // S0 hi + lo (bf16), later [Q; K] S0 (fp32); [Q; K] (bf16), later X and Y
+  // (fp32); V, later U (fp32); alpha, beta, gamma, log2 gamma, depth,
+  // ancestor words
+  return 2 * 128 * kRowB + 2 * np * kRowB + np * kDk * 4 + 64 * 4 * 5 + 64 * 8;
+}
+
+template <typename TO>
+__global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
+    const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NP = (N + 15) / 16 * 16;
+  unsigned char* r1 = smem;                      // S0 hi | S0 lo, then [Q; K] S0 fp32 [2NP][128]
+  unsigned char* r2 = smem + 2 * 128 * kRowB;    // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][NP]
+  float* s_u = reinterpret_cast<float*>(r2 + 2 * NP * kRowB);  // V, then U: fp32 [NP][128]
+  float* s_alpha = s_u + NP * kDk;
+  float* s_beta = s_alpha + 64;
+  float* s_gam = s_beta + 64;
+  float* s_lgam = s_gam + 64;
+  int* s_depth = reinterpret_cast<int*>(s_lgam + 64);
+  uint64_t* s_anc = reinterpret_cast<uint64_t*>(s_depth + 64);
+  __shared__ int s_maxdepth;
+
+  const int bh = blockIdx.x;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const uint64_t live = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
+
+  // ---- phase 0: S0 (split into bf16 hi and lo), q and k rows, v, gates.
+  // Every global load is issued before the first conversion or LDS store.
+  if (tid == 0) s_maxdepth = 1;
+  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk;
+  float4 f[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) f[u] = reinterpret_cast<const float4*>(s0)[tid + u * kMThreads];
+  constexpr int kQKPer = 2 * 64 * (kRowB / 16) / kMThreads;  // q / k granules per thread (at most)
+  constexpr int kVPer = 64 * (kDk / 8) / kMThreads;           // v granules per thread (at most)
+  uint4 gq[kQKPer], gv[kVPer];
+#pragma unroll
+  for (int u = 0; u < kQKPer; ++u) {
+    const int e = tid + u * kMThreads;
+    const int row = e / (kRowB / 16), gr = e % (kRowB / 16);
+    const bool isk = row >= NP;
+    const int t = isk ? row - NP : row;
+    gq[u] = make_uint4(0, 0, 0, 0);
+    if (row < 2 * NP && t < N)
+      gq[u] = *reinterpret_cast<const uint4*>((isk ? k : q) +
+                                              ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) {
+    const int e = tid + u * kMThreads;
+    const int t = e / (kDk / 8), gr = e % (kDk / 8);
+    gv[u] = make_uint4(0, 0, 0, 0);
+    if (t < N)
+      gv[u] = *reinterpret_cast<const uint4*>(v + ((static_cast<size_t>(b) * N + t) * H + h) * kDk +
+                                              gr * 8);
+  }
+  float ga = 1.0f, gb = 0.0f;
+  uint64_t gw = 0ull;
+  if (tid < N) {
+    const size_t nh = (static_cast<size_t>(b) * N + tid) * H + h;
+    ga = alpha[nh];
+    gb = beta[nh];
+    gw = anc[static_cast<size_t>(b) * N + tid];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * kMThreads;
+    const int d = e >> 5, c = (e & 31) * 4;
+    const float x[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t h0 = f32_to_bf16(x[2 * j]), h1 = f32_to_bf16(x[2 * j + 1]);
+      const uint16_t l0 = f32_to_bf16(x[2 * j] - bf16_to_f32(h0));
+      const uint16_t l1 = f32_to_bf16(x[2 * j + 1] - bf16_to_f32(h1));
+      hw[j] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+      lw[j] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+    }
+    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2*>(r1 + 128 * kRowB + gswz(d, 2 * c)) = make_uint2(lw[0], lw[1]);
+  }
+#pragma unroll
+  for (int u = 0; u < kQKPer; ++u) {
+    const int e = tid + u * kMThreads;
+    const int row = e / (kRowB / 16), gr = e % (kRowB / 16);
+    if (row < 2 * NP) *reinterpret_cast<uint4*>(r2 + gswz(row, gr * 16)) = gq[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) {
+    const int e = tid + u * kMThreads;
+    const int t = e / (kDk / 8), gr = e % (kDk / 8);
+    if (t < N) {
+      const uint4 w = gv[u];
+      float4 lo, hi;
+      lo.x = __uint_as_float(w.x << 16); lo.y = __uint_as_float(w.x & 0xffff0000u);
+      lo.z = __uint_as_float(w.y << 16); lo.w = __uint_as_float(w.y & 0xffff0000u);
+      hi.x = __uint_as_float(w.z << 16); hi.y = __uint_as_float(w.z & 0xffff0000u);
+      hi.z = __uint_as_float(w.w << 16); hi.w = __uint_as_float(w.w & 0xffff0000u);
+      reinterpret_cast<float4*>(s_u + t * kDk + gr * 8)[0] = lo;
+      reinterpret_cast<float4*>(s_u + t * kDk + gr * 8)[1] = hi;
+    }
+  }
+  if (tid < 64) {
+    const int t = tid;
+    s_alpha[t] = ga;
+    s_beta[t] = gb;
+    // keep only real, earlier nodes (ancestors precede their descendants);
+    // a node always sees itself
+    const uint64_t below = t >= 63 ? ~0ull >> 1 : ((1ull << t) - 1ull);
+    s_anc[t] = t < N ? ((gw & live & below) | (1ull << t)) : 0ull;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // gamma_t = product of alpha over t's root path; its log2 gives the gate
+    // ratio gamma_t / gamma_i of any ancestor i without a path walk (and
+    // without underflow when the product is tiny)
+    const int t = tid;
+    uint64_t m = s_anc[t];
+    float gm = 1.0f, lg2 = 0.0f;
+    while (m) {
+      const float a = s_alpha[__ffsll(static_cast<unsigned long long>(m)) - 1];
+      gm *= a;
+      lg2 += __log2f(a);
+      m &= m - 1;
+    }
+    s_gam[t] = gm;
+    s_lgam[t] = lg2;
+    const int dpt = __popcll(s_anc[t]);
+    s_depth[t] = dpt;
+    if (t < N) atomicMax(&s_maxdepth, dpt);
+  }
+
+  // ---- phase 1: [Q; K] S0 (transposed) and the Gram products on MFMA
+  const int nqks = NP;          // 8 column tiles x 2NP / 16 node tiles
+  const int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
+  mf32x4_t qks[8], gram[4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int u = wave + 8 * m;
+    qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (u < nqks) {
+      const int ct = u & 7, nt = u >> 3;
+      const int row = 16 * nt + lr;
+#pragma unroll
+      for (int ks = 0; ks < kDk / 32; ++ks) {
+        const int vrow = 32 * ks + 4 * lg + (lr >> 2);
+        const int vcol = ct * 32 + 8 * (lr & 3);
+        const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
+        const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
+        const ms16x4_t l0 = tr_read(r1 + 128 * kRowB + gswz(vrow, vcol));
+        const ms16x4_t l1 = tr_read(r1 + 128 * kRowB + gswz(vrow + 16, vcol));
+        const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
+        const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
+        const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        const ms16x8_t al = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
+        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
+                                                          qks[m], 0, 0, 0);
+        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, al), bb,
+                                                          qks[m], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int u = wave + 8 * m;
+    gram[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (u < ngram) {
+      const int kt = u % (NP / 16), rt = u / (NP / 16);
+#pragma unroll
+      for (int ks = 0; ks < kDk / 32; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(r2 + gswz(16 * rt + lr, 2 * (32 * ks + 8 * lg)));
+        const uint4 bk = *reinterpret_cast<const uint4*>(r2 + gswz(NP + 16 * kt + lr, 2 * (32 * ks + 8 * lg)));
+        gram[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, a),
+                                                           __builtin_bit_cast(mbf16x8_t, bk), gram[m],
+                                                           0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // every read of S0 and of the q / k rows is done
+
+  // results into LDS: [Q; K] S0 rows, and X, Y with their masks and gates
+  float* s_qks = reinterpret_cast<float*>(r1);   // [2NP][128]
+  float* s_x = reinterpret_cast<float*>(r2);     // [NP][NP]
+  float* s_y = s_x + NP * NP;                    // [NP][NP]
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int u = wave + 8 * m;
+    if (u < nqks) {
+      const int ct = u & 7, nt = u >> 3;
+      *reinterpret_cast<float4*>(s_qks + (16 * nt + lr) * kDk + 16 * ct + 4 * lg) =
+          make_float4(qks[m][0], qks[m][1], qks[m][2], qks[m][3]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int u = wave + 8 * m;
+    if (u < ngram) {
+      const int kt = u % (NP / 16), rt = u / (NP / 16);
+      const int i = 16 * kt + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * lg + r;
+        if (row < NP) {
+          // a query row: Y over ancestors-or-self
+          const int t = row;
+          float y = 0.0f;
+          if (t < N && i < N && ((s_anc[t] >> i) & 1ull))
+            y = __builtin_amdgcn_exp2f(s_lgam[t] - s_lgam[i]) * gram[m][r];
+          s_y[t * NP + i] = y;
+        } else {
+          // a key row: X over strict ancestors
+          const int t = row - NP;
+          float x = 0.0f;
+          if (t < N && i < N && i != t && ((s_anc[t] >> i) & 1ull))
+            x = s_beta[t] * __builtin_amdgcn_exp2f(s_lgam[t] - s_lgam[i]) * gram[m][r];
+          s_x[t * NP + i] = x;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: right-hand side beta_t (v_t - gamma_t (K S0)_t), in place of V
+  for (int e = tid; e < N * (kDk / 4); e += kMThreads) {
+    const int t = e / (kDk / 4), c = (e % (kDk / 4)) * 4;
+    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kDk + c);
+    const float4 ks = *reinterpret_cast<const float4*>(s_qks + (NP + t) * kDk + c);
+    const float bt = s_beta[t], gt = s_gam[t];
+    uu.x = bt * (uu.x - gt * ks.x);
+    uu.y = bt * (uu.y - gt * ks.y);
+    uu.z = bt * (uu.z - gt * ks.z);
+    uu.w = bt * (uu.w - gt * ks.w);
+    *reinterpret_cast<float4*>(s_u + t * kDk + c) = uu;
+  }
+  __syncthreads();
+
+  // ---- phase 3: forward substitution by depth level; thread = (row, column run)
+  const int tpr = NP <= 16 ? 32 : (NP <= 32 ? 16 : 8);  // threads per row (tpr * NP <= 512)
+  const int cpt = kDk / tpr;                              // columns per thread (4, 8 or 16)
+  const int t = tid / tpr;
+  const int c0 = (tid % tpr) * cpt;
+  const int maxdepth = s_maxdepth;
+  const bool row_ok = t < N;
+  const int dt = row_ok ? s_depth[t] : 0;
+  for (int lvl = 2; lvl <= maxdepth; ++lvl) {
+    if (row_ok && dt == lvl) {
+      uint64_t m = s_anc[t] & ~(1ull << t);
+      for (int c = c0; c < c0 + cpt; c += 4) {
+        float4 acc = *reinterpret_cast<const float4*>(s_u + t * kDk + c);
+        uint64_t mm = m;
+        while (mm) {
+          const int i = __ffsll(static_cast<unsigned long long>(mm)) - 1;
+          const float xv = s_x[t * NP + i];
+          const float4 ui = *reinterpret_cast<const float4*>(s_u + i * kDk + c);
+          acc.x = fmaf(-xv, ui.x, acc.x);
+          acc.y = fmaf(-xv, ui.y, acc.y);
+          acc.z = fmaf(-xv, ui.z, acc.z);
+          acc.w = fmaf(-xv, ui.w, acc.w);
+          mm &= mm - 1;
+        }
+        *reinterpret_cast<float4*>(s_u + t * kDk + c) = acc;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 4: o_t = gamma_t (Q S0)_t + sum over ancestors-or-self of Y U
+  if (row_ok) {
+    const uint64_t m = s_anc[t];
+    const float gt = s_gam[t];
+    for (int c = c0; c < c0 + cpt; c += 4) {
+      const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + c);
+      float4 o = make_float4(gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w);
+      uint64_t mm = m;
+      while (mm) {
+        const int i = __ffsll(static_cast<unsigned long long>(mm)) - 1;
+        const float yv = s_y[t * NP + i];
+        const float4 ui = *reinterpret_cast<const float4*>(s_u + i * kDk + c);
+        o.x = fmaf(yv, ui.x, o.x);
+        o.y = fmaf(yv, ui.y, o.y);
+        o.z = fmaf(yv, ui.z, o.z);
+        o.w = fmaf(yv, ui.w, o.w);
+        mm &= mm - 1;
+      }
+      const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + c;
+      if constexpr (sizeof(TO) == 2) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(o.x)) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(o.z)) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
+        *reinterpret_cast<uint2*>(out + off) = w;
+      } else {
+        *reinterpret_cast<float4*>(out + off) = o;
+      }
+    }
+  }
+}
+
+template <typename TO>
+hipError_t launch_gdn_mfma(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                           int H, void* out, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gdn_mfma_kernel<TO>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gdn_mfma_lds_bytes(64)));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gdn_mfma_kernel<TO>), dim3(static_cast<unsigned>(B) * H), dim3(kMThreads),
+                     gdn_mfma_lds_bytes(N), stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta, S0,
+                     anc, N, H, static_cast<TO*>(out));
+  return hipGetLastError();
+}
+
 template <typename T, typename TO>
 hipError_t launch_gdn_typed(const void* q, const void* k, const void* v, const float* alpha,
                             const float* beta, const float* S0, const uint64_t* anc, int B, int N,
@@ -301,11 +641,9 @@ hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* 
                       hipStream_t stream) {
   (void)Dk;
   if (dtype == TV_BF16 && out_dtype == TV_BF16)
-    return launch_gdn_typed<uint16_t, uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, Dv, out,
-                                                stream);
+    return launch_gdn_mfma<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_BF16 && out_dtype == TV_F32)
-    return launch_gdn_typed<uint16_t, float>(q, k, v, alpha, beta, S0, anc, B, N, H, Dv, out,
-                                             stream);
+    return launch_gdn_mfma<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_F32 && out_dtype == TV_F32)
     return launch_gdn_typed<float, float>(q, k, v, alpha, beta, S0, anc, B, N, H, Dv, out, stream);
   return hipErrorInvalidValue;
