@@ -296,12 +296,48 @@ __device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
   return __builtin_bit_cast(ms16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
+constexpr int kUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
+
+// bytes of the [Q; K] rows, later X and Y (row pitch NP + 4)
+__host__ __device__ inline size_t gdn_r2_bytes(int np) {
+  const size_t qk = 2 * static_cast<size_t>(np) * kRowB;
+  const size_t xy = 2 * static_cast<size_t>(np) * (np + 4) * 4;
+  return qk > xy ? qk : xy;
+}
+
 size_t gdn_mfma_lds_bytes(int N) {
-  const size_t np = (static_cast<size_t>(N) + 15) / 16 * 16;
+  const int np = (N + 15) / 16 * 16;
   // S0 hi + lo (bf16), later [Q; K] S0 (fp32); [Q; K] (bf16), later X and Y
-  // (fp32); V, later U (fp32); alpha, beta, gamma, log2 gamma, depth,
-  // ancestor words
-  return 2 * 128 * kRowB + 2 * np * kRowB + np * kDk * 4 + 64 * 4 * 5 + 64 * 8;
+  // (fp32); V, later the right-hand side (fp32); alpha, beta, gamma, log2
+  // gamma, depth, ancestor words
+  return 2 * 128 * kRowB + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 + 64 * 4 * 5 + 64 * 8;
+}
+
+// C = A B (+ D), NP x NP fp32 matrices of row pitch mp in LDS, on
+// v_mfma_f32_16x16x4f32; B's entries are scaled by `sb`.  Tiles are dealt to
+// the 8 waves; a lane holds column lr of rows 4 lg .. 4 lg + 3 of its tile.
+template <bool kAdd>
+__device__ __forceinline__ void gdn_mm(const float* A, const float* B, const float* Dm, float* C, int mp,
+                                       int nt, int wave, int lr, int lg, float sb) {
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    const int u = wave + 8 * mm;
+    if (u < nt * nt) {
+      const int rt = u / nt, ct = u % nt;
+      mf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kAdd) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = Dm[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr];
+      }
+      for (int ks = 0; ks < 4 * nt; ++ks) {
+        const float a = A[(16 * rt + lr) * mp + 4 * ks + lg];
+        const float bv = sb * B[(4 * ks + lg) * mp + 16 * ct + lr];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) C[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr] = acc[r];
+    }
+  }
 }
 
 template <typename TO>
@@ -312,9 +348,10 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   const int NP = (N + 15) / 16 * 16;
   unsigned char* r1 = smem;                      // S0 hi | S0 lo, then [Q; K] S0 fp32 [2NP][128]
-  unsigned char* r2 = smem + 2 * 128 * kRowB;    // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][NP]
-  float* s_u = reinterpret_cast<float*>(r2 + 2 * NP * kRowB);  // V, then U: fp32 [NP][128]
-  float* s_alpha = s_u + NP * kDk;
+  const int MP = NP + 4;                         // row pitch of the NP x NP matrices (floats)
+  unsigned char* r2 = smem + 2 * 128 * kRowB;    // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][MP]
+  float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V, then the right-hand side
+  float* s_alpha = s_u + NP * kUP;
   float* s_beta = s_alpha + 64;
   float* s_gam = s_beta + 64;
   float* s_lgam = s_gam + 64;
@@ -372,18 +409,15 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
   for (int u = 0; u < 8; ++u) {
     const int e = tid + u * kMThreads;
     const int d = e >> 5, c = (e & 31) * 4;
-    const float x[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
-    uint32_t hw[2], lw[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint16_t h0 = f32_to_bf16(x[2 * j]), h1 = f32_to_bf16(x[2 * j + 1]);
-      const uint16_t l0 = f32_to_bf16(x[2 * j] - bf16_to_f32(h0));
-      const uint16_t l1 = f32_to_bf16(x[2 * j + 1] - bf16_to_f32(h1));
-      hw[j] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-      lw[j] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-    }
-    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = make_uint2(hw[0], hw[1]);
-    *reinterpret_cast<uint2*>(r1 + 128 * kRowB + gswz(d, 2 * c)) = make_uint2(lw[0], lw[1]);
+    // hi = bf16(x) (round to nearest even, the hardware conversion), lo = bf16(x - hi)
+    const mbf16x4_t hv = {static_cast<__bf16>(f[u].x), static_cast<__bf16>(f[u].y),
+                          static_cast<__bf16>(f[u].z), static_cast<__bf16>(f[u].w)};
+    const mbf16x4_t lv = {static_cast<__bf16>(f[u].x - static_cast<float>(hv[0])),
+                          static_cast<__bf16>(f[u].y - static_cast<float>(hv[1])),
+                          static_cast<__bf16>(f[u].z - static_cast<float>(hv[2])),
+                          static_cast<__bf16>(f[u].w - static_cast<float>(hv[3]))};
+    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, hv);
+    *reinterpret_cast<uint2*>(r1 + 128 * kRowB + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, lv);
   }
 #pragma unroll
   for (int u = 0; u < kQKPer; ++u) {
@@ -395,15 +429,15 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
   for (int u = 0; u < kVPer; ++u) {
     const int e = tid + u * kMThreads;
     const int t = e / (kDk / 8), gr = e % (kDk / 8);
-    if (t < N) {
+    if (t < NP) {  // rows past N are zero (they meet zero weights in the products)
       const uint4 w = gv[u];
       float4 lo, hi;
       lo.x = __uint_as_float(w.x << 16); lo.y = __uint_as_float(w.x & 0xffff0000u);
       lo.z = __uint_as_float(w.y << 16); lo.w = __uint_as_float(w.y & 0xffff0000u);
       hi.x = __uint_as_float(w.z << 16); hi.y = __uint_as_float(w.z & 0xffff0000u);
       hi.z = __uint_as_float(w.w << 16); hi.w = __uint_as_float(w.w & 0xffff0000u);
-      reinterpret_cast<float4*>(s_u + t * kDk + gr * 8)[0] = lo;
-      reinterpret_cast<float4*>(s_u + t * kDk + gr * 8)[1] = hi;
+      reinterpret_cast<float4*>(s_u + t * kUP + gr * 8)[0] = lo;
+      reinterpret_cast<float4*>(s_u + t * kUP + gr * 8)[1] = hi;
     }
   }
   if (tid < 64) {
@@ -487,8 +521,8 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
 
   // results into LDS: [Q; K] S0 rows, and X, Y with their masks and gates
   float* s_qks = reinterpret_cast<float*>(r1);   // [2NP][128]
-  float* s_x = reinterpret_cast<float*>(r2);     // [NP][NP]
-  float* s_y = s_x + NP * NP;                    // [NP][NP]
+  float* s_x = reinterpret_cast<float*>(r2);     // [NP][MP]
+  float* s_y = s_x + NP * MP;                    // [NP][MP]
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int u = wave + 8 * m;
@@ -513,14 +547,14 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
           float y = 0.0f;
           if (t < N && i < N && ((s_anc[t] >> i) & 1ull))
             y = __builtin_amdgcn_exp2f(s_lgam[t] - s_lgam[i]) * gram[m][r];
-          s_y[t * NP + i] = y;
+          s_y[t * MP + i] = y;
         } else {
           // a key row: X over strict ancestors
           const int t = row - NP;
           float x = 0.0f;
           if (t < N && i < N && i != t && ((s_anc[t] >> i) & 1ull))
             x = s_beta[t] * __builtin_amdgcn_exp2f(s_lgam[t] - s_lgam[i]) * gram[m][r];
-          s_x[t * NP + i] = x;
+          s_x[t * MP + i] = x;
         }
       }
     }
@@ -530,73 +564,74 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
   // ---- phase 2: right-hand side beta_t (v_t - gamma_t (K S0)_t), in place of V
   for (int e = tid; e < N * (kDk / 4); e += kMThreads) {
     const int t = e / (kDk / 4), c = (e % (kDk / 4)) * 4;
-    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kDk + c);
+    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kUP + c);
     const float4 ks = *reinterpret_cast<const float4*>(s_qks + (NP + t) * kDk + c);
     const float bt = s_beta[t], gt = s_gam[t];
     uu.x = bt * (uu.x - gt * ks.x);
     uu.y = bt * (uu.y - gt * ks.y);
     uu.z = bt * (uu.z - gt * ks.z);
     uu.w = bt * (uu.w - gt * ks.w);
-    *reinterpret_cast<float4*>(s_u + t * kDk + c) = uu;
+    *reinterpret_cast<float4*>(s_u + t * kUP + c) = uu;
   }
-  __syncthreads();
+  __syncthreads();  // K S0 is no longer needed: its rows hold a third matrix below
 
-  // ---- phase 3: forward substitution by depth level; thread = (row, column run)
-  const int tpr = NP <= 16 ? 32 : (NP <= 32 ? 16 : 8);  // threads per row (tpr * NP <= 512)
-  const int cpt = kDk / tpr;                              // columns per thread (4, 8 or 16)
-  const int t = tid / tpr;
-  const int c0 = (tid % tpr) * cpt;
-  const int maxdepth = s_maxdepth;
-  const bool row_ok = t < N;
-  const int dt = row_ok ? s_depth[t] : 0;
-  for (int lvl = 2; lvl <= maxdepth; ++lvl) {
-    if (row_ok && dt == lvl) {
-      uint64_t m = s_anc[t] & ~(1ull << t);
-      for (int c = c0; c < c0 + cpt; c += 4) {
-        float4 acc = *reinterpret_cast<const float4*>(s_u + t * kDk + c);
-        uint64_t mm = m;
-        while (mm) {
-          const int i = __ffsll(static_cast<unsigned long long>(mm)) - 1;
-          const float xv = s_x[t * NP + i];
-          const float4 ui = *reinterpret_cast<const float4*>(s_u + i * kDk + c);
-          acc.x = fmaf(-xv, ui.x, acc.x);
-          acc.y = fmaf(-xv, ui.y, acc.y);
-          acc.z = fmaf(-xv, ui.z, acc.z);
-          acc.w = fmaf(-xv, ui.w, acc.w);
-          mm &= mm - 1;
-        }
-        *reinterpret_cast<float4*>(s_u + t * kDk + c) = acc;
+  // ---- phase 3: M = Y (I + X)^-1.  X only couples a node to its strict
+  // ancestors, so X^d = 0 past the tree's depth and (I + X)^-1 is the finite
+  // product of (I + (-X)^(2^j)), j < ceil(log2 depth): M starts as Y and takes
+  // one factor per step, the power by repeated squaring.  Three NP x NP
+  // buffers rotate (current M, current power, free); fp32 MFMA throughout.
+  {
+    const int maxdepth = s_maxdepth;
+    int steps = 0;
+    while ((1 << steps) < maxdepth) ++steps;
+    float* bm = s_y;                                   // M
+    float* bp = s_x;                                   // the power of X
+    float* bf = s_qks + NP * kDk;                      // free (the K S0 rows)
+    const int nt = NP / 16;
+    for (int j = 0; j < steps; ++j) {
+      if (j > 0) {
+        // next power: bf = bp bp
+        gdn_mm<false>(bp, bp, nullptr, bf, MP, nt, wave, lr, lg, 1.0f);
+        __syncthreads();
+        float* tmp = bp;
+        bp = bf;
+        bf = tmp;  // the old power is free
       }
+      // M <- M + M (-X)^(2^j): the power is X negated for j = 0, else as stored
+      gdn_mm<true>(bm, bp, bm, bf, MP, nt, wave, lr, lg, j == 0 ? -1.0f : 1.0f);
+      __syncthreads();
+      float* tmp = bm;
+      bm = bf;
+      bf = tmp;
     }
-    __syncthreads();
-  }
 
-  // ---- phase 4: o_t = gamma_t (Q S0)_t + sum over ancestors-or-self of Y U
-  if (row_ok) {
-    const uint64_t m = s_anc[t];
-    const float gt = s_gam[t];
-    for (int c = c0; c < c0 + cpt; c += 4) {
-      const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + c);
-      float4 o = make_float4(gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w);
-      uint64_t mm = m;
-      while (mm) {
-        const int i = __ffsll(static_cast<unsigned long long>(mm)) - 1;
-        const float yv = s_y[t * NP + i];
-        const float4 ui = *reinterpret_cast<const float4*>(s_u + i * kDk + c);
-        o.x = fmaf(yv, ui.x, o.x);
-        o.y = fmaf(yv, ui.y, o.y);
-        o.z = fmaf(yv, ui.z, o.z);
-        o.w = fmaf(yv, ui.w, o.w);
-        mm &= mm - 1;
-      }
-      const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + c;
-      if constexpr (sizeof(TO) == 2) {
-        uint2 w;
-        w.x = static_cast<uint32_t>(f32_to_bf16(o.x)) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
-        w.y = static_cast<uint32_t>(f32_to_bf16(o.z)) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
-        *reinterpret_cast<uint2*>(out + off) = w;
-      } else {
-        *reinterpret_cast<float4*>(out + off) = o;
+    // ---- phase 4: O^T = (right-hand side)^T M^T + gamma (Q S0)^T, tiles of
+    // 16 state columns x 16 nodes; a lane ends with 4 consecutive columns of
+    // one node's output
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int u = wave + 8 * mm;
+      if (u < 8 * nt) {
+        const int ct = u & 7, ntile = u >> 3;
+        const int t = 16 * ntile + lr;
+        const float gt = s_gam[t];
+        const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + 16 * ct + 4 * lg);
+        mf32x4_t acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
+        for (int ks = 0; ks < NP / 4; ++ks) {
+          const float a = s_u[(4 * ks + lg) * kUP + 16 * ct + lr];
+          const float bv = bm[t * MP + 4 * ks + lg];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+        }
+        if (t < N) {
+          const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * ct + 4 * lg;
+          if constexpr (sizeof(TO) == 2) {
+            const mbf16x4_t w = {static_cast<__bf16>(acc[0]), static_cast<__bf16>(acc[1]),
+                                 static_cast<__bf16>(acc[2]), static_cast<__bf16>(acc[3])};
+            *reinterpret_cast<uint2*>(out + off) = __builtin_bit_cast(uint2, w);
+          } else {
+            *reinterpret_cast<float4*>(out + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          }
+        }
       }
     }
   }
