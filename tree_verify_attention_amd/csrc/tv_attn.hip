@@ -50,19 +50,29 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <typename T, int D>
+// kTeams teams of kWaves waves share a workgroup: a ring stage holds kTeams
+// consecutive 32-key tiles, team i computes the i-th, and the teams' softmax
+// states are merged at the end (more waves per CU on short key ranges).
+template <typename T, int D, int kTeams = 1>
 struct Cfg {
   static constexpr int kEsz = sizeof(T);
   static constexpr int kRowBytes = D * kEsz;           // one key (or value) row
   static constexpr int kGran = kRowBytes / 16;          // 16-byte granules per row
   static constexpr int kSwz = (kGran < 16 ? kGran : 16) - 1;
   static constexpr int kTileBytes = kTile * kRowBytes;  // K (or V) of one tile
-  // K and V of a tile live in separate rings of kSlots slots each
+  static constexpr int kStageKeys = kTile * kTeams;     // keys per ring stage
+  static constexpr int kStageBytes = kTileBytes * kTeams;
+  static constexpr int kNW = kWaves * kTeams;           // waves per workgroup
+  // K and V of a stage live in separate rings of kSlots slots each
   static constexpr int kFit = TV_ATTN_LDS_BUDGET / (2 * kTileBytes);
   static constexpr int kSlots = kFit < 2 ? 2 : (kFit > 4 ? 4 : kFit);
-  static constexpr int kInstPerWave = kTileBytes / 1024 / kWaves;  // 1 KB per wave DMA
+  static constexpr int kInstPerWave = kStageBytes / 1024 / kNW;  // 1 KB per wave DMA
   static constexpr int kDT = D / 16;  // 16-wide output column tiles
-  static_assert(kInstPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "tile must split over waves");
+  // workgroups per CU the register budget is sized for: fp32 at D = 256 keeps
+  // 64 query and 64 accumulator registers per lane and gets the whole file
+  static constexpr int kMinWG =
+      kTeams > 1 ? 1 : ((kEsz == 4 && D == 256) ? 1 : TV_ATTN_MIN_WG);
+  static_assert(kInstPerWave >= 1 && kStageBytes % (1024 * kNW) == 0, "stage must split over waves");
   static_assert(kInstPerWave * (2 * kSlots - 1) <= 63, "vmcnt range");
 };
 
@@ -218,7 +228,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 // slot `pslot`.  s_pos holds the tree's position ids and s_pages the page
 // indices of pages k0 / 16 onwards, both filled by the caller before a
 // barrier that this routine also relies on for its own LDS.
-template <typename T, typename TO, int D>
+template <typename T, typename TO, int D, int kTeams>
 __device__ __forceinline__ void attn_segment(
     const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt_b,
@@ -227,16 +237,18 @@ __device__ __forceinline__ void attn_segment(
     int k1, int node_t0, int node_t1, int2 prng, bool final_out, size_t pslot,
     TO* __restrict__ out, float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
     unsigned char* kring, unsigned char* vring, const int* s_pages, const int* s_pos) {
-  using C = Cfg<T, D>;
+  using C = Cfg<T, D, kTeams>;
   const int tid = threadIdx.x;
-  const int nctx_tiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+  // stages: context keys in stages of kStageKeys, then node stages [node_t0, node_t1)
+  const int nctx_tiles = k1 > k0 ? (k1 - k0 + C::kStageKeys - 1) / C::kStageKeys : 0;
   const int ntiles = nctx_tiles + (node_t1 - node_t0);
   // context keys in [win_all, min_pos] are inside every row's window
   const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
   const int p0 = k0 >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int team = wave / kWaves;  // which tile of each stage this wave computes
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int R = rg * kRows + wave * 16 + lr;
+  const int R = rg * kRows + (wave % kWaves) * 16 + lr;
   const bool row_ok = R < rows;
   const int t = row_ok ? R / G : 0;
   const int hl = row_ok ? R % G : 0;
@@ -291,9 +303,9 @@ __device__ __forceinline__ void attn_segment(
   // under the swizzle.  Keys past the end of the range read a valid key
   // instead (masked later), so that LDS never holds non-finite garbage.
   auto issue = [&](int it, bool values) {
-    unsigned char* dst = (values ? vring : kring) + (it % C::kSlots) * C::kTileBytes;
+    unsigned char* dst = (values ? vring : kring) + (it % C::kSlots) * C::kStageBytes;
     const bool is_node = it >= nctx_tiles;
-    const int base = is_node ? (node_t0 + it - nctx_tiles) * kTile : k0 + it * kTile;
+    const int base = is_node ? (node_t0 + it - nctx_tiles) * C::kStageKeys : k0 + it * C::kStageKeys;
     const int lim = is_node ? N : k1;
     const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
 #pragma unroll
@@ -337,10 +349,11 @@ __device__ __forceinline__ void attn_segment(
     lds_barrier();  // keys of tile `it` have landed; every wave is done with tile it - 1
     if (it > 0 && it + C::kSlots - 1 < ntiles) issue(it + C::kSlots - 1, true);
 
-    const unsigned char* Kt = kring + (it % C::kSlots) * C::kTileBytes;
-    const unsigned char* Vt = vring + (it % C::kSlots) * C::kTileBytes;
+    const unsigned char* Kt = kring + (it % C::kSlots) * C::kStageBytes + team * C::kTileBytes;
+    const unsigned char* Vt = vring + (it % C::kSlots) * C::kStageBytes + team * C::kTileBytes;
     const bool is_node = it >= nctx_tiles;
-    const int base = is_node ? (node_t0 + it - nctx_tiles) * kTile : k0 + it * kTile;
+    const int base = (is_node ? (node_t0 + it - nctx_tiles) * C::kStageKeys : k0 + it * C::kStageKeys) +
+                     team * kTile;
     const int lim = is_node ? N : k1;
 
     // S^T for two 16-key halves: lane holds keys 16j + 4lg + i of row lr
@@ -502,7 +515,34 @@ __device__ __forceinline__ void attn_segment(
   }
 
   // row sum over the four lanes that share the row
-  const float l_tot = pair_sum<32>(pair_sum<16>(l_run));
+  float l_tot = pair_sum<32>(pair_sum<16>(l_run));
+  if constexpr (kTeams > 1) {
+    // teams above the first hand (m, l, acc) of their rows to the first team
+    // through LDS (the rings are free now); the first team merges them
+    static_assert(kTeams == 2, "two teams");
+    static_assert(kWaves * C::kDT * 64 * 16 <= C::kSlots * C::kStageBytes, "merge fits");
+    __syncthreads();  // every wave is done with the rings
+    float* mb_acc = reinterpret_cast<float*>(kring);   // [wave][dt][lane][4]
+    float2* mb_ml = reinterpret_cast<float2*>(vring);  // [wave][lane] (m, l)
+    const int wt = wave % kWaves;
+    if (team == 1) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt)
+        *reinterpret_cast<f32x4_t*>(mb_acc + ((wt * C::kDT + dt) * 64 + lane) * 4) = acc[dt];
+      mb_ml[wt * 64 + lane] = make_float2(m_run, l_tot);
+    }
+    __syncthreads();
+    if (team == 1) return;
+    const float2 o = mb_ml[wt * 64 + lane];
+    const float m_new = fmaxf(m_run, o.x);  // finite: every row sees its own node
+    const float c0 = fast_exp2(m_run - m_new), c1 = fast_exp2(o.x - m_new);
+    l_tot = l_tot * c0 + o.y * c1;
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt)
+      acc[dt] = acc[dt] * c0 +
+                *reinterpret_cast<const f32x4_t*>(mb_acc + ((wt * C::kDT + dt) * 64 + lane) * 4) * c1;
+    m_run = m_new;
+  }
   if (!row_ok) return;
 
   if (final_out) {
@@ -535,8 +575,15 @@ __device__ __forceinline__ void attn_segment(
 }
 
 
+// Teams per workgroup of the per-unit layout: two, when two stages of both
+// rings fit in 128 KB of LDS (one such workgroup per CU).
+template <typename T, int D>
+constexpr int split_teams() {
+  return 2 * 2 * 2 * kTile * D * static_cast<int>(sizeof(T)) <= 131072 ? 2 : 1;
+}
+
 template <typename T, typename TO, int D>
-__global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
+__global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_split_kernel(
     const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
     int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
@@ -544,9 +591,10 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
     int G, int rows, int row_groups, int nsplit_max, int split_tokens, int window,
     float scale_log2, int units, TO* __restrict__ out, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
-  using C = Cfg<T, D>;
-  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
-  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
+  constexpr int kSplitTeams = split_teams<T, D>();
+  using C = Cfg<T, D, kSplitTeams>;
+  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kStageBytes];
+  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kStageBytes];
   __shared__ int s_pages[kMaxPages];
   __shared__ int s_pos[64];
   __shared__ int2 s_rng;
@@ -580,11 +628,12 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_split_kernel(
   const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
   const int p0 = k0 >> 4;
   const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-  for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
+  for (int i = tid; i < min(npages, kMaxPages); i += kThreads * kSplitTeams)
     s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
 
-  attn_segment<T, TO, D>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
-                         window, scale_log2, b, g, rg, k0, k1, 0, last ? (N + kTile - 1) / kTile : 0,
+  attn_segment<T, TO, D, kSplitTeams>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G,
+                         rows, window, scale_log2, b, g, rg, k0, k1, 0,
+                         last ? (N + C::kStageKeys - 1) / C::kStageKeys : 0,
                          prng, sp.nsplit == 1,
                          (static_cast<size_t>(b) * Hkv + g) * nsplit_max + s, out, ws_acc, ws_ml,
                          kring, vring, s_pages, s_pos);
@@ -706,7 +755,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
     for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
       s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
 
-    attn_segment<T, TO, D>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
+    attn_segment<T, TO, D, 1>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
                            0, scale_log2, b, g, 0, k0, k1, n0, n1, prng,
                            t0 == 0 && t1 == tiles_b, static_cast<size_t>(w) + b * Hkv + g, out,
                            ws_acc, ws_ml, kring, vring, s_pages, s_pos);
@@ -861,7 +910,8 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                        static_cast<TO*>(out));
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+  hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads * split_teams<T, D>()),
                      0, stream, static_cast<const T*>(q), static_cast<const T*>(k_node),
                      static_cast<const T*>(v_node), static_cast<const T*>(k_cache),
                      static_cast<const T*>(v_cache), block_table, max_blocks, num_blocks, ctx_len,
