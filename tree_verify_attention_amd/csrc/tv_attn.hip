@@ -641,7 +641,7 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
 
 // Stream decomposition of a layer without a window.  The tiles of every
 // (sequence, kv head) unit -- its context keys in tiles of 32, then its node
-// tiles -- are laid end to end in unit order j = b * Hkv + g, and workgroup w
+// tiles -- are laid end to end in unit order j = g * B + b, and workgroup w
 // takes the contiguous share [w * per, (w + 1) * per) of that sequence.  Every
 // workgroup streams the same number of tiles, whatever the mix of context
 // lengths, so the grid ends together.  A workgroup walks the units its share
@@ -714,28 +714,30 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
   const int tid = threadIdx.x;
   const int ntn = (N + kTile - 1) / kTile;
   stream_prefix(ctx_len, max_ctx, B, N, s_pref);
-  const int total = s_pref[B] * Hkv;
+  const int tb_all = s_pref[B];  // tiles of one kv head over all sequences
+  const int total = tb_all * Hkv;
   const int per = (total + gridDim.x - 1) / gridDim.x;
   const int w = blockIdx.x;
   int cur = w * per;
   const int r1 = min(total, cur + per);
 
-  // first sequence whose units reach past `cur`
-  int b = 0;
-  {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_pref[mid] * Hkv <= cur) lo = mid;
-      else hi = mid - 1;
-    }
-    b = lo;
-  }
   while (cur < r1) {
-    while (cur >= s_pref[b + 1] * Hkv) ++b;
+    // units are head-major, j = g * B + b: at any moment the workgroups stream
+    // different sequences' pages rather than the heads of one page block
+    const int g = cur / tb_all;
+    const int rem = cur - g * tb_all;
+    int b = 0;
+    {
+      int lo = 0, hi = B - 1;  // last sequence starting at or before rem
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] <= rem) lo = mid;
+        else hi = mid - 1;
+      }
+      b = lo;
+    }
     const int tiles_b = s_pref[b + 1] - s_pref[b];
-    const int g = (cur - s_pref[b] * Hkv) / tiles_b;
-    const int us = s_pref[b] * Hkv + g * tiles_b;  // first tile of unit (b, g)
+    const int us = g * tb_all + s_pref[b];  // first tile of unit (b, g)
     const int t0 = cur - us;
     const int t1 = min(tiles_b, r1 - us);
     const int ctx = min(max(ctx_len[b], 0), max_ctx);
@@ -757,7 +759,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
 
     attn_segment<T, TO, D, 1>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
                            0, scale_log2, b, g, 0, k0, k1, n0, n1, prng,
-                           t0 == 0 && t1 == tiles_b, static_cast<size_t>(w) + b * Hkv + g, out,
+                           t0 == 0 && t1 == tiles_b, static_cast<size_t>(w) + g * B + b, out,
                            ws_acc, ws_ml, kring, vring, s_pages, s_pos);
     cur = us + t1;
   }
@@ -775,15 +777,16 @@ __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
   constexpr int kRpb = 256 / kTpr;  // rows per block
   __shared__ int s_pref[kMaxSeqs + 1];
   const int chunks = (rows + kRpb - 1) / kRpb;
-  const int j = blockIdx.x / chunks;
+  const int j = blockIdx.x / chunks;  // head-major unit rank g * B + b
   const int chunk = blockIdx.x % chunks;
-  const int g = j % Hkv;
-  const int b = j / Hkv;
+  const int g = j / B;
+  const int b = j % B;
   stream_prefix(ctx_len, max_ctx, B, N, s_pref);
-  const int total = s_pref[B] * Hkv;
+  const int tb_all = s_pref[B];
+  const int total = tb_all * Hkv;
   const int per = (total + nwg - 1) / nwg;
   const int tiles_b = s_pref[b + 1] - s_pref[b];
-  const int us = s_pref[b] * Hkv + g * tiles_b;
+  const int us = g * tb_all + s_pref[b];
   const int w_lo = us / per, w_hi = (us + tiles_b - 1) / per;
   if (w_lo == w_hi) return;
   const int R = chunk * kRpb + threadIdx.x / kTpr;
