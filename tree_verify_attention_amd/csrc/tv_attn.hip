@@ -695,14 +695,43 @@ __device__ __forceinline__ void stream_prefix(const int32_t* ctx_len, int max_ct
   __syncthreads();
 }
 
+// Share of workgroup w of nwg: tiles [x, y) of `total`.  Workgroups w and
+// w + nwg / 2 run on the same CU, and the lower one's loads are served first:
+// with an even grid it takes pm thousandths of the pair's tiles (500: equal
+// shares), so that both end together.  Shares are contiguous and ordered by w.
+__device__ __forceinline__ int2 stream_share(int w, int nwg, int total, int pm) {
+  int r0, len;
+  if ((nwg & 1) || pm == 500) {
+    len = (total + nwg - 1) / nwg;
+    r0 = w * len;
+  } else {
+    const int H = nwg >> 1;
+    const int pp = (total + H - 1) / H;  // tiles per pair
+    const int A = static_cast<int>((static_cast<long long>(pp) * pm + 500) / 1000);
+    r0 = w < H ? w * A : H * A + (w - H) * (pp - A);
+    len = w < H ? A : pp - A;
+  }
+  r0 = min(r0, total);
+  return make_int2(r0, min(total, r0 + len));
+}
+
+// workgroup whose share holds tile x (0 <= x < total)
+__device__ __forceinline__ int stream_owner(int x, int nwg, int total, int pm) {
+  if ((nwg & 1) || pm == 500) return x / ((total + nwg - 1) / nwg);
+  const int H = nwg >> 1;
+  const int pp = (total + H - 1) / H;
+  const int A = static_cast<int>((static_cast<long long>(pp) * pm + 500) / 1000);
+  return x < H * A ? x / A : H + (x - H * A) / (pp - A);  // pp > A there: x < H * pp
+}
+
 template <typename T, typename TO, int D>
 __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
     const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
     int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
     const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int B, int N, int Hq,
-    int Hkv, int G, int rows, float scale_log2, TO* __restrict__ out, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml) {
+    int Hkv, int G, int rows, float scale_log2, int pm, TO* __restrict__ out,
+    float* __restrict__ ws_acc, float2* __restrict__ ws_ml) {
   using C = Cfg<T, D>;
   __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
   __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
@@ -716,10 +745,10 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
   stream_prefix(ctx_len, max_ctx, B, N, s_pref);
   const int tb_all = s_pref[B];  // tiles of one kv head over all sequences
   const int total = tb_all * Hkv;
-  const int per = (total + gridDim.x - 1) / gridDim.x;
   const int w = blockIdx.x;
-  int cur = w * per;
-  const int r1 = min(total, cur + per);
+  const int2 share = stream_share(w, gridDim.x, total, pm);
+  int cur = share.x;
+  const int r1 = share.y;
 
   while (cur < r1) {
     // units are head-major, j = g * B + b: at any moment the workgroups stream
@@ -771,7 +800,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
     const int32_t* __restrict__ ctx_len, int max_ctx, int B, int N, int Hq, int Hkv, int G,
-    int rows, int nwg, const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
+    int rows, int nwg, int pm, const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
     TO* __restrict__ out) {
   constexpr int kTpr = D / 4;       // threads per row
   constexpr int kRpb = 256 / kTpr;  // rows per block
@@ -784,10 +813,10 @@ __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
   stream_prefix(ctx_len, max_ctx, B, N, s_pref);
   const int tb_all = s_pref[B];
   const int total = tb_all * Hkv;
-  const int per = (total + nwg - 1) / nwg;
   const int tiles_b = s_pref[b + 1] - s_pref[b];
   const int us = g * tb_all + s_pref[b];
-  const int w_lo = us / per, w_hi = (us + tiles_b - 1) / per;
+  const int w_lo = stream_owner(us, nwg, total, pm);
+  const int w_hi = stream_owner(us + tiles_b - 1, nwg, total, pm);
   if (w_lo == w_hi) return;
   const int R = chunk * kRpb + threadIdx.x / kTpr;
   if (R >= rows) return;
@@ -905,12 +934,12 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                        static_cast<const T*>(v_node), static_cast<const T*>(k_cache),
                        static_cast<const T*>(v_cache), block_table, max_blocks, num_blocks,
                        ctx_len, max_ctx, anc, pos, B, N, Hq, Hkv, pl.G, pl.rows, scale_log2,
-                       static_cast<TO*>(out), ws_acc, ws_ml);
+                       pl.stream_pm, static_cast<TO*>(out), ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_merge_stream_kernel<TO, D>), dim3(merge_grid), dim3(256), 0, stream,
-                       ctx_len, max_ctx, B, N, Hq, Hkv, pl.G, pl.rows, pl.stream_wg, ws_acc, ws_ml,
-                       static_cast<TO*>(out));
+                       ctx_len, max_ctx, B, N, Hq, Hkv, pl.G, pl.rows, pl.stream_wg, pl.stream_pm,
+                       ws_acc, ws_ml, static_cast<TO*>(out));
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)),
@@ -940,6 +969,9 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
 
 #ifndef TV_ATTN_STREAM_WG_PER_CU
 #define TV_ATTN_STREAM_WG_PER_CU 2  // resident workgroups per CU in the stream layout
+#endif
+#ifndef TV_ATTN_PAIR_PM
+#define TV_ATTN_PAIR_PM 535  // thousandths of a CU's tiles for the first of its two workgroups
 #endif
 #ifndef TV_ATTN_STREAM_MIN_TILES
 #define TV_ATTN_STREAM_MIN_TILES 16  // key tiles per stream workgroup at least
@@ -980,6 +1012,8 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int wi
     if (wg > by_work) wg = by_work;
     if (wg < 1) wg = 1;
     p.stream_wg = static_cast<int>(wg);
+    // a full grid of two workgroups per CU pairs workgroup w with w + CUs
+    p.stream_pm = (TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus()) ? TV_ATTN_PAIR_PM : 500;
     p.nsplit = 1;
     p.split_tokens = kTile;
     p.ws_bytes = static_cast<size_t>(wg + units - 1) * p.rows * (static_cast<size_t>(D) * 4 + 8);

@@ -44,6 +44,7 @@ struct AttnPlan {
   int nsplit;       // maximum context splits per (sequence, kv head)
   int split_tokens; // nominal tokens per split (multiple of the key tile)
   int stream_wg;    // > 0: stream layout over this many workgroups, no splits
+  int stream_pm;    // thousandths of a CU pair's tiles for its first workgroup
   size_t ws_bytes;  // partials
 };
 
