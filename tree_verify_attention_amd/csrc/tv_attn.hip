@@ -695,33 +695,67 @@ __device__ __forceinline__ void stream_prefix(const int32_t* ctx_len, int max_ct
   __syncthreads();
 }
 
-// Share of workgroup w of nwg: tiles [x, y) of `total`.  Workgroups w and
-// w + nwg / 2 run on the same CU, and the lower one's loads are served first:
-// with an even grid it takes pm thousandths of the pair's tiles (500: equal
-// shares), so that both end together.  Shares are contiguous and ordered by w.
-__device__ __forceinline__ int2 stream_share(int w, int nwg, int total, int pm) {
+// Shares of the stream layout.  Workgroups w and w + nwg / 2 run on the same
+// CU, and the first one's loads are served ahead of the second's; workgroup w
+// runs on XCD w % 8, and the odd XCDs stream a little slower than the even
+// ones.  With a grid of a multiple of 4 workgroups, the first of a CU pair
+// takes pm thousandths of the pair's tiles, and workgroups on even XCDs take
+// xm thousandths of their class's average (pm = xm = 1000 / 2 and 1000:
+// equal shares).  Shares are contiguous and ordered by w; the four sizes are
+// those of (first, even), (first, odd), (second, even), (second, odd).
+struct ShareSizes {
+  bool weighted;
+  int eq;                  // equal share, when not weighted
+  int fe, fo, se, so, H;  // sizes and pairs per half
+};
+
+__device__ __forceinline__ ShareSizes share_sizes(int nwg, int total, int pm, int xm) {
+  ShareSizes z;
+  z.weighted = (nwg & 3) == 0 && (pm != 500 || xm != 1000);
+  z.eq = (total + nwg - 1) / nwg;
+  z.H = nwg >> 1;
+  const int pp = z.weighted ? (total + z.H - 1) / z.H : 0;  // tiles per CU pair
+  const int A = static_cast<int>((static_cast<long long>(pp) * pm + 500) / 1000);
+  const int Bs = pp - A;
+  z.fe = static_cast<int>((static_cast<long long>(A) * xm + 500) / 1000);
+  z.fo = 2 * A - z.fe;
+  z.se = static_cast<int>((static_cast<long long>(Bs) * xm + 500) / 1000);
+  z.so = 2 * Bs - z.se;
+  return z;
+}
+
+// share of workgroup w: tiles [x, y) of `total`
+__device__ __forceinline__ int2 stream_share(int w, int nwg, int total, int pm, int xm) {
+  const ShareSizes z = share_sizes(nwg, total, pm, xm);
   int r0, len;
-  if ((nwg & 1) || pm == 500) {
-    len = (total + nwg - 1) / nwg;
-    r0 = w * len;
+  if (!z.weighted) {
+    r0 = w * z.eq;
+    len = z.eq;
+  } else if (w < z.H) {
+    r0 = (w >> 1) * (z.fe + z.fo) + (w & 1) * z.fe;
+    len = (w & 1) ? z.fo : z.fe;
   } else {
-    const int H = nwg >> 1;
-    const int pp = (total + H - 1) / H;  // tiles per pair
-    const int A = static_cast<int>((static_cast<long long>(pp) * pm + 500) / 1000);
-    r0 = w < H ? w * A : H * A + (w - H) * (pp - A);
-    len = w < H ? A : pp - A;
+    const int v = w - z.H;
+    r0 = (z.H >> 1) * (z.fe + z.fo) + (v >> 1) * (z.se + z.so) + (v & 1) * z.se;
+    len = (v & 1) ? z.so : z.se;
   }
   r0 = min(r0, total);
   return make_int2(r0, min(total, r0 + len));
 }
 
 // workgroup whose share holds tile x (0 <= x < total)
-__device__ __forceinline__ int stream_owner(int x, int nwg, int total, int pm) {
-  if ((nwg & 1) || pm == 500) return x / ((total + nwg - 1) / nwg);
-  const int H = nwg >> 1;
-  const int pp = (total + H - 1) / H;
-  const int A = static_cast<int>((static_cast<long long>(pp) * pm + 500) / 1000);
-  return x < H * A ? x / A : H + (x - H * A) / (pp - A);  // pp > A there: x < H * pp
+__device__ __forceinline__ int stream_owner(int x, int nwg, int total, int pm, int xm) {
+  const ShareSizes z = share_sizes(nwg, total, pm, xm);
+  if (!z.weighted) return x / z.eq;
+  const int first = (z.H >> 1) * (z.fe + z.fo);  // tiles of the first workgroups of the pairs
+  if (x < first) {
+    const int k = x / (z.fe + z.fo);
+    return 2 * k + (x - k * (z.fe + z.fo) >= z.fe ? 1 : 0);
+  }
+  // the second workgroups hold the rest: x < H * (tiles per pair), so se + so > 0
+  const int y = x - first;
+  const int k = y / (z.se + z.so);
+  return z.H + 2 * k + (y - k * (z.se + z.so) >= z.se ? 1 : 0);
 }
 
 template <typename T, typename TO, int D>
@@ -730,14 +764,13 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
     int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
     const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int B, int N, int Hq,
-    int Hkv, int G, int rows, float scale_log2, int pm, TO* __restrict__ out,
+    int Hkv, int G, int rows, float scale_log2, int pm, int xm, TO* __restrict__ out,
     float* __restrict__ ws_acc, float2* __restrict__ ws_ml) {
   using C = Cfg<T, D>;
   __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
   __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
   __shared__ int s_pages[kMaxPages];
-  __shared__ int s_pos[64];
-  __shared__ int2 s_rng;
+  __shared__ int s_pos[64];  // node positions: read only under a window, never here
   __shared__ int s_pref[kMaxSeqs + 1];
 
   const int tid = threadIdx.x;
@@ -746,7 +779,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
   const int tb_all = s_pref[B];  // tiles of one kv head over all sequences
   const int total = tb_all * Hkv;
   const int w = blockIdx.x;
-  const int2 share = stream_share(w, gridDim.x, total, pm);
+  const int2 share = stream_share(w, gridDim.x, total, pm, xm);
   int cur = share.x;
   const int r1 = share.y;
 
@@ -778,8 +811,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
 
     __syncthreads();  // the previous segment is done with every LDS buffer
     const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
-    if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
-    const int2 prng = tree_pos_range(pos_b, N, &s_rng);
+    const int2 prng = make_int2(0, 0);  // position range: only windows use it
     const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
     const int p0 = k0 >> 4;
     const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
@@ -797,15 +829,19 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
 // Merge of the stream layout: unit (b, g) covers tiles [us, us + tiles_b);
 // its segments belong to workgroups us / per .. (us + tiles_b - 1) / per and
 // sit in slots w + j.  A unit with one segment was written out directly.
+// A block merges kMergeRows rows of one unit, 16 threads per row, each thread
+// D / 64 groups of 4 columns.
+constexpr int kMergeRows = 16;
+
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
     const int32_t* __restrict__ ctx_len, int max_ctx, int B, int N, int Hq, int Hkv, int G,
-    int rows, int nwg, int pm, const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
-    TO* __restrict__ out) {
-  constexpr int kTpr = D / 4;       // threads per row
-  constexpr int kRpb = 256 / kTpr;  // rows per block
+    int rows, int nwg, int pm, int xm, const float* __restrict__ ws_acc,
+    const float2* __restrict__ ws_ml, TO* __restrict__ out) {
+  constexpr int kV = D / 64;  // float4 column groups per thread
+  static_assert(kV >= 1 && 16 * kMergeRows == 256, "merge layout");
   __shared__ int s_pref[kMaxSeqs + 1];
-  const int chunks = (rows + kRpb - 1) / kRpb;
+  const int chunks = (rows + kMergeRows - 1) / kMergeRows;
   const int j = blockIdx.x / chunks;  // head-major unit rank g * B + b
   const int chunk = blockIdx.x % chunks;
   const int g = j / B;
@@ -815,40 +851,55 @@ __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
   const int total = tb_all * Hkv;
   const int tiles_b = s_pref[b + 1] - s_pref[b];
   const int us = g * tb_all + s_pref[b];
-  const int w_lo = stream_owner(us, nwg, total, pm);
-  const int w_hi = stream_owner(us + tiles_b - 1, nwg, total, pm);
+  const int w_lo = stream_owner(us, nwg, total, pm, xm);
+  const int w_hi = stream_owner(us + tiles_b - 1, nwg, total, pm, xm);
   if (w_lo == w_hi) return;
-  const int R = chunk * kRpb + threadIdx.x / kTpr;
+  const int R = chunk * kMergeRows + threadIdx.x / 16;
   if (R >= rows) return;
-  const int d0 = (threadIdx.x % kTpr) * 4;
+  const int c0 = (threadIdx.x % 16) * 4;
   float mx = -INFINITY, L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+  float4 o[kV];
+#pragma unroll
+  for (int k = 0; k < kV; ++k) o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
   for (int w = w_lo; w <= w_hi; ++w) {
+    const int2 sh = stream_share(w, nwg, total, pm, xm);
+    if (sh.x == sh.y) continue;  // an empty share left no partial
     const size_t ub = (static_cast<size_t>(w) + j) * rows + R;
     const float2 ml = ws_ml[ub];
-    const float4 a = *reinterpret_cast<const float4*>(ws_acc + ub * D + d0);
+    float4 a[kV];
+#pragma unroll
+    for (int k = 0; k < kV; ++k) a[k] = *reinterpret_cast<const float4*>(ws_acc + ub * D + c0 + 64 * k);
     if (ml.x == -INFINITY) continue;  // this segment saw no key of the row
     const float m_new = fmaxf(mx, ml.x);
     const float c_old = fast_exp2(mx - m_new);
     const float c_new = fast_exp2(ml.x - m_new);
     L = L * c_old + ml.y * c_new;
-    o.x = o.x * c_old + a.x * c_new;
-    o.y = o.y * c_old + a.y * c_new;
-    o.z = o.z * c_old + a.z * c_new;
-    o.w = o.w * c_old + a.w * c_new;
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      o[k].x = o[k].x * c_old + a[k].x * c_new;
+      o[k].y = o[k].y * c_old + a[k].y * c_new;
+      o[k].z = o[k].z * c_old + a[k].z * c_new;
+      o[k].w = o[k].w * c_old + a[k].w * c_new;
+    }
     mx = m_new;
   }
   const float inv = 1.0f / L;
   const int t = R / G, hl = R % G;
-  TO* op = out + ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D + d0;
-  if constexpr (sizeof(TO) == 2) {
-    uint2 wv;
-    wv.x = static_cast<uint32_t>(f32_to_bf16(o.x * inv)) | (static_cast<uint32_t>(f32_to_bf16(o.y * inv)) << 16);
-    wv.y = static_cast<uint32_t>(f32_to_bf16(o.z * inv)) | (static_cast<uint32_t>(f32_to_bf16(o.w * inv)) << 16);
-    *reinterpret_cast<uint2*>(op) = wv;
-  } else {
-    *reinterpret_cast<float4*>(op) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  TO* op = out + ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D + c0;
+#pragma unroll
+  for (int k = 0; k < kV; ++k) {
+    if constexpr (sizeof(TO) == 2) {
+      uint2 wv;
+      wv.x = static_cast<uint32_t>(f32_to_bf16(o[k].x * inv)) |
+             (static_cast<uint32_t>(f32_to_bf16(o[k].y * inv)) << 16);
+      wv.y = static_cast<uint32_t>(f32_to_bf16(o[k].z * inv)) |
+             (static_cast<uint32_t>(f32_to_bf16(o[k].w * inv)) << 16);
+      *reinterpret_cast<uint2*>(op + 64 * k) = wv;
+    } else {
+      *reinterpret_cast<float4*>(op + 64 * k) =
+          make_float4(o[k].x * inv, o[k].y * inv, o[k].z * inv, o[k].w * inv);
+    }
   }
 }
 
@@ -934,12 +985,14 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                        static_cast<const T*>(v_node), static_cast<const T*>(k_cache),
                        static_cast<const T*>(v_cache), block_table, max_blocks, num_blocks,
                        ctx_len, max_ctx, anc, pos, B, N, Hq, Hkv, pl.G, pl.rows, scale_log2,
-                       pl.stream_pm, static_cast<TO*>(out), ws_acc, ws_ml);
+                       pl.stream_pm, pl.stream_xm, static_cast<TO*>(out), ws_acc, ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_merge_stream_kernel<TO, D>), dim3(merge_grid), dim3(256), 0, stream,
+    const unsigned sm_grid =
+        static_cast<unsigned>(B) * Hkv * ((pl.rows + kMergeRows - 1) / kMergeRows);
+    hipLaunchKernelGGL((attn_merge_stream_kernel<TO, D>), dim3(sm_grid), dim3(256), 0, stream,
                        ctx_len, max_ctx, B, N, Hq, Hkv, pl.G, pl.rows, pl.stream_wg, pl.stream_pm,
-                       ws_acc, ws_ml, static_cast<TO*>(out));
+                       pl.stream_xm, ws_acc, ws_ml, static_cast<TO*>(out));
     return hipGetLastError();
   }
   hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)),
@@ -973,6 +1026,11 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
 #ifndef TV_ATTN_PAIR_PM
 #define TV_ATTN_PAIR_PM 535  // thousandths of a CU's tiles for the first of its two workgroups
 #endif
+#ifndef TV_ATTN_XCD_PM
+#define TV_ATTN_XCD_PM 1020  // thousandths of the average share for workgroups on even XCDs
+#endif
+static_assert(TV_ATTN_PAIR_PM >= 500 && TV_ATTN_PAIR_PM < 1000, "pair weight");
+static_assert(TV_ATTN_XCD_PM >= 500 && TV_ATTN_XCD_PM <= 1500, "XCD weight");
 #ifndef TV_ATTN_STREAM_MIN_TILES
 #define TV_ATTN_STREAM_MIN_TILES 16  // key tiles per stream workgroup at least
 #endif
@@ -1013,7 +1071,9 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int wi
     if (wg < 1) wg = 1;
     p.stream_wg = static_cast<int>(wg);
     // a full grid of two workgroups per CU pairs workgroup w with w + CUs
-    p.stream_pm = (TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus()) ? TV_ATTN_PAIR_PM : 500;
+    const bool full = TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus();
+    p.stream_pm = full ? TV_ATTN_PAIR_PM : 500;
+    p.stream_xm = full ? TV_ATTN_XCD_PM : 1000;
     p.nsplit = 1;
     p.split_tokens = kTile;
     p.ws_bytes = static_cast<size_t>(wg + units - 1) * p.rows * (static_cast<size_t>(D) * 4 + 8);

@@ -45,6 +45,7 @@ struct AttnPlan {
   int split_tokens; // nominal tokens per split (multiple of the key tile)
   int stream_wg;    // > 0: stream layout over this many workgroups, no splits
   int stream_pm;    // thousandths of a CU pair's tiles for its first workgroup
+  int stream_xm;    // thousandths of the average share for workgroups on even XCDs
   size_t ws_bytes;  // partials
 };
 
