@@ -221,6 +221,70 @@ __device__ __forceinline__ float pair_sum(float v) {
   return a + b;
 }
 
+// Query fragments (MFMA B operand: row lr, 8 (bf16) or 1 (fp32) dims per k
+// step), position and ancestor word of one query row.  Loaded ahead of the
+// plan and the page indices, so that these loads overlap theirs.
+template <typename T, int D>
+struct RowIn {
+  static constexpr int kQ = (sizeof(T) == 2) ? D / 32 : D / 4;
+  bf16x8_t qb[sizeof(T) == 2 ? kQ : 1];
+  float qf[sizeof(T) == 4 ? kQ : 1];
+  int pos;
+  uint64_t anc;
+};
+
+// this lane's query row of row group rg of unit (b, g): R = rg * kRows + 16 *
+// (wave within its team) + lr, node R / G, query head g * G + R % G
+template <typename T, int D>
+__device__ __forceinline__ RowIn<T, D> row_in(const T* __restrict__ q,
+                                              const int32_t* __restrict__ pos_b,
+                                              const uint64_t* __restrict__ anc, int b, int g,
+                                              int rg, int N, int Hq, int G, int rows) {
+  RowIn<T, D> ri;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int R = rg * kRows + (wave % kWaves) * 16 + lr;
+  const bool row_ok = R < rows;
+  const int t = row_ok ? R / G : 0;
+  const int hl = row_ok ? R % G : 0;
+  const size_t qoff = ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < RowIn<T, D>::kQ; ++ks) {
+      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(q + qoff + ks * 32 + lg * 8)
+                       : make_uint4(0, 0, 0, 0);
+      ri.qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < RowIn<T, D>::kQ; ++ks) ri.qf[ks] = row_ok ? q[qoff + ks * 4 + lg] : 0.0f;
+  }
+  ri.pos = pos_b[t];
+  ri.anc = anc[static_cast<size_t>(b) * N + t];
+  return ri;
+}
+
+// page indices [p0, p0 + npages) of one sequence into s_pages (as far as it
+// reaches), clamped into the pool; all loads go out before the first store
+template <int NT>
+__device__ __forceinline__ void fill_pages(int* s_pages, const int32_t* __restrict__ bt_b, int p0,
+                                           int npages, int num_blocks) {
+  constexpr int kPer = kMaxPages / NT;
+  static_assert(kPer * NT == kMaxPages, "page cache layout");
+  const int n = min(npages, kMaxPages);
+  int v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = threadIdx.x + k * NT;
+    v[k] = i < n ? bt_b[p0 + i] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < n) s_pages[i] = min(max(v[k], 0), num_blocks - 1);
+  }
+}
+
 // One segment of the key stream of one (sequence, kv head, row group): the
 // context keys [k0, k1) and the node tiles [node_t0, node_t1) (32 nodes each),
 // accumulated with an online softmax.  With final_out the normalised rows go
@@ -230,7 +294,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 // barrier that this routine also relies on for its own LDS.
 template <typename T, typename TO, int D, int kTeams>
 __device__ __forceinline__ void attn_segment(
-    const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
+    const RowIn<T, D>& ri, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt_b,
     int num_blocks, const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos_b, int N,
     int Hq, int Hkv, int G, int rows, int window, float scale_log2, int b, int g, int rg, int k0,
@@ -252,25 +316,16 @@ __device__ __forceinline__ void attn_segment(
   const bool row_ok = R < rows;
   const int t = row_ok ? R / G : 0;
   const int hl = row_ok ? R % G : 0;
-  const int row_pos = pos_b[t];
-  const uint64_t row_anc = anc[static_cast<size_t>(b) * N + t];
   const size_t qoff = ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D;
-
-  // query fragments (MFMA B operand): row lr, 8 (bf16) or 1 (fp32) dims per k step
-  constexpr int kQ = (sizeof(T) == 2) ? D / 32 : D / 4;
+  constexpr int kQ = RowIn<T, D>::kQ;
   bf16x8_t qf_b[sizeof(T) == 2 ? kQ : 1];
   float qf_f[sizeof(T) == 4 ? kQ : 1];
-  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int ks = 0; ks < kQ; ++ks) {
-      uint4 v = row_ok ? *reinterpret_cast<const uint4*>(q + qoff + ks * 32 + lg * 8)
-                       : make_uint4(0, 0, 0, 0);
-      qf_b[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  } else {
+  for (int ks = 0; ks < (sizeof(T) == 2 ? kQ : 1); ++ks) qf_b[ks] = ri.qb[ks];
 #pragma unroll
-    for (int ks = 0; ks < kQ; ++ks) qf_f[ks] = row_ok ? q[qoff + ks * 4 + lg] : 0.0f;
-  }
+  for (int ks = 0; ks < (sizeof(T) == 4 ? kQ : 1); ++ks) qf_f[ks] = ri.qf[ks];
+  const int row_pos = ri.pos;
+  const uint64_t row_anc = ri.anc;
   // make the query and row loads complete here, so that the compiler's wait
   // bookkeeping does not place a full drain inside the key loop
   if constexpr (sizeof(T) == 2) {
@@ -616,9 +671,12 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
 
   const int tid = threadIdx.x;
   const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
+  // the context length and this lane's query row go out with the tree positions
+  const int ctx_raw = ctx_len[b];
+  const RowIn<T, D> ri = row_in<T, D>(q, pos_b, anc, b, g, rg, N, Hq, G, rows);
   if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
   const int2 prng = tree_pos_range(pos_b, N, &s_rng);
-  const SeqPlan sp = seq_plan(ctx_len[b], max_ctx, window, prng.x, nsplit_max, split_tokens);
+  const SeqPlan sp = seq_plan(ctx_raw, max_ctx, window, prng.x, nsplit_max, split_tokens);
   if (s >= sp.nsplit) return;  // uniform over the workgroup
   const int k0 = sp.start + s * sp.split_len;
   const int k1 = min(k0 + sp.split_len, sp.end);
@@ -628,10 +686,9 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
   const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
   const int p0 = k0 >> 4;
   const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-  for (int i = tid; i < min(npages, kMaxPages); i += kThreads * kSplitTeams)
-    s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
+  fill_pages<kThreads * kSplitTeams>(s_pages, bt_b, p0, npages, num_blocks);
 
-  attn_segment<T, TO, D, kSplitTeams>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G,
+  attn_segment<T, TO, D, kSplitTeams>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G,
                          rows, window, scale_log2, b, g, rg, k0, k1, 0,
                          last ? (N + C::kStageKeys - 1) / C::kStageKeys : 0,
                          prng, sp.nsplit == 1,
@@ -658,7 +715,7 @@ struct StreamLayout {
 // tiles of sequence b's units and their start offsets: s_pref[b] = tiles of
 // sequences before b (one kv head each), filled for b = 0..B
 __device__ __forceinline__ void stream_prefix(const int32_t* ctx_len, int max_ctx, int B, int N,
-                                              int* s_pref) {
+                                              int* s_pref, int* s_ctx = nullptr) {
   const int tid = threadIdx.x;
   const int ntn = (N + kTile - 1) / kTile;
   // each thread owns up to 4 consecutive sequences
@@ -669,6 +726,7 @@ __device__ __forceinline__ void stream_prefix(const int32_t* ctx_len, int max_ct
     int tl = 0;
     if (b < B) {
       const int ctx = min(max(ctx_len[b], 0), max_ctx);
+      if (s_ctx) s_ctx[b] = ctx;
       tl = (ctx + kTile - 1) / kTile + ntn;
     }
     own[i] = tl;
@@ -758,8 +816,15 @@ __device__ __forceinline__ int stream_owner(int x, int nwg, int total, int pm, i
   return z.H + 2 * k + (y - k * (z.se + z.so) >= z.se ? 1 : 0);
 }
 
+// workgroups per CU the stream kernel's register budget is sized for (fp32
+// inputs from D = 128 on need more than half the register file)
+template <typename T, int D>
+constexpr int stream_min_wg() {
+  return (sizeof(T) == 4 && D >= 128) ? 1 : TV_ATTN_MIN_WG;
+}
+
 template <typename T, typename TO, int D>
-__global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
+__global__ __launch_bounds__(kThreads, (stream_min_wg<T, D>())) void attn_stream_kernel(
     const T* __restrict__ q, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt,
     int max_blocks, int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
@@ -772,10 +837,11 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
   __shared__ int s_pages[kMaxPages];
   __shared__ int s_pos[64];  // node positions: read only under a window, never here
   __shared__ int s_pref[kMaxSeqs + 1];
+  __shared__ int s_ctx[kMaxSeqs + 1];
 
   const int tid = threadIdx.x;
   const int ntn = (N + kTile - 1) / kTile;
-  stream_prefix(ctx_len, max_ctx, B, N, s_pref);
+  stream_prefix(ctx_len, max_ctx, B, N, s_pref, s_ctx);
   const int tb_all = s_pref[B];  // tiles of one kv head over all sequences
   const int total = tb_all * Hkv;
   const int w = blockIdx.x;
@@ -802,7 +868,7 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
     const int us = g * tb_all + s_pref[b];  // first tile of unit (b, g)
     const int t0 = cur - us;
     const int t1 = min(tiles_b, r1 - us);
-    const int ctx = min(max(ctx_len[b], 0), max_ctx);
+    const int ctx = s_ctx[b];
     const int nct = tiles_b - ntn;  // context tiles of the unit
     const int k0 = min(min(t0, nct) * kTile, ctx);
     const int k1 = min(min(t1, nct) * kTile, ctx);
@@ -812,13 +878,14 @@ __global__ __launch_bounds__(kThreads, TV_ATTN_MIN_WG) void attn_stream_kernel(
     __syncthreads();  // the previous segment is done with every LDS buffer
     const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
     const int2 prng = make_int2(0, 0);  // position range: only windows use it
+    // the query rows and the page indices go out together
+    const RowIn<T, D> ri = row_in<T, D>(q, pos_b, anc, b, g, 0, N, Hq, G, rows);
     const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
     const int p0 = k0 >> 4;
     const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-    for (int i = tid; i < min(npages, kMaxPages); i += kThreads)
-      s_pages[i] = min(max(bt_b[p0 + i], 0), num_blocks - 1);
+    fill_pages<kThreads>(s_pages, bt_b, p0, npages, num_blocks);
 
-    attn_segment<T, TO, D, 1>(q, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
+    attn_segment<T, TO, D, 1>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
                            0, scale_log2, b, g, 0, k0, k1, n0, n1, prng,
                            t0 == 0 && t1 == tiles_b, static_cast<size_t>(w) + g * B + b, out,
                            ws_acc, ws_ml, kring, vring, s_pages, s_pos);
