@@ -106,3 +106,31 @@ def gdn_tree_solve(q, k, v, alpha, beta, S0, parent):
             U = Ut - W @ S0[b, h]
             out[b, :, h] = gamma[:, None] * (Qh @ S0[b, h]) + Y @ U
     return out
+
+
+def gdn_commit(k, v, alpha, beta, S0, accepted_nodes, num_accepted):
+    """The committed state after the walk: the same recurrence, run as a chain
+    over the accepted nodes in order (each the child of the one before, the
+    first a child of the last accepted token), starting from S0.  With no
+    accepted node the state stays S0.  This is the deferred commit of the
+    same section: the state is published only once the accepted branch is
+    known.
+
+    k [B, N, H, Dk]; v [B, N, H, Dv]; alpha, beta [B, N, H]; S0 [B, H, Dk, Dv];
+    accepted_nodes [B, N] (first num_accepted[b] entries valid);
+    num_accepted [B].  Returns S [B, H, Dk, Dv] float64."""
+    k, v, alpha, beta, S0 = (np.asarray(x, dtype=np.float64) for x in (k, v, alpha, beta, S0))
+    acc = np.asarray(accepted_nodes)
+    na = np.asarray(num_accepted)
+    B, N, H, Dk = k.shape
+    S = S0.copy()
+    for b in range(B):
+        for h in range(H):
+            St = S0[b, h].copy()
+            for s in range(int(na[b])):
+                t = int(acc[b, s])
+                kt, vt = k[b, t, h], v[b, t, h]
+                a, be = alpha[b, t, h], beta[b, t, h]
+                St = a * (St - be * np.outer(kt, kt @ St)) + be * np.outer(kt, vt)
+            S[b, h] = St
+    return S

@@ -134,3 +134,77 @@ def test_triangular_solve_form_matches_recurrence(tree, n):
     o1 = G.gdn_tree(q, k, v, a, b, S0, par)
     o2 = G.gdn_tree_solve(q, k, v, a, b, S0, par)
     np.testing.assert_allclose(o2, o1, rtol=1e-10, atol=1e-11)
+
+
+# ---- deferred state commit (the chain over the accepted nodes) ----
+
+def _root_path(parent_b, t):
+    p, cur = [], t
+    while cur >= 0:
+        p.append(cur)
+        cur = int(parent_b[cur])
+    return p[::-1]
+
+
+def test_commit_without_accept_keeps_s0():
+    (q, k, v, a, b, S0), par = _inputs()
+    acc = np.full(par.shape, -1)
+    S = G.gdn_commit(k, v, a, b, S0, acc, np.zeros(par.shape[0], dtype=int))
+    np.testing.assert_array_equal(S, S0)
+
+
+@pytest.mark.parametrize("tree", ["random_parent", "chain"])
+def test_commit_equals_tree_state_of_last_accepted(tree):
+    """Committing the root path of node t reproduces the state the tree
+    recurrence holds at t: its output for any query equals S^T q (checked
+    through both tree oracles, the plain recurrence and the solve form)."""
+    (q, k, v, a, b, S0), par = _inputs(N=12, tree=tree)
+    B, N, H = q.shape[:3]
+    rng = np.random.default_rng(3)
+    acc = np.full((B, N), -1)
+    na = np.zeros(B, dtype=int)
+    last = []
+    for bb in range(B):
+        t = int(rng.integers(0, N))
+        path = _root_path(par[bb], t)
+        acc[bb, :len(path)] = path
+        na[bb] = len(path)
+        last.append(t)
+    S = G.gdn_commit(k, v, a, b, S0, acc, na)
+    o_plain = G.gdn_tree(q, k, v, a, b, S0, par)
+    o_solve = G.gdn_tree_solve(q, k, v, a, b, S0, par)
+    for bb in range(B):
+        t = last[bb]
+        for h in range(H):
+            np.testing.assert_allclose(S[bb, h].T @ q[bb, t, h], o_plain[bb, t, h], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(S[bb, h].T @ q[bb, t, h], o_solve[bb, t, h], rtol=1e-9, atol=1e-10)
+
+
+def test_commit_beta_zero_is_pure_decay():
+    (q, k, v, a, b, S0), par = _inputs(N=9, tree="chain")
+    b[:] = 0.0
+    B = q.shape[0]
+    acc = np.tile(np.arange(9), (B, 1))
+    na = np.array([9, 4][:B])
+    S = G.gdn_commit(k, v, a, b, S0, acc, na)
+    for bb in range(B):
+        for h in range(q.shape[2]):
+            gamma = np.prod(a[bb, :na[bb], h])
+            np.testing.assert_allclose(S[bb, h], gamma * S0[bb, h], rtol=1e-13, atol=1e-15)
+
+
+def test_commit_orthonormal_keys_recall_every_value():
+    """alpha = 1, beta = 1 and orthonormal keys along the accepted chain: each
+    write replaces the value stored under its key and leaves the others, so
+    S^T k_i = v_i for every accepted node i."""
+    (q, k, v, a, b, S0), par = _inputs(B=1, N=5, H=2, Dk=8, Dv=6, tree="chain")
+    rng = np.random.default_rng(11)
+    for h in range(2):
+        Qm, _ = np.linalg.qr(rng.standard_normal((8, 5)))
+        k[0, :, h] = Qm.T
+    a[:] = 1.0
+    b[:] = 1.0
+    S = G.gdn_commit(k, v, a, b, S0, np.arange(5)[None], np.array([5]))
+    for h in range(2):
+        for i in range(5):
+            np.testing.assert_allclose(S[0, h].T @ k[0, i, h], v[0, i, h], rtol=1e-12, atol=1e-12)
