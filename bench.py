@@ -156,6 +156,53 @@ class Step:
         mark("gdn", 1)
 
 
+def next_rows(step: Step, dev, reps: int) -> dict:
+    """The commits after the walk, outside the timed step: the GDN state
+    advanced over walk-shaped accepted paths (root paths of random nodes), and
+    the same paths' keys and values of the global layer copied into a small
+    pool of two fresh pages per sequence (the step's own caches stay as they
+    are).  Event-timed averages over `reps` calls."""
+    tv = step.tv
+    from synth import workloads as W
+    acc, na = W.accepted_paths(3, step.trees.parent)
+    acc_t = torch.from_numpy(acc).to(dev)
+    na_t = torch.from_numpy(na).to(dev)
+    g = step.gdn
+    S_out = torch.empty_like(g.S0)
+    x = step.layers[1]
+    B = step.B
+    ctx = x.ctx_len.cpu().numpy().astype(np.int64)
+    width = int((ctx.max() + step.N + 15) // 16 + 1)
+    table = np.full((B, width), -1, dtype=np.int32)
+    for b in range(B):
+        table[b, ctx[b] // 16] = 2 * b
+        table[b, ctx[b] // 16 + 1] = 2 * b + 1
+    table_t = torch.from_numpy(table).to(dev)
+    pool_k = torch.zeros(2 * B, x.Hkv, 16, x.D, dtype=x.k_node.dtype, device=dev)
+    pool_v = torch.zeros_like(pool_k)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / reps
+
+    gms = timed(lambda: tv.tree_gdn_commit(g.k, g.v, g.alpha, g.beta, g.S0, acc_t, na_t, out=S_out))
+    kms = timed(lambda: tv.tree_kv_commit(x.k_node, x.v_node, acc_t, na_t, x.ctx_len, table_t, pool_k, pool_v))
+    gbytes = 2 * g.S0.numel() * 4  # the state read and written once
+    kbytes = int(na.sum()) * 2 * x.Hkv * x.D * x.k_node.element_size() * 2  # rows read and written
+    return {"accepted_per_seq_mean": round(float(na.mean()), 2),
+            "gdn_commit": {"ms": round(gms, 4), "bytes": gbytes, "GBps": round(gbytes / (gms * 1e-3) / 1e9, 1),
+                           "frac_of_8TBps": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "kv_commit": {"ms": round(kms, 4), "bytes": kbytes}}
+
+
 def cpu_baseline(step: Step, nseq: int):
     """The oracle on the first `nseq` sequences of the same step (mask, both
     attention layers, walk, GDN), timed on this host's cores."""
@@ -278,6 +325,7 @@ def main():
                      "bytes_per_unit": "8192 B of K+V per (context token, sequence): 2 x Hkv 8 x D 256 x 2 B",
                      "call_ms": round(per_call["attn1"], 4)},
     }
+    out["next_rows"] = next_rows(step, dev, args.steps)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

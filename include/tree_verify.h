@@ -196,6 +196,62 @@ tv_status tree_walk_accept(const int32_t* tokens, const int32_t* parent,
                            void* workspace, size_t workspace_bytes,
                            tv_stream stream);
 
+/* ------------------------------------------------------------------------
+ * tree_gdn_commit — the Gated DeltaNet state after the walk.
+ *
+ * DFlash-TfM summary (gist.science, "Trees from Marginals"), section
+ * "3. Rollback-vrije Boom-verificatie voor GDN": the verify pass writes no
+ * state; once the accepted branch is known, the committed state advances
+ * along it by S <- alpha_t (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T for
+ * the accepted nodes t in order (the first a child of the last accepted
+ * token).  With no accepted node the state stays S0.
+ *
+ *   k          [B, N, H, Dk]   dtype (the verify pass's keys)
+ *   v          [B, N, H, Dv]   dtype
+ *   alpha      float [B, N, H] gates
+ *   beta       float [B, N, H] write strengths
+ *   S0         float [B, H, Dk, Dv] committed state before the step
+ *   accepted_nodes int32 [B, N]  from tree_walk_accept (first num_accepted
+ *                                entries used; indices are clamped into [0, N))
+ *   num_accepted   int32 [B]     from tree_walk_accept (clamped into [0, N])
+ *   S_out      float [B, H, Dk, Dv] out: the new committed state; may be S0
+ *              itself (each (sequence, head) block is read before it is written)
+ * Supported: 1 <= N <= TV_MAX_NODES, Dk == Dv == 128, dtype TV_F32 or TV_BF16.
+ * ------------------------------------------------------------------------ */
+tv_status tree_gdn_commit(const void* k, const void* v, const float* alpha,
+                          const float* beta, const float* S0,
+                          const int32_t* accepted_nodes, const int32_t* num_accepted,
+                          int32_t B, int32_t N, int32_t H, int32_t Dk, int32_t Dv,
+                          tv_dtype dtype, float* S_out, tv_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tree_kv_commit — the accepted path's keys and values into the paged cache.
+ *
+ * Serve-integration spec, layout contract and "3. Rejection sampler: tree
+ * walk": accepted node s (depth s + 1) has position id ctx_len - 1 + depth =
+ * ctx_len + s.  Its key and value rows of every kv head, as the verify pass
+ * computed them, are copied bit for bit into slot (ctx_len + s) % 16 of page
+ * block_table[b][(ctx_len + s) / 16].  The caller allocates the pages; no
+ * other cache entry changes.
+ *
+ *   k_node, v_node [B, N, Hkv, D]   dtype, as given to tree_verify_attn
+ *   accepted_nodes int32 [B, N], num_accepted int32 [B]  from tree_walk_accept
+ *   ctx_len        int32 [B]        context length before the step
+ *   block_table    int32 [B, max_blocks_per_seq]
+ *   k_cache, v_cache [num_blocks, Hkv, 16, D]  dtype, updated in place
+ * Entries past num_accepted, node indices outside [0, N), negative positions
+ * and positions whose page index lies outside the table or the pool are not
+ * written.  All four K/V pointers must be 16-byte aligned.
+ * Supported: 1 <= N <= TV_MAX_NODES, D in {64, 128, 256}, block_size == 16,
+ * dtype TV_F32 or TV_BF16.
+ * ------------------------------------------------------------------------ */
+tv_status tree_kv_commit(const void* k_node, const void* v_node,
+                         const int32_t* accepted_nodes, const int32_t* num_accepted,
+                         const int32_t* ctx_len, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, int32_t num_blocks, int32_t B,
+                         int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
+                         tv_dtype dtype, void* k_cache, void* v_cache, tv_stream stream);
+
 /* Static description of a status code. */
 const char* tv_status_string(tv_status s);
 

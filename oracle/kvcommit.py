@@ -10,7 +10,8 @@ are copied into the page the block table gives for that position.
 Readings: position j of sequence b lives in page block_table[b][j // 16],
 slot j % 16, of the [num_blocks, Hkv, 16, D] caches (as in the attention
 oracle); the caller has allocated the pages; a position whose page index is
-outside the pool is not written.
+outside the table or the pool, or a node index outside [0, N), is not
+written.
 
 Test infrastructure: only tests, smoke() and the benchmark's CPU baseline use
 this module.
@@ -34,6 +35,8 @@ def kv_commit(k_cache, v_cache, k_node, v_node, accepted_nodes, num_accepted, ct
         for s in range(int(num_accepted[b])):
             t = int(accepted_nodes[b, s])
             p = int(ctx_len[b]) + s
+            if not 0 <= t < k_node.shape[1] or p < 0 or p // BLOCK >= block_table.shape[1]:
+                continue
             page = int(block_table[b, p // BLOCK])
             if not 0 <= page < kc.shape[0]:
                 continue

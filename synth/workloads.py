@@ -25,6 +25,7 @@ BLOCK = 16  # tokens per KV page
 # tensor tags for the PCG64 streams
 TAG_TREE, TAG_CTX, TAG_PERM, TAG_Q, TAG_KN, TAG_VN, TAG_KC, TAG_VC, TAG_LOGIT, TAG_PLANT = range(10)
 TAG_GQ, TAG_GK, TAG_GV, TAG_GA, TAG_GB, TAG_GS = range(20, 26)
+TAG_ACC = 30
 
 
 @dataclasses.dataclass
@@ -253,3 +254,27 @@ def gdn_inputs(config: int, *, B: int, N: int, H: int, Dk: int, Dv: int, tree: s
     st = lambda xs: torch.stack(xs).to(device)
     return GdnInputs(B=B, N=N, H=H, Dk=Dk, Dv=Dv, trees=trees, q=st(qs), k=st(ks), v=st(vs),
                      alpha=st(als), beta=st(bes), S0=st(ss))
+
+
+# ---------------------------------------------------------------- accepted paths
+
+def accepted_paths(config: int, parent: np.ndarray, *, tag: int = TAG_ACC, p_none: float = 0.15):
+    """A walk-shaped outcome per sequence: the root path of a random node (root
+    side first), or no accepted node with probability p_none.  Returns
+    accepted_nodes int32 [B, N] (-1 past the count) and num_accepted int32 [B]."""
+    B, N = parent.shape
+    acc = np.full((B, N), -1, dtype=np.int32)
+    na = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        r = T.rng_for(config, tag, b)
+        if r.random() < p_none:
+            continue
+        t = int(r.integers(0, N))
+        path = []
+        while t >= 0:
+            path.append(t)
+            t = int(parent[b, t])
+        path.reverse()
+        acc[b, :len(path)] = path
+        na[b] = len(path)
+    return acc, na

@@ -132,3 +132,40 @@ def test_walk_validation(lib):
     assert f(*bad) == tv.TV_ERR_WORKSPACE
     bad = list(base); bad[10] = None
     assert f(*bad) == tv.TV_ERR_WORKSPACE
+
+
+def test_gdn_commit_validation(lib):
+    f = lib.tree_gdn_commit
+    args = [FAKE] * 7 + [4, 32, 16, 128, 128, tv.TV_BF16, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == tv.TV_ERR_NULL
+    assert call(a6=None) == tv.TV_ERR_NULL          # num_accepted
+    assert call(a13=None) == tv.TV_ERR_NULL         # S_out
+    assert call(a7=0) == tv.TV_ERR_SHAPE
+    assert call(a8=65) == tv.TV_ERR_UNSUPPORTED
+    assert call(a10=64) == tv.TV_ERR_UNSUPPORTED     # Dk
+    assert call(a12=5) == tv.TV_ERR_UNSUPPORTED      # dtype
+
+
+def test_kv_commit_validation(lib):
+    f = lib.tree_kv_commit
+    args = [FAKE] * 6 + [64, 100, 4, 32, 8, 256, 16, tv.TV_BF16, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=None) == tv.TV_ERR_NULL
+    assert call(a15=None) == tv.TV_ERR_NULL         # v_cache
+    assert call(a8=0) == tv.TV_ERR_SHAPE
+    assert call(a7=0) == tv.TV_ERR_SHAPE            # empty pool
+    assert call(a11=96) == tv.TV_ERR_UNSUPPORTED     # D
+    assert call(a12=32) == tv.TV_ERR_UNSUPPORTED     # block size
+    assert call(a9=65) == tv.TV_ERR_UNSUPPORTED
+    assert call(a0=ctypes.c_void_p(0x1008)) == tv.TV_ERR_UNSUPPORTED   # not 16-byte aligned

@@ -27,7 +27,7 @@ BLOCK_SIZE = 16
 EXPORTS = (
     "tree_mask_build", "tree_verify_attn_workspace_size", "tree_verify_attn",
     "tree_gdn_verify", "tree_walk_accept_workspace_size", "tree_walk_accept",
-    "tv_status_string",
+    "tree_gdn_commit", "tree_kv_commit", "tv_status_string",
 )
 
 _lib = None
@@ -61,6 +61,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tree_walk_accept_workspace_size.restype = Z
     lib.tree_walk_accept.argtypes = [P, P, P, I, I, I, S, P, P, P, P, Z, P]
     lib.tree_walk_accept.restype = S
+    lib.tree_gdn_commit.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, S, P, P]
+    lib.tree_gdn_commit.restype = S
+    lib.tree_kv_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, S, P, P, P]
+    lib.tree_kv_commit.restype = S
     lib.tv_status_string.argtypes = [S]
     lib.tv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -235,3 +239,56 @@ def tree_walk_accept(tokens, parent, logits, out=None, workspace=None) -> dict:
                                 _stream(dev))
     _check("tree_walk_accept", code)
     return out
+
+
+# ---------------------------------------------------------------- commits
+
+def tree_gdn_commit(k, v, alpha, beta, S0, accepted_nodes, num_accepted, out=None) -> torch.Tensor:
+    """The committed GDN state [B, H, Dk, Dv] (float32) after the walk; out
+    may be S0 itself (in place)."""
+    lib = load()
+    dev = k.device
+    B, N, H, Dk = k.shape
+    Dv = v.shape[-1]
+    dt = k.dtype
+    _need(k, "k", dt, dev)
+    _need(v, "v", dt, dev, (B, N, H, Dv))
+    _need(alpha, "alpha", torch.float32, dev, (B, N, H))
+    _need(beta, "beta", torch.float32, dev, (B, N, H))
+    _need(S0, "S0", torch.float32, dev, (B, H, Dk, Dv))
+    _need(accepted_nodes, "accepted_nodes", torch.int32, dev, (B, N))
+    _need(num_accepted, "num_accepted", torch.int32, dev, (B,))
+    if out is None:
+        out = torch.empty(B, H, Dk, Dv, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev, (B, H, Dk, Dv))
+    code = lib.tree_gdn_commit(_ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                               _ptr(accepted_nodes), _ptr(num_accepted), B, N, H, Dk, Dv,
+                               _dtype_code(dt), _ptr(out), _stream(dev))
+    _check("tree_gdn_commit", code)
+    return out
+
+
+def tree_kv_commit(k_node, v_node, accepted_nodes, num_accepted, ctx_len, block_table, k_cache,
+                   v_cache) -> None:
+    """Copy the accepted nodes' key/value rows into positions ctx_len + s of
+    the paged caches (in place)."""
+    lib = load()
+    dev = k_node.device
+    B, N, Hkv, D = k_node.shape
+    dt = k_node.dtype
+    _need(k_node, "k_node", dt, dev)
+    _need(v_node, "v_node", dt, dev, (B, N, Hkv, D))
+    _need(accepted_nodes, "accepted_nodes", torch.int32, dev, (B, N))
+    _need(num_accepted, "num_accepted", torch.int32, dev, (B,))
+    _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
+    _need(block_table, "block_table", torch.int32, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    nb = k_cache.shape[0]
+    _need(k_cache, "k_cache", dt, dev, (nb, Hkv, BLOCK_SIZE, D))
+    _need(v_cache, "v_cache", dt, dev, (nb, Hkv, BLOCK_SIZE, D))
+    code = lib.tree_kv_commit(_ptr(k_node), _ptr(v_node), _ptr(accepted_nodes), _ptr(num_accepted),
+                              _ptr(ctx_len), _ptr(block_table), block_table.shape[1], nb, B, N, Hkv,
+                              D, BLOCK_SIZE, _dtype_code(dt), _ptr(k_cache), _ptr(v_cache),
+                              _stream(dev))
+    _check("tree_kv_commit", code)

@@ -93,6 +93,41 @@ tv_status tree_gdn_verify(const void* q, const void* k, const void* v, const flo
                                  out_dtype, out, as_stream(stream)));
 }
 
+tv_status tree_gdn_commit(const void* k, const void* v, const float* alpha, const float* beta,
+                          const float* S0, const int32_t* accepted_nodes,
+                          const int32_t* num_accepted, int32_t B, int32_t N, int32_t H, int32_t Dk,
+                          int32_t Dv, tv_dtype dtype, float* S_out, tv_stream stream) {
+  if (!k || !v || !alpha || !beta || !S0 || !accepted_nodes || !num_accepted || !S_out)
+    return TV_ERR_NULL;
+  if (B < 1 || N < 1 || H < 1 || Dk < 1 || Dv < 1) return TV_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return TV_ERR_UNSUPPORTED;
+  if (N > TV_MAX_NODES || Dk != 128 || Dv != 128) return TV_ERR_UNSUPPORTED;
+  return launched(tv::launch_gdn_commit(k, v, alpha, beta, S0, accepted_nodes, num_accepted, B, N,
+                                        H, dtype, S_out, as_stream(stream)));
+}
+
+tv_status tree_kv_commit(const void* k_node, const void* v_node, const int32_t* accepted_nodes,
+                         const int32_t* num_accepted, const int32_t* ctx_len,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         int32_t num_blocks, int32_t B, int32_t N, int32_t Hkv, int32_t D,
+                         int32_t block_size, tv_dtype dtype, void* k_cache, void* v_cache,
+                         tv_stream stream) {
+  if (!k_node || !v_node || !accepted_nodes || !num_accepted || !ctx_len || !block_table ||
+      !k_cache || !v_cache)
+    return TV_ERR_NULL;
+  if (B < 1 || N < 1 || Hkv < 1 || D < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return TV_ERR_SHAPE;
+  if (!dtype_ok(dtype) || block_size != TV_BLOCK_SIZE) return TV_ERR_UNSUPPORTED;
+  if (N > TV_MAX_NODES || (D != 64 && D != 128 && D != 256)) return TV_ERR_UNSUPPORTED;
+  // rows are copied in 16-byte pieces
+  const uintptr_t align = reinterpret_cast<uintptr_t>(k_node) | reinterpret_cast<uintptr_t>(v_node) |
+                          reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache);
+  if (align & 15u) return TV_ERR_UNSUPPORTED;
+  return launched(tv::launch_kv_commit(k_node, v_node, accepted_nodes, num_accepted, ctx_len,
+                                       block_table, max_blocks_per_seq, num_blocks, B, N, Hkv, D,
+                                       dtype, k_cache, v_cache, as_stream(stream)));
+}
+
 size_t tree_walk_accept_workspace_size(int32_t B, int32_t N) {
   if (B < 1 || N < 1) return 0;
   return static_cast<size_t>(B) * (N + 1) * sizeof(int32_t);

@@ -839,7 +839,6 @@ __global__ __launch_bounds__(kThreads, (stream_min_wg<T, D>())) void attn_stream
   __shared__ int s_pref[kMaxSeqs + 1];
   __shared__ int s_ctx[kMaxSeqs + 1];
 
-  const int tid = threadIdx.x;
   const int ntn = (N + kTile - 1) / kTile;
   stream_prefix(ctx_len, max_ctx, B, N, s_pref, s_ctx);
   const int tb_all = s_pref[B];  // tiles of one kv head over all sequences

@@ -33,6 +33,16 @@ hipError_t launch_mask(const int32_t* parent, const int32_t* depth_in, const int
                        int B, int N, uint64_t* anc, int32_t* depth_out, int32_t* pos,
                        float* dense_bias, int32_t* status, hipStream_t stream);
 
+hipError_t launch_gdn_commit(const void* k, const void* v, const float* alpha, const float* beta,
+                             const float* S0, const int32_t* acc_nodes, const int32_t* num_acc,
+                             int B, int N, int H, tv_dtype dtype, float* S_out,
+                             hipStream_t stream);
+
+hipError_t launch_kv_commit(const void* k_node, const void* v_node, const int32_t* acc_nodes,
+                            const int32_t* num_acc, const int32_t* ctx_len, const int32_t* bt,
+                            int max_blocks, int num_blocks, int B, int N, int Hkv, int D,
+                            tv_dtype dtype, void* k_cache, void* v_cache, hipStream_t stream);
+
 hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void* logits, int B,
                        int N, int V, tv_dtype dtype, int32_t* acc_tok, int32_t* acc_node,
                        int32_t* num_acc, int32_t* argmax_ws, hipStream_t stream);
