@@ -216,6 +216,7 @@ tv_status tree_walk_accept(const int32_t* tokens, const int32_t* parent,
  *   num_accepted   int32 [B]     from tree_walk_accept (clamped into [0, N])
  *   S_out      float [B, H, Dk, Dv] out: the new committed state; may be S0
  *              itself (each (sequence, head) block is read before it is written)
+ * k, v, S0 and S_out must be 16-byte aligned.
  * Supported: 1 <= N <= TV_MAX_NODES, Dk == Dv == 128, dtype TV_F32 or TV_BF16.
  * ------------------------------------------------------------------------ */
 tv_status tree_gdn_commit(const void* k, const void* v, const float* alpha,

@@ -150,6 +150,7 @@ def test_gdn_commit_validation(lib):
     assert call(a8=65) == tv.TV_ERR_UNSUPPORTED
     assert call(a10=64) == tv.TV_ERR_UNSUPPORTED     # Dk
     assert call(a12=5) == tv.TV_ERR_UNSUPPORTED      # dtype
+    assert call(a4=ctypes.c_void_p(0x1004)) == tv.TV_ERR_UNSUPPORTED   # S0 not 16-byte aligned
 
 
 def test_kv_commit_validation(lib):

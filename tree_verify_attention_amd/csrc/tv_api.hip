@@ -102,6 +102,10 @@ tv_status tree_gdn_commit(const void* k, const void* v, const float* alpha, cons
   if (B < 1 || N < 1 || H < 1 || Dk < 1 || Dv < 1) return TV_ERR_SHAPE;
   if (!dtype_ok(dtype)) return TV_ERR_UNSUPPORTED;
   if (N > TV_MAX_NODES || Dk != 128 || Dv != 128) return TV_ERR_UNSUPPORTED;
+  // the state and the key/value rows move in 16-byte pieces
+  const uintptr_t align = reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+                          reinterpret_cast<uintptr_t>(S0) | reinterpret_cast<uintptr_t>(S_out);
+  if (align & 15u) return TV_ERR_UNSUPPORTED;
   return launched(tv::launch_gdn_commit(k, v, alpha, beta, S0, accepted_nodes, num_accepted, B, N,
                                         H, dtype, S_out, as_stream(stream)));
 }
