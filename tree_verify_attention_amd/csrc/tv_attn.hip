@@ -42,7 +42,8 @@ constexpr int kWaves = 4;
 constexpr int kRows = kWaves * 16;  // query rows per workgroup
 constexpr int kTile = 32;           // keys per LDS stage
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxPages = 1024;     // page indices of one split cached in LDS
+constexpr int kMaxPages = 1024;     // page indices of one stream segment cached in LDS
+constexpr int kSplitPages = 4096;   // of one split (splits are capped to fit)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -266,12 +267,12 @@ __device__ __forceinline__ RowIn<T, D> row_in(const T* __restrict__ q,
 
 // page indices [p0, p0 + npages) of one sequence into s_pages (as far as it
 // reaches), clamped into the pool; all loads go out before the first store
-template <int NT>
+template <int NT, int kPages>
 __device__ __forceinline__ void fill_pages(int* s_pages, const int32_t* __restrict__ bt_b, int p0,
                                            int npages, int num_blocks) {
-  constexpr int kPer = kMaxPages / NT;
-  static_assert(kPer * NT == kMaxPages, "page cache layout");
-  const int n = min(npages, kMaxPages);
+  constexpr int kPer = kPages / NT;
+  static_assert(kPer * NT == kPages, "page cache layout");
+  const int n = min(npages, kPages);
   int v[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
@@ -292,7 +293,7 @@ __device__ __forceinline__ void fill_pages(int* s_pages, const int32_t* __restri
 // slot `pslot`.  s_pos holds the tree's position ids and s_pages the page
 // indices of pages k0 / 16 onwards, both filled by the caller before a
 // barrier that this routine also relies on for its own LDS.
-template <typename T, typename TO, int D, int kTeams>
+template <typename T, typename TO, int D, int kTeams, int kPages>
 __device__ __forceinline__ void attn_segment(
     const RowIn<T, D>& ri, const T* __restrict__ kn, const T* __restrict__ vn,
     const T* __restrict__ kc, const T* __restrict__ vc, const int32_t* __restrict__ bt_b,
@@ -376,7 +377,7 @@ __device__ __forceinline__ void attn_segment(
         off = ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes;
       } else {
         const int pi = (key >> 4) - p0;
-        const int page = pi < kMaxPages ? s_pages[pi] : min(max(bt_b[key >> 4], 0), num_blocks - 1);
+        const int page = pi < kPages ? s_pages[pi] : min(max(bt_b[key >> 4], 0), num_blocks - 1);
         off = ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes;
       }
       lds_dma16(src + off + part * 16, dst + blk * 1024);
@@ -650,7 +651,7 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
   using C = Cfg<T, D, kSplitTeams>;
   __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kStageBytes];
   __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kStageBytes];
-  __shared__ int s_pages[kMaxPages];
+  __shared__ int s_pages[kSplitPages];
   __shared__ int s_pos[64];
   __shared__ int2 s_rng;
 
@@ -686,14 +687,362 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
   const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
   const int p0 = k0 >> 4;
   const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-  fill_pages<kThreads * kSplitTeams>(s_pages, bt_b, p0, npages, num_blocks);
+  fill_pages<kThreads * kSplitTeams, kSplitPages>(s_pages, bt_b, p0, npages, num_blocks);
 
-  attn_segment<T, TO, D, kSplitTeams>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G,
+  attn_segment<T, TO, D, kSplitTeams, kSplitPages>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G,
                          rows, window, scale_log2, b, g, rg, k0, k1, 0,
                          last ? (N + C::kStageKeys - 1) / C::kStageKeys : 0,
                          prng, sp.nsplit == 1,
                          (static_cast<size_t>(b) * Hkv + g) * nsplit_max + s, out, ws_acc, ws_ml,
                          kring, vring, s_pages, s_pos);
+}
+
+// Online softmax of one row tile over a tile's masked, log2-scaled scores x
+// (as in attn_segment): running max and sum, rescaling the accumulator when
+// some row's max moved; p receives the tile's weights.
+template <int kDT>
+__device__ __forceinline__ void tile_softmax_w(const float x[2][4], float& m_run, float& l_run,
+                                               f32x4_t* acc, float p[2][4]) {
+  float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                   fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+  mt = pair_max<32>(pair_max<16>(mt));
+  const float m_new = fmaxf(m_run, mt);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  float ps = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[j][i] = fast_exp2(x[j][i] - m_use);
+      ps += p[j][i];
+    }
+  if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0ull) {
+    const float alpha = fast_exp2(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) acc[dt] *= alpha;
+  }
+  l_run += ps;
+  m_run = m_new;
+}
+
+// a finished row: the normalised output, or the partial (acc, m, l) in row ub
+template <typename TO, int D>
+__device__ __forceinline__ void wide_row_store(bool final_out, const f32x4_t* acc, float m_run,
+                                               float l_tot, int lg, TO* __restrict__ o,
+                                               float* __restrict__ ws_acc,
+                                               float2* __restrict__ ws_ml, size_t ub) {
+  constexpr int kDT = D / 16;
+  if (final_out) {
+    const float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+      const int d0 = dt * 16 + 4 * lg;
+      if constexpr (sizeof(TO) == 2) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f32_to_bf16(acc[dt][0] * inv)) |
+              (static_cast<uint32_t>(f32_to_bf16(acc[dt][1] * inv)) << 16);
+        w.y = static_cast<uint32_t>(f32_to_bf16(acc[dt][2] * inv)) |
+              (static_cast<uint32_t>(f32_to_bf16(acc[dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(o + d0) = w;
+      } else {
+        *reinterpret_cast<float4*>(o + d0) =
+            make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+      }
+    }
+  } else {
+    float* pa = ws_acc + ub * D;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+      *reinterpret_cast<float4*>(pa + dt * 16 + 4 * lg) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (lg == 0) ws_ml[ub] = make_float2(m_run, l_tot);
+  }
+}
+
+// Query tiles wider than one workgroup of 64 rows (G * N > 64, for instance
+// 8 query heads per kv head times 64 nodes = 512 rows).  Each wave carries
+// kRT tiles of 16 rows, so a workgroup covers 64 kRT rows of a unit and each
+// key or value fragment read from LDS feeds kRT products; the row groups of
+// a unit no longer stream the same keys once per 64 rows.  Same work units
+// (unit, row group, split), ring, masking and partials as the per-unit
+// layout, bf16 inputs only.
+// Waves per workgroup and 16-row tiles per wave of the wide layout: 8 waves
+// (two per SIMD, so that one wave's softmax runs under the other's matrix
+// products) of 2 row tiles, or 1 at D = 256 (registers); at D = 64 a tile of
+// keys is too small to give 8 waves a 1 KB load each, so 4 waves of 4.
+template <int D>
+constexpr int wide_waves() {
+  return D == 64 ? 4 : 8;
+}
+template <int D>
+constexpr int wide_tiles() {
+  return D == 64 ? 4 : (D == 256 ? 1 : 2);
+}
+
+template <typename TO, int D>
+__global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, int max_blocks,
+    int num_blocks, const int32_t* __restrict__ ctx_len, int max_ctx,
+    const uint64_t* __restrict__ anc, const int32_t* __restrict__ pos, int N, int Hq, int Hkv,
+    int G, int rows, int row_groups, int nsplit_max, int split_tokens, int window,
+    float scale_log2, int units, TO* __restrict__ out, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
+  using T = uint16_t;
+  using C = Cfg<T, D>;
+  constexpr int kRT = wide_tiles<D>();
+  constexpr int kW = wide_waves<D>();
+  constexpr int kNT = 64 * kW;
+  constexpr int kIPW = C::kTileBytes / 1024 / kW;  // 1 KB loads per wave per tile
+  static_assert(kIPW >= 1 && kIPW * 1024 * kW == C::kTileBytes, "tile must split over the waves");
+  constexpr int kQ = D / 32;  // k steps of the score products
+  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
+  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
+  __shared__ int s_pages[kSplitPages];
+  __shared__ int s_pos[64];
+  __shared__ int2 s_rng;
+
+  // work units as in the per-unit layout: split-major, XCD-interleaved, the
+  // row groups of one unit on one XCD
+  const int xcd = blockIdx.x % 8;
+  const int slot = blockIdx.x / 8;
+  const int u = (slot / row_groups) * 8 + xcd;
+  if (u >= units) return;
+  const int rg = slot % row_groups;
+  const int n_bg = units / nsplit_max;  // B * Hkv
+  const int s = u / n_bg;
+  const int g = (u % n_bg) % Hkv;
+  const int b = (u % n_bg) / Hkv;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
+
+  // rows R = rg * 64 kRT + wave * 16 kRT + 16 rt + lr; their queries,
+  // positions and ancestor words go out with the context length
+  const int ctx_raw = ctx_len[b];
+  int Rr[kRT];
+  bool ok[kRT];
+  bf16x8_t qf[kRT][kQ];
+  int rpos[kRT];
+  uint64_t ranc[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    Rr[rt] = (rg * kW + wave) * 16 * kRT + 16 * rt + lr;
+    ok[rt] = Rr[rt] < rows;
+    const int t = ok[rt] ? Rr[rt] / G : 0;
+    const int hl = ok[rt] ? Rr[rt] % G : 0;
+    const size_t qoff = ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D;
+#pragma unroll
+    for (int ks = 0; ks < kQ; ++ks) {
+      const uint4 v = ok[rt] ? *reinterpret_cast<const uint4*>(q + qoff + ks * 32 + lg * 8)
+                             : make_uint4(0, 0, 0, 0);
+      qf[rt][ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    rpos[rt] = pos_b[t];
+    ranc[rt] = anc[static_cast<size_t>(b) * N + t];
+  }
+  if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
+  const int2 prng = tree_pos_range(pos_b, N, &s_rng);
+  const SeqPlan sp = seq_plan(ctx_raw, max_ctx, window, prng.x, nsplit_max, split_tokens);
+  if (s >= sp.nsplit) return;  // uniform over the workgroup
+  const int k0 = sp.start + s * sp.split_len;
+  const int k1 = min(k0 + sp.split_len, sp.end);
+  const bool last = s == sp.nsplit - 1;
+  const bool final_out = sp.nsplit == 1;
+  const size_t pslot = (static_cast<size_t>(b) * Hkv + g) * nsplit_max + s;
+  const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
+  const int p0 = k0 >> 4;
+  const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
+  fill_pages<kNT, kSplitPages>(s_pages, bt_b, p0, npages, num_blocks);
+
+  // make the row loads complete here (see attn_segment)
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+    for (int ks = 0; ks < kQ; ++ks) asm volatile("" ::"v"(qf[rt][ks]));
+    asm volatile("" ::"v"(rpos[rt]), "v"(ranc[rt]));
+  }
+  f32x4_t acc[kRT][C::kDT];
+  float m_run[kRT], l_run[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.0f;
+  }
+  const int nctx_tiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
+  const int node_t1 = last ? (N + kTile - 1) / kTile : 0;
+  const int ntiles = nctx_tiles + node_t1;
+  const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
+  const unsigned char* kcb = reinterpret_cast<const unsigned char*>(kc);
+  const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc);
+  const unsigned char* knb = reinterpret_cast<const unsigned char*>(kn);
+  const unsigned char* vnb = reinterpret_cast<const unsigned char*>(vn);
+  wait_vmem<0>();
+  __syncthreads();  // page cache ready
+
+  // loads of one tile's keys (or values) into its slot, as in attn_segment
+  auto issue = [&](int it, bool values) {
+    unsigned char* dst = (values ? vring : kring) + (it % C::kSlots) * C::kTileBytes;
+    const bool is_node = it >= nctx_tiles;
+    const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
+    const int lim = is_node ? N : k1;
+    const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
+#pragma unroll
+    for (int j = 0; j < kIPW; ++j) {
+      const int blk = wave * kIPW + j;
+      const int gl = blk * 64 + lane;
+      const int row = gl / C::kGran;
+      const int part = (gl % C::kGran) ^ swz_key<T, D>(row);
+      const int key = min(base + row, lim - 1);
+      size_t off;
+      if (is_node) {
+        off = ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes;
+      } else {
+        const int pi = (key >> 4) - p0;
+        const int page = pi < kSplitPages ? s_pages[pi] : min(max(bt_b[key >> 4], 0), num_blocks - 1);
+        off = ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes;
+      }
+      lds_dma16(src + off + part * 16, dst + blk * 1024);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  if (ntiles > 0) {
+    for (int i = 0; i < C::kSlots && i < ntiles; ++i) {
+      issue(i, false);
+      issue(i, true);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      const int newest = min(it + C::kSlots - 1, ntiles - 1);
+      const int v_out = it == 0 ? newest : min(it + C::kSlots - 2, ntiles - 1);
+      wait_vm_upto(kIPW * ((v_out - it + 1) + (newest - it)));
+      lds_barrier();  // keys of tile `it` have landed; every wave is done with tile it - 1
+      if (it > 0 && it + C::kSlots - 1 < ntiles) issue(it + C::kSlots - 1, true);
+
+      const unsigned char* Kt = kring + (it % C::kSlots) * C::kTileBytes;
+      const unsigned char* Vt = vring + (it % C::kSlots) * C::kTileBytes;
+      const bool is_node = it >= nctx_tiles;
+      const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
+      const int lim = is_node ? N : k1;
+
+      // S^T of every row tile: the key fragments of a k step are read once
+      // (two k steps ahead) and feed all kRT row tiles
+      f32x4_t S[kRT][2];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) S[rt][0] = S[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      constexpr int kAh = kQ < 2 ? kQ : 2;
+      uint4 ka[kAh + 1][2];
+      auto kread = [&](int ks, int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
+      };
+#pragma unroll
+      for (int ks = 0; ks < kAh; ++ks) {
+        ka[ks][0] = kread(ks, 0);
+        ka[ks][1] = kread(ks, 1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kQ; ++ks) {
+        if (ks + kAh < kQ) {
+          ka[(ks + kAh) % (kAh + 1)][0] = kread(ks + kAh, 0);
+          ka[(ks + kAh) % (kAh + 1)][1] = kread(ks + kAh, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          S[rt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][0]), qf[rt][ks], S[rt][0], 0, 0, 0);
+          S[rt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][1]), qf[rt][ks], S[rt][1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // mask and online softmax per row tile; P split into bf16 high and low parts
+      const bool full = !is_node && base + kTile <= lim &&
+                        (window <= 0 || (base >= win_all && base + kTile - 1 <= prng.x));
+      bf16x8_t ph[kRT], pl[kRT];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        float x[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (full) {
+              x[j][i] = S[rt][j][i] * scale_log2;
+            } else {
+              const int key = base + 16 * j + 4 * lg + i;
+              const int kpos = is_node ? s_pos[key & 63] : key;
+              const int dpos = rpos[rt] - kpos;
+              bool vis = ok[rt] & (key < lim);
+              vis &= !is_node | (((ranc[rt] >> (key & 63)) & 1ull) != 0ull);
+              vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+              x[j][i] = vis ? S[rt][j][i] * scale_log2 : -INFINITY;
+            }
+          }
+        float p[2][4];
+        tile_softmax_w<C::kDT>(x, m_run[rt], l_run[rt], acc[rt], p);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const __bf16 h = static_cast<__bf16>(p[j][i]);
+            ph[rt][4 * j + i] = h;
+            pl[rt][4 * j + i] = static_cast<__bf16>(p[j][i] - static_cast<float>(h));
+          }
+      }
+
+      wait_vm_upto(kIPW * 2 * (newest - it));
+      lds_barrier();  // values of tile `it` have landed; every wave is done with its keys
+      if (it + C::kSlots < ntiles) issue(it + C::kSlots, false);
+
+      // O^T += V^T P^T: the value fragments of a column tile feed all row tiles
+      const int vrow = 4 * lg + (lr >> 2);
+      const int vcol = 8 * (lr & 3);
+      constexpr int kVA = C::kDT < 2 ? C::kDT : 2;
+      s16x4_t vlo[kVA + 1], vhi[kVA + 1];
+#pragma unroll
+      for (int dt = 0; dt < kVA; ++dt) {
+        vlo[dt] = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
+        vhi[dt] = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+      }
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) {
+        if (dt + kVA < C::kDT) {
+          vlo[(dt + kVA) % (kVA + 1)] = lds_read_tr16(Vt + swz<T, D>(vrow, (dt + kVA) * 32 + vcol));
+          vhi[(dt + kVA) % (kVA + 1)] =
+              lds_read_tr16(Vt + swz<T, D>(16 + vrow, (dt + kVA) * 32 + vcol));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const s16x4_t lo = vlo[dt % (kVA + 1)];
+        const s16x4_t hi = vhi[dt % (kVA + 1)];
+        const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], acc[rt][dt], 0, 0, 0);
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], acc[rt][dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const float l_tot = pair_sum<32>(pair_sum<16>(l_run[rt]));
+    if (!ok[rt]) continue;
+    const int t = Rr[rt] / G, hl = Rr[rt] % G;
+    const size_t qoff = ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D;
+    wide_row_store<TO, D>(final_out, acc[rt], m_run[rt], l_tot, lg, out + qoff, ws_acc, ws_ml,
+                          pslot * rows + Rr[rt]);
+  }
 }
 
 // Stream decomposition of a layer without a window.  The tiles of every
@@ -882,9 +1231,9 @@ __global__ __launch_bounds__(kThreads, (stream_min_wg<T, D>())) void attn_stream
     const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
     const int p0 = k0 >> 4;
     const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-    fill_pages<kThreads>(s_pages, bt_b, p0, npages, num_blocks);
+    fill_pages<kThreads, kMaxPages>(s_pages, bt_b, p0, npages, num_blocks);
 
-    attn_segment<T, TO, D, 1>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
+    attn_segment<T, TO, D, 1, kMaxPages>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
                            0, scale_log2, b, g, 0, k0, k1, n0, n1, prng,
                            t0 == 0 && t1 == tiles_b, static_cast<size_t>(w) + g * B + b, out,
                            ws_acc, ws_ml, kring, vring, s_pages, s_pos);
@@ -1061,6 +1410,27 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
                        pl.stream_xm, ws_acc, ws_ml, static_cast<TO*>(out));
     return hipGetLastError();
   }
+  if constexpr (sizeof(T) == 2) {
+    if (pl.rows > kRows) {
+      // wide query tiles: 16 kRT rows per wave
+      constexpr int kRowsW = 16 * wide_tiles<D>() * wide_waves<D>();
+      const int rgw = (pl.rows + kRowsW - 1) / kRowsW;
+      const long long gridw = (units + 7) / 8 * 8 * rgw;
+      hipLaunchKernelGGL((attn_wide_kernel<TO, D>), dim3(static_cast<unsigned>(gridw)),
+                         dim3(64 * wide_waves<D>()), 0, stream, static_cast<const T*>(q),
+                         static_cast<const T*>(k_node), static_cast<const T*>(v_node),
+                         static_cast<const T*>(k_cache), static_cast<const T*>(v_cache),
+                         block_table, max_blocks, num_blocks, ctx_len, max_ctx, anc, pos, N, Hq,
+                         Hkv, pl.G, pl.rows, rgw, pl.nsplit, pl.split_tokens, window, scale_log2,
+                         static_cast<int>(units), static_cast<TO*>(out), ws_acc, ws_ml);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || pl.nsplit == 1) return e;
+      hipLaunchKernelGGL((attn_merge_kernel<TO, D>), dim3(merge_grid), dim3(256), 0, stream, ctx_len,
+                         max_ctx, pos, N, Hq, Hkv, pl.G, pl.rows, pl.nsplit, pl.split_tokens, window,
+                         ws_acc, ws_ml, static_cast<TO*>(out));
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_split_kernel<T, TO, D>), dim3(static_cast<unsigned>(grid)),
                      dim3(kThreads * split_teams<T, D>()),
                      0, stream, static_cast<const T*>(q), static_cast<const T*>(k_node),
@@ -1158,6 +1528,11 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int wi
   int st = static_cast<int>((range + want - 1) / want);
   st = (st + kTile - 1) / kTile * kTile;
   if (st < kTile) st = kTile;
+  // a split's page indices must fit the page cache (a window start or split
+  // start inside a page adds one page): otherwise every load past the cache
+  // would wait for a block-table read
+  constexpr int kMaxSplit = (kSplitPages - 2) * 16 / kTile * kTile;
+  if (st > kMaxSplit) st = kMaxSplit;
   p.split_tokens = st;
   p.nsplit = range > 0 ? (range + st - 1) / st : 1;
   p.ws_bytes = p.nsplit > 1
