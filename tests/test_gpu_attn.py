@@ -183,3 +183,15 @@ def test_c4_full_size_sampled(lib):
     x, _ = make(4, kv_on_device=True)
     say("attn c4 full")
     _sampled_check(lib, x, 0, [(0, 0), (63, 7)], nodes=[0, 1, 30, 63])
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_wide_query_tiles(lib, D):
+    """More than 64 query rows per kv head (G * N = 160): the row tiles of a
+    workgroup end inside the tile; ragged contexts from empty to several
+    splits; no window, a window inside a stage and one past the context."""
+    trees = W.make_trees(51, "random_parent", 6, 40, 100)
+    x, _ = make(1, B=6, N=40, Hq=8, Hkv=2, D=D, trees=trees, dtype=torch.bfloat16,
+                ctx_len=np.array([0, 1, 17, 63, 700, 5000], dtype=np.int32))
+    for w in (0, 37, 6000):
+        check_full(lib, x, w, f"wide D={D}")

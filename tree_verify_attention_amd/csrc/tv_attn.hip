@@ -762,15 +762,18 @@ __device__ __forceinline__ void wide_row_store(bool final_out, const f32x4_t* ac
 
 // Query tiles wider than one workgroup of 64 rows (G * N > 64, for instance
 // 8 query heads per kv head times 64 nodes = 512 rows).  Each wave carries
-// kRT tiles of 16 rows, so a workgroup covers 64 kRT rows of a unit and each
-// key or value fragment read from LDS feeds kRT products; the row groups of
-// a unit no longer stream the same keys once per 64 rows.  Same work units
-// (unit, row group, split), ring, masking and partials as the per-unit
-// layout, bf16 inputs only.
-// Waves per workgroup and 16-row tiles per wave of the wide layout: 8 waves
-// (two per SIMD, so that one wave's softmax runs under the other's matrix
-// products) of 2 row tiles, or 1 at D = 256 (registers); at D = 64 a tile of
-// keys is too small to give 8 waves a 1 KB load each, so 4 waves of 4.
+// kRT tiles of 16 rows, so a workgroup covers 16 kRT kW rows of a unit and
+// each key or value fragment read from LDS feeds kRT products; the row
+// groups of a unit no longer stream the same keys once per 64 rows.  Keys
+// go through the ring in stages of two 32-key tiles, and the softmax runs
+// once per stage, so the per-iteration work (waits, barriers, issue,
+// cross-lane reductions) is spread over 64 keys.  Same work units (unit, row
+// group, split), masking and partials as the per-unit layout; bf16 inputs.
+//
+// Waves per workgroup and row tiles per wave: 8 waves (two per SIMD, so that
+// one wave's softmax runs under the other's matrix products) of 2 row tiles,
+// or 1 at D = 256 (registers); at D = 64 a stage is too small to give 8 waves
+// a 1 KB load each, so 4 waves of 4.
 template <int D>
 constexpr int wide_waves() {
   return D == 64 ? 4 : 8;
@@ -795,11 +798,16 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   constexpr int kRT = wide_tiles<D>();
   constexpr int kW = wide_waves<D>();
   constexpr int kNT = 64 * kW;
-  constexpr int kIPW = C::kTileBytes / 1024 / kW;  // 1 KB loads per wave per tile
-  static_assert(kIPW >= 1 && kIPW * 1024 * kW == C::kTileBytes, "tile must split over the waves");
+  constexpr int kKT = 2;                                 // 32-key tiles per stage
+  constexpr int kSK = kKT * kTile;                       // keys per stage
+  constexpr int kSB = kKT * C::kTileBytes;               // bytes of a stage (keys or values)
+  constexpr int kSlots = (98304 / (2 * kSB)) < 2 ? 2 : ((98304 / (2 * kSB)) > 4 ? 4 : 98304 / (2 * kSB));
+  constexpr int kIPW = kSB / 1024 / kW;                  // 1 KB loads per wave per stage
+  static_assert(kIPW >= 1 && kIPW * 1024 * kW == kSB, "stage must split over the waves");
+  static_assert(kIPW * (2 * kSlots - 1) <= 63, "vmcnt range");
   constexpr int kQ = D / 32;  // k steps of the score products
-  __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
-  __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
+  __shared__ __align__(1024) unsigned char kring[kSlots * kSB];
+  __shared__ __align__(1024) unsigned char vring[kSlots * kSB];
   __shared__ int s_pages[kSplitPages];
   __shared__ int s_pos[64];
   __shared__ int2 s_rng;
@@ -821,8 +829,8 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
 
-  // rows R = rg * 64 kRT + wave * 16 kRT + 16 rt + lr; their queries,
-  // positions and ancestor words go out with the context length
+  // rows R = (rg kW + wave) 16 kRT + 16 rt + lr; their queries, positions and
+  // ancestor words go out with the context length
   const int ctx_raw = ctx_len[b];
   int Rr[kRT];
   bool ok[kRT];
@@ -875,9 +883,9 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
     m_run[rt] = -INFINITY;
     l_run[rt] = 0.0f;
   }
-  const int nctx_tiles = k1 > k0 ? (k1 - k0 + kTile - 1) / kTile : 0;
-  const int node_t1 = last ? (N + kTile - 1) / kTile : 0;
-  const int ntiles = nctx_tiles + node_t1;
+  // stages: context keys [k0, k1) in stages of 64, then the node keys (N <= 64)
+  const int nctx = k1 > k0 ? (k1 - k0 + kSK - 1) / kSK : 0;
+  const int ntiles = nctx + (last ? 1 : 0);
   const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
   const unsigned char* kcb = reinterpret_cast<const unsigned char*>(kc);
   const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc);
@@ -886,11 +894,12 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   wait_vmem<0>();
   __syncthreads();  // page cache ready
 
-  // loads of one tile's keys (or values) into its slot, as in attn_segment
+  // loads of one stage's keys (or values) into its slot: stage row r (0..63)
+  // is row r % 32 of tile r / 32, swizzled as in the per-unit layout
   auto issue = [&](int it, bool values) {
-    unsigned char* dst = (values ? vring : kring) + (it % C::kSlots) * C::kTileBytes;
-    const bool is_node = it >= nctx_tiles;
-    const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
+    unsigned char* dst = (values ? vring : kring) + (it % kSlots) * kSB;
+    const bool is_node = it >= nctx;
+    const int base = is_node ? 0 : k0 + it * kSK;
     const int lim = is_node ? N : k1;
     const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
 #pragma unroll
@@ -914,120 +923,158 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   };
 
   if (ntiles > 0) {
-    for (int i = 0; i < C::kSlots && i < ntiles; ++i) {
+    for (int i = 0; i < kSlots && i < ntiles; ++i) {
       issue(i, false);
       issue(i, true);
     }
     for (int it = 0; it < ntiles; ++it) {
-      const int newest = min(it + C::kSlots - 1, ntiles - 1);
-      const int v_out = it == 0 ? newest : min(it + C::kSlots - 2, ntiles - 1);
-      wait_vm_upto(kIPW * ((v_out - it + 1) + (newest - it)));
-      lds_barrier();  // keys of tile `it` have landed; every wave is done with tile it - 1
-      if (it > 0 && it + C::kSlots - 1 < ntiles) issue(it + C::kSlots - 1, true);
+      const int newest = min(it + kSlots - 1, ntiles - 1);
+      const int v_out = it == 0 ? newest : min(it + kSlots - 2, ntiles - 1);
+      // the full ring in flight: the count is a constant
+      const bool steady = it > 0 && it + kSlots - 1 < ntiles;
+      if (steady) wait_vmem<kIPW * 2 * (kSlots - 1)>();
+      else wait_vm_upto(kIPW * ((v_out - it + 1) + (newest - it)));
+      lds_barrier();  // keys of stage `it` have landed; every wave is done with stage it - 1
+      if (it > 0 && it + kSlots - 1 < ntiles) issue(it + kSlots - 1, true);
 
-      const unsigned char* Kt = kring + (it % C::kSlots) * C::kTileBytes;
-      const unsigned char* Vt = vring + (it % C::kSlots) * C::kTileBytes;
-      const bool is_node = it >= nctx_tiles;
-      const int base = is_node ? (it - nctx_tiles) * kTile : k0 + it * kTile;
+      const unsigned char* Ks = kring + (it % kSlots) * kSB;
+      const unsigned char* Vs = vring + (it % kSlots) * kSB;
+      const bool is_node = it >= nctx;
+      const int base = is_node ? 0 : k0 + it * kSK;
       const int lim = is_node ? N : k1;
 
-      // S^T of every row tile: the key fragments of a k step are read once
-      // (two k steps ahead) and feed all kRT row tiles
-      f32x4_t S[kRT][2];
+      // S^T of every row tile for the four 16-key quarters of the stage: the
+      // key fragments of a k step are read once (two k steps ahead) and feed
+      // all kRT row tiles
+      f32x4_t S[kRT][2 * kKT];
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) S[rt][0] = S[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      constexpr int kAh = kQ < 2 ? kQ : 2;
-      uint4 ka[kAh + 1][2];
-      auto kread = [&](int ks, int j) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
-      };
+      for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-      for (int ks = 0; ks < kAh; ++ks) {
-        ka[ks][0] = kread(ks, 0);
-        ka[ks][1] = kread(ks, 1);
-      }
+        for (int h = 0; h < 2 * kKT; ++h) S[rt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kQ; ++ks) {
-        if (ks + kAh < kQ) {
-          ka[(ks + kAh) % (kAh + 1)][0] = kread(ks + kAh, 0);
-          ka[(ks + kAh) % (kAh + 1)][1] = kread(ks + kAh, 1);
+      for (int kt = 0; kt < kKT; ++kt) {
+        const unsigned char* Kt = Ks + kt * C::kTileBytes;
+        constexpr int kAh = kQ < 2 ? kQ : 2;
+        uint4 ka[kAh + 1][2];
+        auto kread = [&](int ks, int j) __attribute__((always_inline)) {
+          return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
+        };
+#pragma unroll
+        for (int ks = 0; ks < kAh; ++ks) {
+          ka[ks][0] = kread(ks, 0);
+          ka[ks][1] = kread(ks, 1);
         }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          S[rt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][0]), qf[rt][ks], S[rt][0], 0, 0, 0);
-          S[rt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][1]), qf[rt][ks], S[rt][1], 0, 0, 0);
+        for (int ks = 0; ks < kQ; ++ks) {
+          if (ks + kAh < kQ) {
+            ka[(ks + kAh) % (kAh + 1)][0] = kread(ks + kAh, 0);
+            ka[(ks + kAh) % (kAh + 1)][1] = kread(ks + kAh, 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) {
+            S[rt][2 * kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][0]), qf[rt][ks], S[rt][2 * kt], 0, 0, 0);
+            S[rt][2 * kt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][1]), qf[rt][ks], S[rt][2 * kt + 1], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
 
-      // mask and online softmax per row tile; P split into bf16 high and low parts
-      const bool full = !is_node && base + kTile <= lim &&
-                        (window <= 0 || (base >= win_all && base + kTile - 1 <= prng.x));
-      bf16x8_t ph[kRT], pl[kRT];
+      // mask and online softmax per row tile over the 64 keys; P split into
+      // bf16 high and low parts (keys 16 h + 4 lg + i of quarter h)
+      const bool full = !is_node && base + kSK <= lim &&
+                        (window <= 0 || (base >= win_all && base + kSK - 1 <= prng.x));
+      bf16x8_t ph[kRT][kKT], pl[kRT][kKT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        float x[2][4];
+        float x[2 * kKT][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (full) {
-              x[j][i] = S[rt][j][i] * scale_log2;
+              x[h][i] = S[rt][h][i] * scale_log2;
             } else {
-              const int key = base + 16 * j + 4 * lg + i;
+              const int key = base + 16 * h + 4 * lg + i;
               const int kpos = is_node ? s_pos[key & 63] : key;
               const int dpos = rpos[rt] - kpos;
               bool vis = ok[rt] & (key < lim);
               vis &= !is_node | (((ranc[rt] >> (key & 63)) & 1ull) != 0ull);
               vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-              x[j][i] = vis ? S[rt][j][i] * scale_log2 : -INFINITY;
+              x[h][i] = vis ? S[rt][h][i] * scale_log2 : -INFINITY;
             }
           }
-        float p[2][4];
-        tile_softmax_w<C::kDT>(x, m_run[rt], l_run[rt], acc[rt], p);
+        float mt = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int h = 0; h < 2 * kKT; ++h)
+          mt = fmaxf(mt, fmaxf(fmaxf(x[h][0], x[h][1]), fmaxf(x[h][2], x[h][3])));
+        mt = pair_max<32>(pair_max<16>(mt));
+        const float m_new = fmaxf(m_run[rt], mt);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        float ps = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const __bf16 h = static_cast<__bf16>(p[j][i]);
-            ph[rt][4 * j + i] = h;
-            pl[rt][4 * j + i] = static_cast<__bf16>(p[j][i] - static_cast<float>(h));
+            x[h][i] = fast_exp2(x[h][i] - m_use);
+            ps += x[h][i];
           }
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run[rt]) != 0ull) {
+          const float alpha = fast_exp2(m_run[rt] - m_use);
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha;
+        }
+        l_run[rt] += ps;
+        m_run[rt] = m_new;
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pv = x[2 * kt + j][i];
+              const __bf16 hb = static_cast<__bf16>(pv);
+              ph[rt][kt][4 * j + i] = hb;
+              pl[rt][kt][4 * j + i] = static_cast<__bf16>(pv - static_cast<float>(hb));
+            }
       }
 
-      wait_vm_upto(kIPW * 2 * (newest - it));
-      lds_barrier();  // values of tile `it` have landed; every wave is done with its keys
-      if (it + C::kSlots < ntiles) issue(it + C::kSlots, false);
+      if (steady) wait_vmem<kIPW * 2 * (kSlots - 1)>();
+      else wait_vm_upto(kIPW * 2 * (newest - it));
+      lds_barrier();  // values of stage `it` have landed; every wave is done with its keys
+      if (it + kSlots < ntiles) issue(it + kSlots, false);
 
-      // O^T += V^T P^T: the value fragments of a column tile feed all row tiles
+      // O^T += V^T P^T, one 32-key tile at a time: the value fragments of a
+      // column tile feed all row tiles; reads run two steps ahead
       const int vrow = 4 * lg + (lr >> 2);
       const int vcol = 8 * (lr & 3);
-      constexpr int kVA = C::kDT < 2 ? C::kDT : 2;
+      constexpr int kSteps = C::kDT * kKT;  // (column tile, key tile) pairs
+      constexpr int kVA = 2;
       s16x4_t vlo[kVA + 1], vhi[kVA + 1];
+      auto vread = [&](int st, s16x4_t& lo, s16x4_t& hi) __attribute__((always_inline)) {
+        const int dt = st / kKT, kt = st % kKT;
+        const unsigned char* Vt = Vs + kt * C::kTileBytes;
+        lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
+        hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+      };
 #pragma unroll
-      for (int dt = 0; dt < kVA; ++dt) {
-        vlo[dt] = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
-        vhi[dt] = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
-      }
+      for (int st = 0; st < kVA; ++st) vread(st, vlo[st], vhi[st]);
 #pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) {
-        if (dt + kVA < C::kDT) {
-          vlo[(dt + kVA) % (kVA + 1)] = lds_read_tr16(Vt + swz<T, D>(vrow, (dt + kVA) * 32 + vcol));
-          vhi[(dt + kVA) % (kVA + 1)] =
-              lds_read_tr16(Vt + swz<T, D>(16 + vrow, (dt + kVA) * 32 + vcol));
-        }
+      for (int st = 0; st < kSteps; ++st) {
+        if (st + kVA < kSteps) vread(st + kVA, vlo[(st + kVA) % (kVA + 1)], vhi[(st + kVA) % (kVA + 1)]);
         __builtin_amdgcn_sched_barrier(0);
-        const s16x4_t lo = vlo[dt % (kVA + 1)];
-        const s16x4_t hi = vhi[dt % (kVA + 1)];
+        const int dt = st / kKT, kt = st % kKT;
+        const s16x4_t lo = vlo[st % (kVA + 1)];
+        const s16x4_t hi = vhi[st % (kVA + 1)];
         const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], acc[rt][dt], 0, 0, 0);
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], acc[rt][dt], 0, 0, 0);
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt][kt], acc[rt][dt], 0, 0, 0);
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt][kt], acc[rt][dt], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
