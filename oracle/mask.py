@@ -8,6 +8,12 @@ ctx_len - 1 + depth.  Section "Layout contract": parent[i] is a node index,
 flattened by depth.  The DDTree validation post ("The Successful Test") prints
 depth 1 for every node whose parent is -1, which fixes the depth origin.
 
+Trees of up to 128 nodes are covered: the ancestor set of a node is packed
+into ceil(N / 64) 64-bit words, word w holding nodes 64 w .. 64 w + 63 (bit
+j % 64 of word j // 64 stands for node j).  The pages' trees stop near 32
+nodes; 128 is the tree size the DFlash-TfM summary measures its fused GDN
+verify at.
+
 Status codes per sequence (the same numbering as the library):
   0 ok, 1 a parent index outside [-1, i), 2 a given depth that differs from
   the derived one, 3 ctx_len < 1.  Checks apply in that order; the first that
@@ -32,10 +38,23 @@ def path_to_root(parent, t):
     return seen
 
 
+def anc_words(nodes, n):
+    """Pack a set of node indices into ceil(n / 64) uint64 words."""
+    w = np.zeros((n + 63) // 64, dtype=np.uint64)
+    for j in nodes:
+        w[j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return w
+
+
+def anc_value(words):
+    """The packed words of one node as one Python integer (bit j = node j)."""
+    return sum(int(x) << (64 * i) for i, x in enumerate(np.asarray(words, dtype=np.uint64)))
+
+
 def tree_mask(parent, ctx_len, depth_in=None):
     """Returns dict with
        vis    bool   [B, N, N]  vis[b, t, j] = (j is t or an ancestor of t)
-       anc    uint64 [B, N]     sum of 2**j over visible j
+       anc    uint64 [B, N, W]  visible j packed into W = ceil(N / 64) words
        depth  int32  [B, N]     |P(t)|
        pos    int64  [B, N]     ctx_len[b] - 1 + depth
        status int32  [B]
@@ -44,7 +63,7 @@ def tree_mask(parent, ctx_len, depth_in=None):
     ctx_len = np.asarray(ctx_len, dtype=np.int64)
     B, N = parent.shape
     vis = np.zeros((B, N, N), dtype=bool)
-    anc = np.zeros((B, N), dtype=np.uint64)
+    anc = np.zeros((B, N, (N + 63) // 64), dtype=np.uint64)
     depth = np.zeros((B, N), dtype=np.int32)
     pos = np.zeros((B, N), dtype=np.int64)
     status = np.zeros(B, dtype=np.int32)
@@ -55,7 +74,7 @@ def tree_mask(parent, ctx_len, depth_in=None):
             status[b] = TREE_BAD_PARENT
             for t in range(N):
                 vis[b, t, t] = True
-                anc[b, t] = np.uint64(1) << np.uint64(t)
+                anc[b, t] = anc_words([t], N)
                 depth[b, t] = 1
                 pos[b, t] = ctx_len[b]
             continue
@@ -63,7 +82,7 @@ def tree_mask(parent, ctx_len, depth_in=None):
             P = path_to_root(par, t)
             for j in P:
                 vis[b, t, j] = True
-            anc[b, t] = np.uint64(sum(1 << j for j in P))
+            anc[b, t] = anc_words(P, N)
             depth[b, t] = len(P)
             pos[b, t] = ctx_len[b] - 1 + len(P)
         if depth_in is not None and np.any(np.asarray(depth_in)[b] != depth[b]):

@@ -44,10 +44,11 @@ def _sdpa(qrows, K, V, allowed, scale):
         scale=scale)[0, 0]
 
 
-def test_chain_equals_causal_attention():
+@pytest.mark.parametrize("N", [9, 128])
+def test_chain_equals_causal_attention(N):
     """A chain tree is plain causal attention over context ++ chain (the chain
-    verify the serve spec starts from)."""
-    N = 9
+    verify the serve spec starts from); at 128 nodes the ancestor sets span
+    two words."""
     x = _case(tree="chain", N=N, ctx=(45, 45))
     out, _ = _run_oracle(x)
     G = x.Hq // x.Hkv

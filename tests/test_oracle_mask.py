@@ -36,7 +36,7 @@ def test_worked_example_mask_shape():
     assert not dense[0, 0, 10, ctx + 16] and not dense[0, 0, 10, ctx + 1]
 
 
-@pytest.mark.parametrize("n", [1, 2, 7, 32, 64])
+@pytest.mark.parametrize("n", [1, 2, 7, 32, 64, 65, 128])
 def test_chain_is_lower_triangular(n):
     par = np.arange(-1, n - 1)[None]
     r = M.tree_mask(par, [37])
@@ -45,12 +45,23 @@ def test_chain_is_lower_triangular(n):
     assert r["pos"][0].tolist() == list(range(37, 37 + n))
 
 
-@pytest.mark.parametrize("n", [1, 5, 64])
+@pytest.mark.parametrize("n", [1, 5, 64, 100, 128])
 def test_star_is_identity(n):
     r = M.tree_mask(np.full((1, n), -1), [9])
     assert np.array_equal(r["vis"][0], np.eye(n, dtype=bool))
     assert np.all(r["depth"] == 1) and np.all(r["pos"] == 9)
-    assert r["anc"][0].tolist() == [1 << i for i in range(n)]
+    assert [M.anc_value(w) for w in r["anc"][0]] == [1 << i for i in range(n)]
+    assert r["anc"].shape == (1, n, (n + 63) // 64)
+
+
+def test_word_layout():
+    """Node j is bit j % 64 of word j // 64: the chain's node 100 holds nodes
+    0..63 in word 0 and 64..100 in word 1."""
+    r = M.tree_mask(np.arange(-1, 127)[None], [1])
+    w = r["anc"][0, 100]
+    assert int(w[0]) == (1 << 64) - 1 and int(w[1]) == (1 << 37) - 1
+    assert r["anc"][0, 63].tolist() == [(1 << 64) - 1, 0]
+    assert r["anc"][0, 64].tolist() == [(1 << 64) - 1, 1]
 
 
 def test_leaf_sibling_closed_form():
@@ -83,7 +94,8 @@ def _ancestor_matrix_by_powers(par):
 
 
 @pytest.mark.parametrize("kind,n", [("random_parent", 16), ("random_parent", 64),
-                                    ("spine_first", 32), ("ddtree", 24)])
+                                    ("spine_first", 32), ("ddtree", 24), ("random_parent", 128),
+                                    ("ddtree", 128), ("random_parent", 77)])
 def test_against_matrix_powers_and_invariants(kind, n):
     kw = dict(max_depth=8) if kind == "spine_first" else {}
     vocab = 64 if kind == "ddtree" else 1000
@@ -97,12 +109,12 @@ def test_against_matrix_powers_and_invariants(kind, n):
         assert np.array_equal(vis, _ancestor_matrix_by_powers(par))
         # popcount(anc) == depth; anc is the packed row of vis
         for t in range(n):
-            a = int(r["anc"][b, t])
+            a = M.anc_value(r["anc"][b, t])
             assert bin(a).count("1") == r["depth"][b, t]
             assert a == sum(1 << int(j) for j in np.flatnonzero(vis[t]))
             # recurrence: own bit plus the parent's set
             if par[t] >= 0:
-                assert a == (1 << t) | int(r["anc"][b, par[t]])
+                assert a == (1 << t) | M.anc_value(r["anc"][b, par[t]])
                 assert r["depth"][b, t] == r["depth"][b, par[t]] + 1
             else:
                 assert a == 1 << t and r["depth"][b, t] == 1

@@ -100,7 +100,8 @@ def check_greedy_identity(tokens, parent, history, vocab, rng, ties=False):
 
 
 @pytest.mark.parametrize("kind,n", [("random_parent", 16), ("spine_first", 32),
-                                    ("leaf_sibling", 32), ("random_parent", 64), ("chain", 8)])
+                                    ("leaf_sibling", 32), ("random_parent", 64), ("chain", 8),
+                                    ("random_parent", 128)])
 def test_greedy_identity_random_trees(kind, n):
     vocab = 50
     tb = W.make_trees(21, kind, 40, n, vocab, max_depth=8)
@@ -181,14 +182,15 @@ def test_adversarial_cases():
     assert check_greedy_identity(np.array([-5, vocab + 3]), np.array([-1, -1]), hist, vocab, rng) == 0
 
 
-def test_max_nodes_chain_of_64():
+@pytest.mark.parametrize("n", [64, 128])
+def test_max_nodes_chain(n):
     vocab = 1000
     hist = [7]
-    g = greedy_decode(hist, 65, vocab)
-    toks = np.array(g[:64])
-    par = np.arange(-1, 63)
+    g = greedy_decode(hist, n + 1, vocab)
+    toks = np.array(g[:n])
+    par = np.arange(-1, n - 1)
     rng = np.random.default_rng(0)
-    assert check_greedy_identity(toks, par, hist, vocab, rng) == 64
+    assert check_greedy_identity(toks, par, hist, vocab, rng) == n
 
 
 def _brute_force(tokens, parent, am):
