@@ -55,8 +55,11 @@ enum {
 
 typedef void* tv_stream;
 
-#define TV_MAX_NODES 64   /* one 64-bit ancestor word per node, one wave64 per tree */
-#define TV_BLOCK_SIZE 16  /* tokens per KV-cache page                               */
+#define TV_MAX_NODES 128     /* draft nodes per tree (mask, attention, walk, KV commit) */
+#define TV_GDN_MAX_NODES 64  /* draft nodes per tree for the Gated DeltaNet calls       */
+#define TV_BLOCK_SIZE 16     /* tokens per KV-cache page                                */
+/* 64-bit words of one node's ancestor set: node j is bit j % 64 of word j / 64 */
+#define TV_ANC_WORDS(N) (((N) + 63) / 64)
 
 /* ------------------------------------------------------------------------
  * tree_mask_build — ancestor-or-self mask, depths and position ids.
@@ -72,7 +75,8 @@ typedef void* tv_stream;
  *                               the derived ones
  *   ctx_len      int32 [B]      committed tokens per sequence (the last accepted
  *                               token included, at position ctx_len - 1)
- *   anc_mask     uint64 [B, N]  out: bit j set iff node j is node t or an ancestor
+ *   anc_mask     uint64 [B, N, TV_ANC_WORDS(N)]  out: bit j % 64 of word j / 64
+ *                               set iff node j is node t or an ancestor of t
  *   depth_out    int32 [B, N]   out: derived depth (1 = child of the root)
  *   position_ids int32 [B, N]   out: ctx_len[b] - 1 + depth
  *   dense_bias   float [B, N, N] optional out (NULL = skip): 0 where anc bit set,
@@ -112,7 +116,7 @@ tv_status tree_mask_build(const int32_t* parent, const int32_t* depth_in,
  *   block_table  int32 [B, max_blocks_per_seq]  page of positions 16j..16j+15
  *   ctx_len      int32 [B]               context length (<= max_ctx_len)
  *   max_ctx_len  host bound on ctx_len, <= 16 * max_blocks_per_seq; sizes the grid
- *   anc_mask     uint64 [B, N]           from tree_mask_build
+ *   anc_mask     uint64 [B, N, TV_ANC_WORDS(N)]  from tree_mask_build
  *   position_ids int32 [B, N]            from tree_mask_build
  *   out          [B, N, Hq, D]           attention output, in out_dtype
  *   workspace    device scratch of tree_verify_attn_workspace_size(...) bytes
@@ -156,9 +160,9 @@ tv_status tree_verify_attn(const void* q, const void* k_node, const void* v_node
  *   alpha     float [B, N, H] gates
  *   beta      float [B, N, H] write strengths
  *   S0        float [B, H, Dk, Dv] committed state (read only)
- *   anc_mask  uint64 [B, N]   from tree_mask_build
+ *   anc_mask  uint64 [B, N]   from tree_mask_build (one word per node: N <= 64)
  *   out       [B, N, H, Dv]   out_dtype (TV_F32, or TV_BF16 with bf16 inputs)
- * Supported: 1 <= N <= TV_MAX_NODES, Dk == Dv == 128.
+ * Supported: 1 <= N <= TV_GDN_MAX_NODES, Dk == Dv == 128.
  * ------------------------------------------------------------------------ */
 tv_status tree_gdn_verify(const void* q, const void* k, const void* v,
                           const float* alpha, const float* beta, const float* S0,
@@ -217,7 +221,7 @@ tv_status tree_walk_accept(const int32_t* tokens, const int32_t* parent,
  *   S_out      float [B, H, Dk, Dv] out: the new committed state; may be S0
  *              itself (each (sequence, head) block is read before it is written)
  * k, v, S0 and S_out must be 16-byte aligned.
- * Supported: 1 <= N <= TV_MAX_NODES, Dk == Dv == 128, dtype TV_F32 or TV_BF16.
+ * Supported: 1 <= N <= TV_GDN_MAX_NODES, Dk == Dv == 128, dtype TV_F32 or TV_BF16.
  * ------------------------------------------------------------------------ */
 tv_status tree_gdn_commit(const void* k, const void* v, const float* alpha,
                           const float* beta, const float* S0,

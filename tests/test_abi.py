@@ -49,7 +49,7 @@ def test_mask_validation(lib):
     assert f(FAKE, None, FAKE, 1, 4, None, FAKE, FAKE, None, FAKE, None) == tv.TV_ERR_NULL
     assert f(FAKE, None, FAKE, 0, 4, FAKE, FAKE, FAKE, None, FAKE, None) == tv.TV_ERR_SHAPE
     assert f(FAKE, None, FAKE, 1, 0, FAKE, FAKE, FAKE, None, FAKE, None) == tv.TV_ERR_SHAPE
-    assert f(FAKE, None, FAKE, 1, 65, FAKE, FAKE, FAKE, None, FAKE, None) == tv.TV_ERR_UNSUPPORTED
+    assert f(FAKE, None, FAKE, 1, 129, FAKE, FAKE, FAKE, None, FAKE, None) == tv.TV_ERR_UNSUPPORTED
 
 
 def _attn(lib, **kw):
@@ -71,7 +71,7 @@ def test_attn_validation(lib):
     assert _attn(lib, Hq=12, Hkv=8) == tv.TV_ERR_SHAPE
     assert _attn(lib, maxctx=4097) == tv.TV_ERR_SHAPE          # beyond 16 * max_blocks
     assert _attn(lib, nblk=0) == tv.TV_ERR_SHAPE
-    assert _attn(lib, N=65) == tv.TV_ERR_UNSUPPORTED
+    assert _attn(lib, N=129) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, D=96) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, bs=32) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, dt=7) == tv.TV_ERR_UNSUPPORTED
@@ -124,7 +124,7 @@ def test_walk_validation(lib):
     assert f(*bad) == tv.TV_ERR_NULL
     bad = list(base); bad[5] = 0
     assert f(*bad) == tv.TV_ERR_SHAPE
-    bad = list(base); bad[4] = 65
+    bad = list(base); bad[4] = 129
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
     bad = list(base); bad[6] = 5
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
@@ -168,5 +168,5 @@ def test_kv_commit_validation(lib):
     assert call(a7=0) == tv.TV_ERR_SHAPE            # empty pool
     assert call(a11=96) == tv.TV_ERR_UNSUPPORTED     # D
     assert call(a12=32) == tv.TV_ERR_UNSUPPORTED     # block size
-    assert call(a9=65) == tv.TV_ERR_UNSUPPORTED
+    assert call(a9=129) == tv.TV_ERR_UNSUPPORTED
     assert call(a0=ctypes.c_void_p(0x1008)) == tv.TV_ERR_UNSUPPORTED   # not 16-byte aligned

@@ -195,3 +195,24 @@ def test_wide_query_tiles(lib, D):
                 ctx_len=np.array([0, 1, 17, 63, 700, 5000], dtype=np.int32))
     for w in (0, 37, 6000):
         check_full(lib, x, w, f"wide D={D}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("tree,N,G,D", [("chain", 128, 1, 64), ("random_parent", 100, 2, 128),
+                                        ("ddtree", 128, 4, 128), ("random_parent", 65, 1, 256)])
+def test_trees_past_one_word(lib, dtype, tree, N, G, D):
+    """Trees of 65 to 128 nodes: ancestor sets in two words, node keys over
+    several tiles (and, for bf16, 64-key stages); windows that cut into the
+    node keys of deep chains."""
+    trees = W.make_trees(52, tree, 3, N, 4096 if tree == "ddtree" else 100)
+    x, _ = make(1, B=3, N=N, Hq=2 * G, Hkv=2, D=D, trees=trees, dtype=dtype,
+                ctx_len=np.array([0, 40, 900], dtype=np.int32))
+    for w in (0, 20, 70):
+        check_full(lib, x, w, f"{tree} N={N} G={G} D={D} {dtype}")
+
+
+def test_c4_shape_at_128_nodes(lib):
+    """The DDTree batch's head shape (G = 8, D = 128) with 128-node trees:
+    1024 query rows per kv head."""
+    x, _ = make(4, B=2, N=128, ctx_lo=1500, ctx_hi=2100, tree="ddtree")
+    check_full(lib, x, 0, "c4-shape N=128")

@@ -142,3 +142,13 @@ def test_kv_commit_skips_pages_outside(lib):
     table[0, 1] = kc.shape[0] + 5        # positions 16..31 of sequence 0: outside the pool
     table[1, 2] = -7
     _kv_check(lib, x, table, kc, vc, acc, na, ctx, "pages outside")
+
+
+def test_kv_commit_128_node_chain(lib):
+    """A 128-node tree whose whole chain is accepted: positions ctx .. ctx + 127
+    over nine pages."""
+    ctx = [5, 300]
+    x, table, kc, vc, acc, na = _kv_case(72, B=2, N=128, Hkv=2, D=128, dtype=torch.bfloat16, ctx=ctx)
+    acc[:] = np.arange(128)
+    na[:] = [128, 77]
+    _kv_check(lib, x, table, kc, vc, acc, na, ctx, "128 nodes")

@@ -33,7 +33,10 @@ def run_and_compare(lib, parent, ctx, depth_in=None, dense=True):
                                             ("spine_first", 32, 32, 1000), ("ddtree", 64, 64, 4096),
                                             ("random_parent", 16, 64, 1000), ("chain", 2, 64, 10),
                                             ("star", 3, 64, 10), ("random_parent", 5, 1, 10),
-                                            ("random_parent", 7, 33, 10)])
+                                            ("random_parent", 7, 33, 10), ("random_parent", 4, 128, 1000),
+                                            ("chain", 2, 128, 10), ("star", 2, 100, 10),
+                                            ("ddtree", 8, 128, 4096), ("random_parent", 3, 65, 10),
+                                            ("chain", 1, 65, 10)])
 def test_trees(lib, kind, B, N, vocab):
     tb = W.make_trees(40, kind, B, N, vocab, max_depth=8)
     ctx = np.random.default_rng(1).integers(1, 40000, size=B)

@@ -38,7 +38,9 @@ def test_c1_shape(lib, dtype, plant):
 
 
 @pytest.mark.parametrize("kind,B,N,V", [("ddtree", 4, 64, 262144), ("spine_first", 8, 32, 32000),
-                                        ("leaf_sibling", 8, 32, 5003), ("random_parent", 6, 64, 77)])
+                                        ("leaf_sibling", 8, 32, 5003), ("random_parent", 6, 64, 77),
+                                        ("ddtree", 3, 128, 262144), ("random_parent", 5, 128, 77),
+                                        ("random_parent", 4, 97, 1000), ("chain", 2, 128, 50)])
 def test_planted_trees(lib, kind, B, N, V):
     tb = W.make_trees(41, kind, B, N, V if kind != "ddtree" else 262144, max_depth=8)
     for plant_len in (None, 3, 0):
@@ -58,7 +60,7 @@ def test_greedy_identity_adversarial(lib):
     vocab = 64
     cases = []
     for trial in range(60):
-        n = int(rng.integers(1, 65))
+        n = int(rng.integers(1, 129))
         parent = np.array([int(rng.integers(-1, i)) if i else -1 for i in range(n)])
         if trial % 5 == 0:
             parent = np.arange(-1, n - 1)
@@ -101,7 +103,8 @@ def test_ties_and_duplicates(lib):
 
 def test_edge_sizes(lib):
     rng = np.random.default_rng(6)
-    for (B, N, V) in [(1, 1, 1), (3, 1, 2), (2, 64, 3), (1, 64, 262144), (5, 5, 1001), (2, 3, 262145)]:
+    for (B, N, V) in [(1, 1, 1), (3, 1, 2), (2, 64, 3), (1, 64, 262144), (5, 5, 1001), (2, 3, 262145),
+                      (2, 65, 3), (1, 127, 5), (2, 128, 3), (1, 128, 262144)]:
         parent = np.stack([np.array([int(rng.integers(-1, i)) if i else -1 for i in range(N)])
                            for _ in range(B)])
         tokens = rng.integers(-1, V + 1, size=(B, N))
@@ -154,3 +157,22 @@ def test_full_size_ddtree_batch(lib):
         assert got["accepted_nodes"][b, :a].tolist() == nodes
         assert np.all(got["accepted_tokens"][b, a + 1:] == -1) and np.all(got["accepted_nodes"][b, a:] == -1)
     assert got["num_accepted"][::2].min() >= 1
+
+
+@pytest.mark.parametrize("n", [63, 64, 65, 127, 128])
+def test_full_chain_acceptance(lib, n):
+    """A chain whose every node is the target's greedy token: all n nodes are
+    accepted and the bonus lands in the last token slot (slot n)."""
+    vocab = 1000
+    hist = [11, 5]
+    g = greedy_decode(hist, n + 1, vocab)
+    tokens = np.array(g[:n])
+    parent = np.arange(-1, n - 1)
+    rng = np.random.default_rng(n)
+    L = logits_from_target(hist, tokens, parent, vocab, rng, ties=False)
+    say(f"walk full chain n={n}")
+    got = gpu_walk(lib, tokens[None], parent[None], torch.from_numpy(L[None].astype(np.float32)).to(DEV))
+    assert int(got["num_accepted"][0]) == n
+    assert got["accepted_tokens"][0].tolist() == g
+    assert got["accepted_nodes"][0].tolist() == list(range(n))
+    compare(got, OWk.tree_walk(tokens[None], parent[None], L[None].astype(np.float32).astype(np.float64)))

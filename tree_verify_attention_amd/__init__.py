@@ -21,7 +21,13 @@ LIB_PATH = os.path.join(_HERE, "libtreeverify.so")
 TV_OK, TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_LAUNCH = range(6)
 TV_F32, TV_BF16 = 0, 1
 TV_TREE_OK, TV_TREE_BAD_PARENT, TV_TREE_BAD_DEPTH, TV_TREE_BAD_CTX = range(4)
-MAX_NODES = 64
+MAX_NODES = 128      # mask, attention, walk, KV commit
+GDN_MAX_NODES = 64   # the Gated DeltaNet calls
+
+
+def anc_words(n: int) -> int:
+    """64-bit words of one node's ancestor set (node j: bit j % 64 of word j // 64)."""
+    return (n + 63) // 64
 BLOCK_SIZE = 16
 
 EXPORTS = (
@@ -113,7 +119,7 @@ def _dtype_code(dt) -> int:
 
 def tree_mask_build(parent: torch.Tensor, ctx_len: torch.Tensor, depth_in: Optional[torch.Tensor] = None,
                     dense_bias: bool = False, out: Optional[dict] = None) -> dict:
-    """Ancestor words (int64 tensor holding the uint64 bits), depths, position
+    """Ancestor words [B, N, anc_words(N)] (int64 tensor holding the uint64 bits), depths, position
     ids, per-sequence status and optionally the N x N additive bias."""
     lib = load()
     dev = parent.device
@@ -123,7 +129,7 @@ def tree_mask_build(parent: torch.Tensor, ctx_len: torch.Tensor, depth_in: Optio
     if depth_in is not None:
         _need(depth_in, "depth_in", torch.int32, dev, (B, N))
     if out is None:
-        out = dict(anc=torch.empty(B, N, dtype=torch.int64, device=dev),
+        out = dict(anc=torch.empty(B, N, anc_words(N), dtype=torch.int64, device=dev),
                    depth=torch.empty(B, N, dtype=torch.int32, device=dev),
                    pos=torch.empty(B, N, dtype=torch.int32, device=dev),
                    status=torch.empty(B, dtype=torch.int32, device=dev),
@@ -161,7 +167,7 @@ def tree_verify_attn(q, k_node, v_node, k_cache, v_cache, block_table, ctx_len, 
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
     _need(ctx_len, "ctx_len", torch.int32, dev, (B,))
-    _need(anc, "anc", torch.int64, dev, (B, N))
+    _need(anc, "anc", torch.int64, dev, (B, N, anc_words(N)))
     _need(pos, "pos", torch.int32, dev, (B, N))
     odt = out.dtype if out is not None else (out_dtype or dt)
     if out is None:
@@ -197,7 +203,7 @@ def tree_gdn_verify(q, k, v, alpha, beta, S0, anc, out=None, out_dtype=None) -> 
     _need(alpha, "alpha", torch.float32, dev, (B, N, H))
     _need(beta, "beta", torch.float32, dev, (B, N, H))
     _need(S0, "S0", torch.float32, dev, (B, H, Dk, Dv))
-    _need(anc, "anc", torch.int64, dev, (B, N))
+    _need(anc, "anc", torch.int64, dev, (B, N, anc_words(N)))
     odt = out.dtype if out is not None else (out_dtype or dt)
     if out is None:
         out = torch.empty(B, N, H, Dv, dtype=odt, device=dev)

@@ -44,6 +44,8 @@ constexpr int kTile = 32;           // keys per LDS stage
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxPages = 1024;     // page indices of one stream segment cached in LDS
 constexpr int kSplitPages = 4096;   // of one split (splits are capped to fit)
+constexpr int kAncW = (TV_MAX_NODES + 63) / 64;  // ancestor words per node at most
+static_assert(kThreads >= TV_MAX_NODES, "one thread per node position");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -172,12 +174,18 @@ __device__ __forceinline__ SeqPlan seq_plan(int ctx_raw, int max_ctx, int window
   return p;
 }
 
-// smallest and largest position id of the tree (N <= 64 nodes, read by wave 0)
+// smallest and largest position id of the tree (read by wave 0, lane l taking
+// nodes l, l + 64, ...)
 __device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2* s_rng) {
   const int tid = threadIdx.x;
   if (tid < 64) {
-    int lo = tid < N ? pos_b[tid] : 0x7fffffff;
-    int hi = tid < N ? pos_b[tid] : -0x7fffffff;
+    int lo = 0x7fffffff, hi = -0x7fffffff;
+#pragma unroll
+    for (int i = tid; i < TV_MAX_NODES; i += 64) {
+      const int v = i < N ? pos_b[i] : 0;
+      lo = i < N ? min(lo, v) : lo;
+      hi = i < N ? max(hi, v) : hi;
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       lo = min(lo, __shfl_xor(lo, off, 64));
@@ -222,8 +230,18 @@ __device__ __forceinline__ float pair_sum(float v) {
   return a + b;
 }
 
+// Ancestor word that holds the node keys from key_base on (key_base a multiple
+// of 32, so a tile's keys share it); selected, not indexed, so that the words
+// stay in registers.
+__device__ __forceinline__ uint64_t anc_word(const uint64_t (&a)[kAncW], int key_base) {
+  uint64_t r = a[0];
+#pragma unroll
+  for (int w = 1; w < kAncW; ++w) r = (key_base >> 6) == w ? a[w] : r;
+  return r;
+}
+
 // Query fragments (MFMA B operand: row lr, 8 (bf16) or 1 (fp32) dims per k
-// step), position and ancestor word of one query row.  Loaded ahead of the
+// step), position and ancestor words of one query row.  Loaded ahead of the
 // plan and the page indices, so that these loads overlap theirs.
 template <typename T, int D>
 struct RowIn {
@@ -231,7 +249,7 @@ struct RowIn {
   bf16x8_t qb[sizeof(T) == 2 ? kQ : 1];
   float qf[sizeof(T) == 4 ? kQ : 1];
   int pos;
-  uint64_t anc;
+  uint64_t anc[kAncW];  // words past the tree's word count are 0
 };
 
 // this lane's query row of row group rg of unit (b, g): R = rg * kRows + 16 *
@@ -261,7 +279,10 @@ __device__ __forceinline__ RowIn<T, D> row_in(const T* __restrict__ q,
     for (int ks = 0; ks < RowIn<T, D>::kQ; ++ks) ri.qf[ks] = row_ok ? q[qoff + ks * 4 + lg] : 0.0f;
   }
   ri.pos = pos_b[t];
-  ri.anc = anc[static_cast<size_t>(b) * N + t];
+  const int nw = (N + 63) / 64;
+#pragma unroll
+  for (int w = 0; w < kAncW; ++w)
+    ri.anc[w] = w < nw ? anc[(static_cast<size_t>(b) * N + t) * nw + w] : 0ull;
   return ri;
 }
 
@@ -326,7 +347,9 @@ __device__ __forceinline__ void attn_segment(
 #pragma unroll
   for (int ks = 0; ks < (sizeof(T) == 4 ? kQ : 1); ++ks) qf_f[ks] = ri.qf[ks];
   const int row_pos = ri.pos;
-  const uint64_t row_anc = ri.anc;
+  uint64_t row_anc[kAncW];
+#pragma unroll
+  for (int w = 0; w < kAncW; ++w) row_anc[w] = ri.anc[w];
   // make the query and row loads complete here, so that the compiler's wait
   // bookkeeping does not place a full drain inside the key loop
   if constexpr (sizeof(T) == 2) {
@@ -336,7 +359,9 @@ __device__ __forceinline__ void attn_segment(
 #pragma unroll
     for (int ks = 0; ks < kQ; ++ks) asm volatile("" ::"v"(qf_f[ks]));
   }
-  asm volatile("" ::"v"(row_pos), "v"(row_anc));
+  asm volatile("" ::"v"(row_pos));
+#pragma unroll
+  for (int w = 0; w < kAncW; ++w) asm volatile("" ::"v"(row_anc[w]));
 
   f32x4_t acc[C::kDT];
 #pragma unroll
@@ -469,15 +494,17 @@ __device__ __forceinline__ void attn_segment(
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[j][i] = S[j][i] * scale_log2;
     } else {
+      // a node tile's 32 keys share one ancestor word
+      const uint64_t aw = anc_word(row_anc, base);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = base + 16 * j + 4 * lg + i;
-          const int kpos = is_node ? s_pos[key & 63] : key;
+          const int kpos = is_node ? s_pos[key & (TV_MAX_NODES - 1)] : key;
           const int dpos = row_pos - kpos;
           bool vis = row_ok & (key < lim);
-          vis &= !is_node | (((row_anc >> (key & 63)) & 1ull) != 0ull);
+          vis &= !is_node | (((aw >> (key & 63)) & 1ull) != 0ull);
           vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
           x[j][i] = vis ? S[j][i] * scale_log2 : -INFINITY;
         }
@@ -652,7 +679,7 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
   __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kStageBytes];
   __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kStageBytes];
   __shared__ int s_pages[kSplitPages];
-  __shared__ int s_pos[64];
+  __shared__ int s_pos[TV_MAX_NODES];
   __shared__ int2 s_rng;
 
   // Blocks are dealt round-robin to the 8 XCDs.  Work units are numbered
@@ -675,7 +702,7 @@ __global__ __launch_bounds__((kThreads * split_teams<T, D>()), 1) void attn_spli
   // the context length and this lane's query row go out with the tree positions
   const int ctx_raw = ctx_len[b];
   const RowIn<T, D> ri = row_in<T, D>(q, pos_b, anc, b, g, rg, N, Hq, G, rows);
-  if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
+  if (tid < TV_MAX_NODES) s_pos[tid] = tid < N ? pos_b[tid] : 0;
   const int2 prng = tree_pos_range(pos_b, N, &s_rng);
   const SeqPlan sp = seq_plan(ctx_raw, max_ctx, window, prng.x, nsplit_max, split_tokens);
   if (s >= sp.nsplit) return;  // uniform over the workgroup
@@ -809,7 +836,7 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   __shared__ __align__(1024) unsigned char kring[kSlots * kSB];
   __shared__ __align__(1024) unsigned char vring[kSlots * kSB];
   __shared__ int s_pages[kSplitPages];
-  __shared__ int s_pos[64];
+  __shared__ int s_pos[TV_MAX_NODES];
   __shared__ int2 s_rng;
 
   // work units as in the per-unit layout: split-major, XCD-interleaved, the
@@ -836,7 +863,8 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   bool ok[kRT];
   bf16x8_t qf[kRT][kQ];
   int rpos[kRT];
-  uint64_t ranc[kRT];
+  uint64_t ranc[kRT][kAncW];
+  const int nw = (N + 63) / 64;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     Rr[rt] = (rg * kW + wave) * 16 * kRT + 16 * rt + lr;
@@ -851,9 +879,11 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
       qf[rt][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
     rpos[rt] = pos_b[t];
-    ranc[rt] = anc[static_cast<size_t>(b) * N + t];
+#pragma unroll
+    for (int w = 0; w < kAncW; ++w)
+      ranc[rt][w] = w < nw ? anc[(static_cast<size_t>(b) * N + t) * nw + w] : 0ull;
   }
-  if (tid < 64) s_pos[tid] = tid < N ? pos_b[tid] : 0;
+  if (tid < TV_MAX_NODES) s_pos[tid] = tid < N ? pos_b[tid] : 0;
   const int2 prng = tree_pos_range(pos_b, N, &s_rng);
   const SeqPlan sp = seq_plan(ctx_raw, max_ctx, window, prng.x, nsplit_max, split_tokens);
   if (s >= sp.nsplit) return;  // uniform over the workgroup
@@ -872,7 +902,9 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
     for (int ks = 0; ks < kQ; ++ks) asm volatile("" ::"v"(qf[rt][ks]));
-    asm volatile("" ::"v"(rpos[rt]), "v"(ranc[rt]));
+    asm volatile("" ::"v"(rpos[rt]));
+#pragma unroll
+    for (int w = 0; w < kAncW; ++w) asm volatile("" ::"v"(ranc[rt][w]));
   }
   f32x4_t acc[kRT][C::kDT];
   float m_run[kRT], l_run[kRT];
@@ -883,9 +915,9 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
     m_run[rt] = -INFINITY;
     l_run[rt] = 0.0f;
   }
-  // stages: context keys [k0, k1) in stages of 64, then the node keys (N <= 64)
+  // stages: context keys [k0, k1) in stages of 64, then the node keys
   const int nctx = k1 > k0 ? (k1 - k0 + kSK - 1) / kSK : 0;
-  const int ntiles = nctx + (last ? 1 : 0);
+  const int ntiles = nctx + (last ? (N + kSK - 1) / kSK : 0);
   const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
   const unsigned char* kcb = reinterpret_cast<const unsigned char*>(kc);
   const unsigned char* vcb = reinterpret_cast<const unsigned char*>(vc);
@@ -899,7 +931,7 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   auto issue = [&](int it, bool values) {
     unsigned char* dst = (values ? vring : kring) + (it % kSlots) * kSB;
     const bool is_node = it >= nctx;
-    const int base = is_node ? 0 : k0 + it * kSK;
+    const int base = is_node ? (it - nctx) * kSK : k0 + it * kSK;
     const int lim = is_node ? N : k1;
     const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
 #pragma unroll
@@ -940,7 +972,7 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
       const unsigned char* Ks = kring + (it % kSlots) * kSB;
       const unsigned char* Vs = vring + (it % kSlots) * kSB;
       const bool is_node = it >= nctx;
-      const int base = is_node ? 0 : k0 + it * kSK;
+      const int base = is_node ? (it - nctx) * kSK : k0 + it * kSK;
       const int lim = is_node ? N : k1;
 
       // S^T of every row tile for the four 16-key quarters of the stage: the
@@ -989,6 +1021,7 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
       bf16x8_t ph[kRT][kKT], pl[kRT][kKT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
+        const uint64_t aw = anc_word(ranc[rt], base);  // a 64-key stage: one word
         float x[2 * kKT][4];
 #pragma unroll
         for (int h = 0; h < 2 * kKT; ++h)
@@ -998,10 +1031,10 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
               x[h][i] = S[rt][h][i] * scale_log2;
             } else {
               const int key = base + 16 * h + 4 * lg + i;
-              const int kpos = is_node ? s_pos[key & 63] : key;
+              const int kpos = is_node ? s_pos[key & (TV_MAX_NODES - 1)] : key;
               const int dpos = rpos[rt] - kpos;
               bool vis = ok[rt] & (key < lim);
-              vis &= !is_node | (((ranc[rt] >> (key & 63)) & 1ull) != 0ull);
+              vis &= !is_node | (((aw >> (key & 63)) & 1ull) != 0ull);
               vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
               x[h][i] = vis ? S[rt][h][i] * scale_log2 : -INFINITY;
             }
@@ -1231,7 +1264,7 @@ __global__ __launch_bounds__(kThreads, (stream_min_wg<T, D>())) void attn_stream
   __shared__ __align__(1024) unsigned char kring[C::kSlots * C::kTileBytes];
   __shared__ __align__(1024) unsigned char vring[C::kSlots * C::kTileBytes];
   __shared__ int s_pages[kMaxPages];
-  __shared__ int s_pos[64];  // node positions: read only under a window, never here
+  __shared__ int s_pos[TV_MAX_NODES];  // node positions: read only under a window, never here
   __shared__ int s_pref[kMaxSeqs + 1];
   __shared__ int s_ctx[kMaxSeqs + 1];
 

@@ -29,8 +29,8 @@ __global__ __launch_bounds__(256) void gdn_commit_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* S0, const int32_t* __restrict__ acc_nodes,
     const int32_t* __restrict__ num_acc, int N, int H, float* S_out) {
-  __shared__ __align__(16) float s_kv[TV_MAX_NODES][2 * kGD];  // [step][k | v]
-  __shared__ float2 s_ab[TV_MAX_NODES];                        // (alpha, beta) per step
+  __shared__ __align__(16) float s_kv[TV_GDN_MAX_NODES][2 * kGD];  // [step][k | v]
+  __shared__ float2 s_ab[TV_GDN_MAX_NODES];                    // (alpha, beta) per step
   __shared__ __align__(16) float s_u[8][kGD];                  // partial k^T S per row group
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x;

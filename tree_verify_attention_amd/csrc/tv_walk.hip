@@ -5,7 +5,7 @@
 // target argmax at the current node, then emit the argmax where no child
 // matches.  Two kernels: a row argmax over the vocabulary (an HBM stream, one
 // workgroup per logits row), then one wave per tree that walks the parent
-// pointers (lane = node; a ballot finds the matching child each step).
+// pointers (lanes = nodes; ballots find the matching child each step).
 #include "tv_internal.h"
 
 namespace tv {
@@ -116,6 +116,11 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_kernel(const T* __restr
   }
 }
 
+// Lane l holds nodes l and l + 64 (trees of up to 128 nodes): one ballot per
+// half finds the matching children, the lower half first, so the lowest
+// matching index wins.
+constexpr int kWalkSlots = (TV_MAX_NODES + 63) / 64;
+
 __global__ __launch_bounds__(64) void walk_kernel(const int32_t* __restrict__ tokens,
                                                   const int32_t* __restrict__ parent,
                                                   const int32_t* __restrict__ am, int N,
@@ -124,33 +129,52 @@ __global__ __launch_bounds__(64) void walk_kernel(const int32_t* __restrict__ to
                                                   int32_t* __restrict__ num_acc) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const bool act = t < N;
   const size_t base = static_cast<size_t>(b) * N;
-  const int tok = act ? tokens[base + t] : -1;
-  const int par = act ? parent[base + t] : -2;
-  const bool valid = act && par >= -1 && par < t;
   const int32_t* amb = am + static_cast<size_t>(b) * (N + 1);
+  int tok[kWalkSlots], par[kWalkSlots];
+  bool valid[kWalkSlots];
+#pragma unroll
+  for (int s = 0; s < kWalkSlots; ++s) {
+    const int n = t + 64 * s;
+    const bool act = n < N;
+    tok[s] = act ? tokens[base + n] : -1;
+    par[s] = act ? parent[base + n] : -2;
+    valid[s] = act && par[s] >= -1 && par[s] < n;
+  }
 
-  int cur = -1, row = 0, a = 0;
-  int my_node = -1, my_tok = -1;
+  int cur = -1, a = 0;
+  int my_node[kWalkSlots], my_tok[kWalkSlots];
+#pragma unroll
+  for (int s = 0; s < kWalkSlots; ++s) my_node[s] = my_tok[s] = -1;
   int pred = amb[0];
   // a matched child always has a larger index than its parent, so the walk
   // ends within N steps
   for (int step = 0; step < N; ++step) {
-    const uint64_t m = __ballot(valid && par == cur && tok == pred);
-    if (m == 0ull) break;
-    const int i = __ffsll(static_cast<unsigned long long>(m)) - 1;
-    if (t == a) { my_node = i; my_tok = pred; }
+    int i = -1;
+#pragma unroll
+    for (int s = 0; s < kWalkSlots; ++s) {
+      const uint64_t m = __ballot(valid[s] && par[s] == cur && tok[s] == pred);
+      if (i < 0 && m != 0ull) i = 64 * s + __ffsll(static_cast<unsigned long long>(m)) - 1;
+    }
+    if (i < 0) break;
+    // accepted entry a lives in lane a % 64, slot a / 64
+#pragma unroll
+    for (int s = 0; s < kWalkSlots; ++s)
+      if (t + 64 * s == a) { my_node[s] = i; my_tok[s] = pred; }
     ++a;
     cur = i;
-    row = 1 + i;
-    pred = amb[row];
+    pred = amb[1 + i];
   }
   // pred is now the bonus token (argmax at the last accepted node)
   int32_t* ot = acc_tok + static_cast<size_t>(b) * (N + 1);
-  if (act) acc_node[base + t] = t < a ? my_node : -1;
-  if (t < N + 1) ot[t] = t < a ? my_tok : (t == a ? pred : -1);
-  if (t == 0 && N + 1 > 64) ot[64] = (64 == a) ? pred : -1;  // N == 64: slot 64
+#pragma unroll
+  for (int s = 0; s < kWalkSlots; ++s) {
+    const int n = t + 64 * s;
+    if (n < N) acc_node[base + n] = n < a ? my_node[s] : -1;
+    if (n < N + 1) ot[n] = n < a ? my_tok[s] : (n == a ? pred : -1);
+  }
+  // slot N of the token row when the lane slots end before it (never below a)
+  if (t == 0 && N == 64 * kWalkSlots) ot[N] = (N == a) ? pred : -1;
   if (t == 0) num_acc[b] = a;
 }
 
