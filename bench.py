@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-curve", action="store_true",
+                    help="skip the cost curve over tree sizes (its attention calls share kernel "
+                         "names with the step's, which muddles a kernel trace of the step)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=2)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per global-layer attention call (rocprofv3 --pmc)")
@@ -102,7 +105,7 @@ class Step:
         self.gdn = W.gdn_inputs(3, B=self.B, N=self.N, H=g["H"], Dk=g["Dk"], Dv=g["Dv"], tree="spine_first",
                                 dtype=torch.bfloat16, trees=trees, device=dev)
         B, N = self.B, self.N
-        self.mask_out = dict(anc=torch.empty(B, N, dtype=torch.int64, device=dev),
+        self.mask_out = dict(anc=torch.empty(B, N, tv.anc_words(N), dtype=torch.int64, device=dev),
                              depth=torch.empty(B, N, dtype=torch.int32, device=dev),
                              pos=torch.empty(B, N, dtype=torch.int32, device=dev),
                              status=torch.empty(B, dtype=torch.int32, device=dev), dense_bias=None)
@@ -201,6 +204,71 @@ def next_rows(step: Step, dev, reps: int) -> dict:
             "gdn_commit": {"ms": round(gms, 4), "bytes": gbytes, "GBps": round(gbytes / (gms * 1e-3) / 1e9, 1),
                            "frac_of_8TBps": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "kv_commit": {"ms": round(kms, 4), "bytes": kbytes}}
+
+
+CURVE_NODES = (1, 2, 4, 8, 16, 32, 64, 128)
+
+
+def cost_curve(step: Step, dev, reps: int) -> dict:
+    """Verify cost against tree size on the mixed batch: the same 32 sequences,
+    context lengths, paged caches and head shapes, with spine-first trees of
+    N nodes (depth <= 8) and fresh seeded queries and node keys/values for
+    each N.  Per N: event-timed mask + window-layer + global-layer attention
+    (the verify calls of that workload), averaged over `reps` passes; the
+    least-squares slope gives the cost per extra candidate."""
+    tv = step.tv
+    from synth import workloads as W
+    B = step.B
+    res = {"N": [], "ms": [], "mask_ms": [], "window_ms": [], "global_ms": []}
+    for N in CURVE_NODES:
+        trees = W.make_trees(3, "spine_first", B, N, 1000, max_depth=min(8, N), tag=1000 + N)
+        parent = torch.from_numpy(trees.parent).to(dev)
+        mo = dict(anc=torch.empty(B, N, tv.anc_words(N), dtype=torch.int64, device=dev),
+                  depth=torch.empty(B, N, dtype=torch.int32, device=dev),
+                  pos=torch.empty(B, N, dtype=torch.int32, device=dev),
+                  status=torch.empty(B, dtype=torch.int32, device=dev), dense_bias=None)
+        calls = []
+        for li, x in enumerate(step.layers):
+            seed = 7000 + 10 * N + 3 * li
+            q = W._device_normal(seed, (B, N, x.Hq, x.D), x.q.dtype, dev)
+            kn = W._device_normal(seed + 1, (B, N, x.Hkv, x.D), x.q.dtype, dev)
+            vn = W._device_normal(seed + 2, (B, N, x.Hkv, x.D), x.q.dtype, dev)
+            ws = torch.empty(max(1, tv.tree_verify_attn_workspace_size(B, N, x.Hq, x.Hkv, x.D, x.max_ctx_len,
+                                                                       x.window)), dtype=torch.uint8, device=dev)
+            o = torch.empty_like(q)
+            calls.append((x, q, kn, vn, ws, o))
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+
+        def once(e=None):
+            if e: e[0].record()
+            tv.tree_mask_build(parent, step.ctx_len, out=mo)
+            if e: e[1].record()
+            for li, (x, q, kn, vn, ws, o) in enumerate(calls):
+                tv.tree_verify_attn(q, kn, vn, x.k_cache, x.v_cache, x.block_table, x.ctx_len, x.max_ctx_len,
+                                    mo["anc"], mo["pos"], x.window, x.scale, out=o, workspace=ws)
+                if e: e[2 + li].record()
+        for _ in range(10):
+            once()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            once(ev[i])
+        torch.cuda.synchronize()
+        # mask, window layer, global layer
+        parts = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev]).mean(axis=0)
+        res["N"].append(N)
+        res["mask_ms"].append(round(float(parts[0]), 4))
+        res["window_ms"].append(round(float(parts[1]), 4))
+        res["global_ms"].append(round(float(parts[2]), 4))
+        res["ms"].append(round(float(parts.sum()), 4))
+        del calls
+    n = np.array(res["N"], dtype=np.float64)
+    t = np.array(res["ms"])
+    small = n <= 32
+    res["ms_per_candidate_N_le_32"] = round(float(np.polyfit(n[small], t[small], 1)[0]), 5)
+    res["ms_per_candidate_all"] = round(float(np.polyfit(n, t, 1)[0]), 5)
+    res["workload"] = ("mixed batch (B=32, ctx U[1024,32768], Hq=16, Hkv=8, D=256, bf16) with "
+                       "spine-first trees of N nodes; mask + W=512 layer + global layer")
+    return res
 
 
 def cpu_baseline(step: Step, nseq: int):
@@ -326,6 +394,8 @@ def main():
                      "call_ms": round(per_call["attn1"], 4)},
     }
     out["next_rows"] = next_rows(step, dev, args.steps)
+    if not args.no_curve:
+        out["next_rows"]["cost_curve"] = cost_curve(step, dev, min(args.steps, 20))
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
