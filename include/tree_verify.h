@@ -126,7 +126,7 @@ tv_status tree_mask_build(const int32_t* parent, const int32_t* depth_in,
  * leaves the buffers).
  * Supported: 1 <= N <= TV_MAX_NODES, D in {64, 128, 256}, block_size == 16,
  * Hq % Hkv == 0, dtype TV_F32 or TV_BF16 (out_dtype TV_F32, or TV_BF16 with
- * bf16 inputs), Hq / Hkv * N <= 4096.
+ * bf16 inputs), Hq / Hkv * N <= 4096, 0 < scale < infinity.
  * ------------------------------------------------------------------------ */
 size_t tree_verify_attn_workspace_size(int32_t B, int32_t N, int32_t Hq,
                                        int32_t Hkv, int32_t D,

@@ -73,6 +73,10 @@ def test_attn_validation(lib):
     assert _attn(lib, nblk=0) == tv.TV_ERR_SHAPE
     assert _attn(lib, N=129) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, D=96) == tv.TV_ERR_UNSUPPORTED
+    assert _attn(lib, scale=0.0) == tv.TV_ERR_UNSUPPORTED
+    assert _attn(lib, scale=-0.5) == tv.TV_ERR_UNSUPPORTED
+    assert _attn(lib, scale=float("inf")) == tv.TV_ERR_UNSUPPORTED
+    assert _attn(lib, scale=float("nan")) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, bs=32) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, dt=7) == tv.TV_ERR_UNSUPPORTED
     assert _attn(lib, dt=tv.TV_F32, odt=tv.TV_BF16) == tv.TV_ERR_UNSUPPORTED

@@ -71,6 +71,9 @@ tv_status tree_verify_attn(const void* q, const void* k_node, const void* v_node
   if (!dtype_ok(dtype) || !out_dtype_ok(dtype, out_dtype)) return TV_ERR_UNSUPPORTED;
   if (N > TV_MAX_NODES || block_size != TV_BLOCK_SIZE) return TV_ERR_UNSUPPORTED;
   if (D != 64 && D != 128 && D != 256) return TV_ERR_UNSUPPORTED;
+  // a softmax scale is positive and finite (the kernels take row maxima on the
+  // unscaled scores)
+  if (!(scale > 0.0f) || !(scale < INFINITY)) return TV_ERR_UNSUPPORTED;
   if (static_cast<long long>(Hq / Hkv) * N > kMaxRowsPerKvHead) return TV_ERR_UNSUPPORTED;
   const tv::AttnPlan plan = tv::attn_plan(B, N, Hq, Hkv, D, max_ctx_len, window);
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))

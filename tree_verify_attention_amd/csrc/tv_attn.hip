@@ -45,6 +45,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxPages = 1024;     // page indices of one stream segment cached in LDS
 constexpr int kSplitPages = 4096;   // of one split (splits are capped to fit)
 constexpr int kAncW = (TV_MAX_NODES + 63) / 64;  // ancestor words per node at most
+constexpr float kLazy = 8.0f;  // log2 headroom of the lazily moved softmax reference
 static_assert(kThreads >= TV_MAX_NODES, "one thread per node position");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -52,6 +53,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // kTeams teams of kWaves waves share a workgroup: a ring stage holds kTeams
 // consecutive 32-key tiles, team i computes the i-th, and the teams' softmax
@@ -1018,61 +1021,99 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
       // bf16 high and low parts (keys 16 h + 4 lg + i of quarter h)
       const bool full = !is_node && base + kSK <= lim &&
                         (window <= 0 || (base >= win_all && base + kSK - 1 <= prng.x));
+      // raw scores, -inf where a key is not visible; the mask runs only on
+      // partial stages, as one straight block per kind of stage
+      float sv[kRT][2 * kKT][4];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[rt][h][i] = S[rt][h][i];
+      if (!full) {
+        if (is_node) {
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt) {
+            const uint64_t aw = anc_word(ranc[rt], base);  // a 64-key stage: one word
+#pragma unroll
+            for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int key = base + 16 * h + 4 * lg + i;
+                const int dpos = rpos[rt] - s_pos[key & (TV_MAX_NODES - 1)];
+                bool vis = ok[rt] & (key < lim) & (((aw >> (key & 63)) & 1ull) != 0ull);
+                vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+                sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+              }
+          }
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+            for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int key = base + 16 * h + 4 * lg + i;
+                const int dpos = rpos[rt] - key;
+                bool vis = ok[rt] & (key < lim);
+                vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+                sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+              }
+        }
+      }
+
+      // online softmax per row tile in the log2 domain (scale > 0, so the
+      // maximum is taken on the raw scores and the scale folds into one fma
+      // per score).  The reference point m moves only when the stage maximum
+      // passes it by more than kLazy (always from -inf): the probabilities stay
+      // below 2^kLazy, and most stages skip the rescale of the accumulators.
+      // P goes to bf16 high and low parts, pairs at a time.
       bf16x8_t ph[kRT][kKT], pl[kRT][kKT];
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const uint64_t aw = anc_word(ranc[rt], base);  // a 64-key stage: one word
-        float x[2 * kKT][4];
-#pragma unroll
-        for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (full) {
-              x[h][i] = S[rt][h][i] * scale_log2;
-            } else {
-              const int key = base + 16 * h + 4 * lg + i;
-              const int kpos = is_node ? s_pos[key & (TV_MAX_NODES - 1)] : key;
-              const int dpos = rpos[rt] - kpos;
-              bool vis = ok[rt] & (key < lim);
-              vis &= !is_node | (((aw >> (key & 63)) & 1ull) != 0ull);
-              vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-              x[h][i] = vis ? S[rt][h][i] * scale_log2 : -INFINITY;
-            }
-          }
         float mt = -INFINITY;
 #pragma unroll
         for (int h = 0; h < 2 * kKT; ++h)
-          mt = fmaxf(mt, fmaxf(fmaxf(x[h][0], x[h][1]), fmaxf(x[h][2], x[h][3])));
+          mt = fmaxf(mt, fmaxf(fmaxf(sv[rt][h][0], sv[rt][h][1]), fmaxf(sv[rt][h][2], sv[rt][h][3])));
         mt = pair_max<32>(pair_max<16>(mt));
-        const float m_new = fmaxf(m_run[rt], mt);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float mc = mt * scale_log2;
+        const bool need = mc > m_run[rt] + kLazy;
+        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+          // rows that keep their reference scale by exactly 1 (also rows still
+          // at -inf, where the difference of references would be NaN)
+          const float alpha = need ? fast_exp2(m_run[rt] - mc) : 1.0f;  // 0 from -inf
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha;
+          m_run[rt] = need ? mc : m_run[rt];
+        }
+        const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
         float ps = 0.0f;
+        float pv[2 * kKT][4];
 #pragma unroll
         for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            x[h][i] = fast_exp2(x[h][i] - m_use);
-            ps += x[h][i];
+            pv[h][i] = fast_exp2(fmaf(sv[rt][h][i], scale_log2, neg_m));
+            ps += pv[h][i];
           }
-        if (__builtin_amdgcn_ballot_w64(m_new != m_run[rt]) != 0ull) {
-          const float alpha = fast_exp2(m_run[rt] - m_use);
-          l_run[rt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha;
-        }
         l_run[rt] += ps;
-        m_run[rt] = m_new;
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
+        for (int kt = 0; kt < kKT; ++kt) {
+          uint32_t hw[4], lw[4];
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float pv = x[2 * kt + j][i];
-              const __bf16 hb = static_cast<__bf16>(pv);
-              ph[rt][kt][4 * j + i] = hb;
-              pl[rt][kt][4 * j + i] = static_cast<__bf16>(pv - static_cast<float>(hb));
-            }
+          for (int e = 0; e < 4; ++e) {
+            // elements 2e, 2e + 1 of the fragment: keys (16 j + 4 lg + i), j = e / 2, i = 2 (e % 2) + 0, 1
+            const float a0 = pv[2 * kt + e / 2][2 * (e % 2)];
+            const float a1 = pv[2 * kt + e / 2][2 * (e % 2) + 1];
+            const f32x2_t f = {a0, a1};
+            hw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+            const f32x2_t r = {a0 - __uint_as_float(hw[e] << 16), a1 - __uint_as_float(hw[e] & 0xffff0000u)};
+            lw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+          }
+          ph[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          pl[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
       }
 
       if (steady) wait_vmem<kIPW * 2 * (kSlots - 1)>();
