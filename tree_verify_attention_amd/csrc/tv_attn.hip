@@ -792,29 +792,31 @@ __device__ __forceinline__ void wide_row_store(bool final_out, const f32x4_t* ac
 
 // Query tiles wider than one workgroup of 64 rows (G * N > 64, for instance
 // 8 query heads per kv head times 64 nodes = 512 rows).  Each wave carries
-// kRT tiles of 16 rows, so a workgroup covers 16 kRT kW rows of a unit and
+// kRT tiles of 16 rows, so a workgroup covers 16 kRT * 8 rows of a unit and
 // each key or value fragment read from LDS feeds kRT products; the row
 // groups of a unit no longer stream the same keys once per 64 rows.  Keys
-// go through the ring in stages of two 32-key tiles, and the softmax runs
-// once per stage, so the per-iteration work (waits, barriers, issue,
-// cross-lane reductions) is spread over 64 keys.  Same work units (unit, row
-// group, split), masking and partials as the per-unit layout; bf16 inputs.
+// go through the ring in stages of two 32-key tiles (one at D = 256), and
+// the softmax runs once per stage.  Same work units (unit, row group, split),
+// masking and partials as the per-unit layout; bf16 inputs.
 //
-// Waves per workgroup and row tiles per wave: 8 waves (two per SIMD, so that
-// one wave's softmax runs under the other's matrix products) of 2 row tiles,
-// or 1 at D = 256 (registers); at D = 64 a stage is too small to give 8 waves
-// a 1 KB load each, so 4 waves of 4.
-template <int D>
-constexpr int wide_waves() {
-  return D == 64 ? 4 : 8;
-}
+// Eight waves, two per SIMD, in two groups: waves 0-3 and 4-7 (one of each
+// per SIMD) take the three steps of a stage -- scores (MFMA), softmax (VALU),
+// P.V (MFMA) -- in opposite orders.  In iteration i, group 0 runs P.V of
+// stage i - 1, then the scores and the softmax of stage i; group 1 runs the
+// softmax of stage i - 1, then P.V of stage i - 1 and the scores of stage i.
+// So on every SIMD one wave's softmax runs while the other wave's products
+// keep the matrix unit busy.  One barrier per stage: behind it the keys of
+// stage i and the values of stage i - 1 have landed, and every wave is done
+// with the keys of stage i - 1 and the values of stage i - 2, whose slots are
+// refilled at once.
 template <int D>
 constexpr int wide_tiles() {
-  return D == 64 ? 4 : (D == 256 ? 1 : 2);
+  return D == 256 ? 1 : 2;
 }
+constexpr int kWideWaves = 8;
 
 template <typename TO, int D>
-__global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
+__global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kn,
     const uint16_t* __restrict__ vn, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ bt, int max_blocks,
@@ -826,14 +828,19 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   using T = uint16_t;
   using C = Cfg<T, D>;
   constexpr int kRT = wide_tiles<D>();
-  constexpr int kW = wide_waves<D>();
+  constexpr int kW = kWideWaves;
   constexpr int kNT = 64 * kW;
-  constexpr int kKT = 2;                                 // 32-key tiles per stage
+  constexpr int kKT = D == 256 ? 1 : 2;                  // 32-key tiles per stage
   constexpr int kSK = kKT * kTile;                       // keys per stage
   constexpr int kSB = kKT * C::kTileBytes;               // bytes of a stage (keys or values)
-  constexpr int kSlots = (98304 / (2 * kSB)) < 2 ? 2 : ((98304 / (2 * kSB)) > 4 ? 4 : 98304 / (2 * kSB));
-  constexpr int kIPW = kSB / 1024 / kW;                  // 1 KB loads per wave per stage
-  static_assert(kIPW >= 1 && kIPW * 1024 * kW == kSB, "stage must split over the waves");
+  constexpr int kFitW = 131072 / (2 * kSB);
+  constexpr int kSlots = kFitW > 6 ? 6 : kFitW;
+  // the waves of group 0 issue every load (group 1 carries the longer chain
+  // of an iteration): kIPW 1 KB loads per loading wave and stage
+  constexpr int kLW = kW / 2;
+  constexpr int kIPW = kSB / 1024 / kLW;
+  static_assert(kSlots >= 3, "the ring holds the keys of stage i + 1 while stage i is in use");
+  static_assert(kIPW >= 1 && kIPW * 1024 * kLW == kSB, "stage must split over the loading waves");
   static_assert(kIPW * (2 * kSlots - 1) <= 63, "vmcnt range");
   constexpr int kQ = D / 32;  // k steps of the score products
   __shared__ __align__(1024) unsigned char kring[kSlots * kSB];
@@ -856,6 +863,7 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
 
@@ -918,7 +926,7 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
     m_run[rt] = -INFINITY;
     l_run[rt] = 0.0f;
   }
-  // stages: context keys [k0, k1) in stages of 64, then the node keys
+  // stages: context keys [k0, k1) in stages of kSK, then the node keys
   const int nctx = k1 > k0 ? (k1 - k0 + kSK - 1) / kSK : 0;
   const int ntiles = nctx + (last ? (N + kSK - 1) / kSK : 0);
   const int win_all = window > 0 ? prng.y - window + 1 : -0x7fffffff;
@@ -929,228 +937,276 @@ __global__ __launch_bounds__(64 * wide_waves<D>(), 1) void attn_wide_kernel(
   wait_vmem<0>();
   __syncthreads();  // page cache ready
 
-  // loads of one stage's keys (or values) into its slot: stage row r (0..63)
-  // is row r % 32 of tile r / 32, swizzled as in the per-unit layout
-  auto issue = [&](int it, bool values) {
-    unsigned char* dst = (values ? vring : kring) + (it % kSlots) * kSB;
-    const bool is_node = it >= nctx;
-    const int base = is_node ? (it - nctx) * kSK : k0 + it * kSK;
-    const int lim = is_node ? N : k1;
-    const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
+  // Loads of stage keys (or values) into their slot: stage row r is row r % 32
+  // of tile r / 32, swizzled as in the per-unit layout.  Lane data of load j
+  // (group 0): its stage row and granule, fixed for the whole stream.
+  const int lwave = wave % kLW;
+  int ld_row[kIPW], ld_part[kIPW];
 #pragma unroll
-    for (int j = 0; j < kIPW; ++j) {
-      const int blk = wave * kIPW + j;
-      const int gl = blk * 64 + lane;
-      const int row = gl / C::kGran;
-      const int part = (gl % C::kGran) ^ swz_key<T, D>(row);
-      const int key = min(base + row, lim - 1);
-      size_t off;
-      if (is_node) {
-        off = ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes;
-      } else {
-        const int pi = (key >> 4) - p0;
-        const int page = pi < kSplitPages ? s_pages[pi] : min(max(bt_b[key >> 4], 0), num_blocks - 1);
-        off = ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes;
+  for (int j = 0; j < kIPW; ++j) {
+    const int gl = (lwave * kIPW + j) * 64 + lane;
+    ld_row[j] = gl / C::kGran;
+    ld_part[j] = (gl % C::kGran) ^ swz_key<T, D>(ld_row[j]);
+  }
+  // the values of stage sv and the keys of stage sk (either may lie past the
+  // stream, then it is skipped): every page index is read from LDS first, so
+  // that one wait covers all of them (splits are capped so that every page of
+  // a split is in the cache)
+  auto refill = [&](int sv, int sk) __attribute__((always_inline)) {
+    if (grp != 0) return;
+    const int st[2] = {sv, sk};
+    int key[2][kIPW], page[2][kIPW];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool is_node = st[q] >= nctx;
+      const int base = is_node ? (st[q] - nctx) * kSK : k0 + st[q] * kSK;
+      const int lim = is_node ? N : k1;
+#pragma unroll
+      for (int j = 0; j < kIPW; ++j) {
+        key[q][j] = min(base + ld_row[j], lim - 1);
+        page[q][j] = s_pages[min(max((key[q][j] >> 4) - p0, 0), kSplitPages - 1)];
       }
-      lds_dma16(src + off + part * 16, dst + blk * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (st[q] >= ntiles) continue;
+      const bool values = q == 0;
+      unsigned char* dst = (values ? vring : kring) + (st[q] % kSlots) * kSB;
+      const bool is_node = st[q] >= nctx;
+      const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
+#pragma unroll
+      for (int j = 0; j < kIPW; ++j) {
+        const size_t off =
+            is_node ? ((static_cast<size_t>(b) * N + key[q][j]) * Hkv + g) * C::kRowBytes
+                    : ((static_cast<size_t>(page[q][j]) * Hkv + g) * 16 + (key[q][j] & 15)) * C::kRowBytes;
+        lds_dma16(src + off + ld_part[j] * 16, dst + (lwave * kIPW + j) * 1024);
+      }
     }
     asm volatile("" ::: "memory");
   };
 
-  if (ntiles > 0) {
-    for (int i = 0; i < kSlots && i < ntiles; ++i) {
-      issue(i, false);
-      issue(i, true);
-    }
-    for (int it = 0; it < ntiles; ++it) {
-      const int newest = min(it + kSlots - 1, ntiles - 1);
-      const int v_out = it == 0 ? newest : min(it + kSlots - 2, ntiles - 1);
-      // the full ring in flight: the count is a constant
-      const bool steady = it > 0 && it + kSlots - 1 < ntiles;
-      if (steady) wait_vmem<kIPW * 2 * (kSlots - 1)>();
-      else wait_vm_upto(kIPW * ((v_out - it + 1) + (newest - it)));
-      lds_barrier();  // keys of stage `it` have landed; every wave is done with stage it - 1
-      if (it > 0 && it + kSlots - 1 < ntiles) issue(it + kSlots - 1, true);
+  f32x4_t S[kRT][2 * kKT];               // scores of a stage, from its products to its softmax
+  bf16x8_t ph[kRT][kKT], pl[kRT][kKT];  // its probabilities, from the softmax to P.V
 
-      const unsigned char* Ks = kring + (it % kSlots) * kSB;
-      const unsigned char* Vs = vring + (it % kSlots) * kSB;
-      const bool is_node = it >= nctx;
-      const int base = is_node ? (it - nctx) * kSK : k0 + it * kSK;
-      const int lim = is_node ? N : k1;
-
-      // S^T of every row tile for the four 16-key quarters of the stage: the
-      // key fragments of a k step are read once (two k steps ahead) and feed
-      // all kRT row tiles
-      f32x4_t S[kRT][2 * kKT];
+  // S^T of every row tile for the 16-key quarters of stage `it`: the key
+  // fragments of a k step are read once (two k steps ahead) and feed all kRT
+  // row tiles
+  auto scores = [&](int it) __attribute__((always_inline)) {
+    const unsigned char* Ks = kring + (it % kSlots) * kSB;
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
+    for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-        for (int h = 0; h < 2 * kKT; ++h) S[rt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2 * kKT; ++h) S[rt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        const unsigned char* Kt = Ks + kt * C::kTileBytes;
-        constexpr int kAh = kQ < 2 ? kQ : 2;
-        uint4 ka[kAh + 1][2];
-        auto kread = [&](int ks, int j) __attribute__((always_inline)) {
-          return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
-        };
-#pragma unroll
-        for (int ks = 0; ks < kAh; ++ks) {
-          ka[ks][0] = kread(ks, 0);
-          ka[ks][1] = kread(ks, 1);
-        }
-#pragma unroll
-        for (int ks = 0; ks < kQ; ++ks) {
-          if (ks + kAh < kQ) {
-            ka[(ks + kAh) % (kAh + 1)][0] = kread(ks + kAh, 0);
-            ka[(ks + kAh) % (kAh + 1)][1] = kread(ks + kAh, 1);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            S[rt][2 * kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][0]), qf[rt][ks], S[rt][2 * kt], 0, 0, 0);
-            S[rt][2 * kt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][1]), qf[rt][ks], S[rt][2 * kt + 1], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // mask and online softmax per row tile over the 64 keys; P split into
-      // bf16 high and low parts (keys 16 h + 4 lg + i of quarter h)
-      const bool full = !is_node && base + kSK <= lim &&
-                        (window <= 0 || (base >= win_all && base + kSK - 1 <= prng.x));
-      // raw scores, -inf where a key is not visible; the mask runs only on
-      // partial stages, as one straight block per kind of stage
-      float sv[kRT][2 * kKT][4];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-        for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[rt][h][i] = S[rt][h][i];
-      if (!full) {
-        if (is_node) {
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt) {
-            const uint64_t aw = anc_word(ranc[rt], base);  // a 64-key stage: one word
-#pragma unroll
-            for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = base + 16 * h + 4 * lg + i;
-                const int dpos = rpos[rt] - s_pos[key & (TV_MAX_NODES - 1)];
-                bool vis = ok[rt] & (key < lim) & (((aw >> (key & 63)) & 1ull) != 0ull);
-                vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-                sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
-              }
-          }
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-            for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = base + 16 * h + 4 * lg + i;
-                const int dpos = rpos[rt] - key;
-                bool vis = ok[rt] & (key < lim);
-                vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-                sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
-              }
-        }
-      }
-
-      // online softmax per row tile in the log2 domain (scale > 0, so the
-      // maximum is taken on the raw scores and the scale folds into one fma
-      // per score).  The reference point m moves only when the stage maximum
-      // passes it by more than kLazy (always from -inf): the probabilities stay
-      // below 2^kLazy, and most stages skip the rescale of the accumulators.
-      // P goes to bf16 high and low parts, pairs at a time.
-      bf16x8_t ph[kRT][kKT], pl[kRT][kKT];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        float mt = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 2 * kKT; ++h)
-          mt = fmaxf(mt, fmaxf(fmaxf(sv[rt][h][0], sv[rt][h][1]), fmaxf(sv[rt][h][2], sv[rt][h][3])));
-        mt = pair_max<32>(pair_max<16>(mt));
-        const float mc = mt * scale_log2;
-        const bool need = mc > m_run[rt] + kLazy;
-        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-          // rows that keep their reference scale by exactly 1 (also rows still
-          // at -inf, where the difference of references would be NaN)
-          const float alpha = need ? fast_exp2(m_run[rt] - mc) : 1.0f;  // 0 from -inf
-          l_run[rt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha;
-          m_run[rt] = need ? mc : m_run[rt];
-        }
-        const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
-        float ps = 0.0f;
-        float pv[2 * kKT][4];
-#pragma unroll
-        for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[h][i] = fast_exp2(fmaf(sv[rt][h][i], scale_log2, neg_m));
-            ps += pv[h][i];
-          }
-        l_run[rt] += ps;
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) {
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // elements 2e, 2e + 1 of the fragment: keys (16 j + 4 lg + i), j = e / 2, i = 2 (e % 2) + 0, 1
-            const float a0 = pv[2 * kt + e / 2][2 * (e % 2)];
-            const float a1 = pv[2 * kt + e / 2][2 * (e % 2) + 1];
-            const f32x2_t f = {a0, a1};
-            hw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-            const f32x2_t r = {a0 - __uint_as_float(hw[e] << 16), a1 - __uint_as_float(hw[e] & 0xffff0000u)};
-            lw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
-          }
-          ph[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-          pl[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-        }
-      }
-
-      if (steady) wait_vmem<kIPW * 2 * (kSlots - 1)>();
-      else wait_vm_upto(kIPW * 2 * (newest - it));
-      lds_barrier();  // values of stage `it` have landed; every wave is done with its keys
-      if (it + kSlots < ntiles) issue(it + kSlots, false);
-
-      // O^T += V^T P^T, one 32-key tile at a time: the value fragments of a
-      // column tile feed all row tiles; reads run two steps ahead
-      const int vrow = 4 * lg + (lr >> 2);
-      const int vcol = 8 * (lr & 3);
-      constexpr int kSteps = C::kDT * kKT;  // (column tile, key tile) pairs
-      constexpr int kVA = 2;
-      s16x4_t vlo[kVA + 1], vhi[kVA + 1];
-      auto vread = [&](int st, s16x4_t& lo, s16x4_t& hi) __attribute__((always_inline)) {
-        const int dt = st / kKT, kt = st % kKT;
-        const unsigned char* Vt = Vs + kt * C::kTileBytes;
-        lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
-        hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+    for (int kt = 0; kt < kKT; ++kt) {
+      const unsigned char* Kt = Ks + kt * C::kTileBytes;
+      constexpr int kAh = kQ < 2 ? kQ : 2;
+      uint4 ka[kAh + 1][2];
+      auto kread = [&](int ks, int j) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
       };
 #pragma unroll
-      for (int st = 0; st < kVA; ++st) vread(st, vlo[st], vhi[st]);
+      for (int ks = 0; ks < kAh; ++ks) {
+        ka[ks][0] = kread(ks, 0);
+        ka[ks][1] = kread(ks, 1);
+      }
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        if (st + kVA < kSteps) vread(st + kVA, vlo[(st + kVA) % (kVA + 1)], vhi[(st + kVA) % (kVA + 1)]);
-        __builtin_amdgcn_sched_barrier(0);
-        const int dt = st / kKT, kt = st % kKT;
-        const s16x4_t lo = vlo[st % (kVA + 1)];
-        const s16x4_t hi = vhi[st % (kVA + 1)];
-        const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt][kt], acc[rt][dt], 0, 0, 0);
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt][kt], acc[rt][dt], 0, 0, 0);
+      for (int ks = 0; ks < kQ; ++ks) {
+        if (ks + kAh < kQ) {
+          ka[(ks + kAh) % (kAh + 1)][0] = kread(ks + kAh, 0);
+          ka[(ks + kAh) % (kAh + 1)][1] = kread(ks + kAh, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          S[rt][2 * kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][0]), qf[rt][ks], S[rt][2 * kt], 0, 0, 0);
+          S[rt][2 * kt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ka[ks % (kAh + 1)][1]), qf[rt][ks], S[rt][2 * kt + 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // mask and online softmax of stage `it` in the log2 domain.  Masks run only
+  // on partial stages, as one straight block per kind of stage.  The scale is
+  // positive, so row maxima are taken on the raw scores and the scale folds
+  // into one fma per score.  The reference point m moves only when a stage
+  // maximum passes it by more than kLazy (always from -inf): probabilities
+  // stay below 2^kLazy and most stages skip the rescale of the accumulators.
+  // P goes to bf16 high and low parts, pairs at a time (keys 16 h + 4 lg + i).
+  auto softmax = [&](int it) __attribute__((always_inline)) {
+    const bool is_node = it >= nctx;
+    const int base = is_node ? (it - nctx) * kSK : k0 + it * kSK;
+    const int lim = is_node ? N : k1;
+    const bool full = !is_node && base + kSK <= lim &&
+                      (window <= 0 || (base >= win_all && base + kSK - 1 <= prng.x));
+    float sv[kRT][2 * kKT][4];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[rt][h][i] = S[rt][h][i];
+    if (!full) {
+      if (is_node) {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          const uint64_t aw = anc_word(ranc[rt], base);  // a stage lies within one word
+#pragma unroll
+          for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = base + 16 * h + 4 * lg + i;
+              const int dpos = rpos[rt] - s_pos[key & (TV_MAX_NODES - 1)];
+              bool vis = ok[rt] & (key < lim) & (((aw >> (key & 63)) & 1ull) != 0ull);
+              vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+              sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+            }
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = base + 16 * h + 4 * lg + i;
+              const int dpos = rpos[rt] - key;
+              bool vis = ok[rt] & (key < lim);
+              vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+              sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+            }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2 * kKT; ++h)
+        mt = fmaxf(mt, fmaxf(fmaxf(sv[rt][h][0], sv[rt][h][1]), fmaxf(sv[rt][h][2], sv[rt][h][3])));
+      mt = pair_max<32>(pair_max<16>(mt));
+      const float mc = mt * scale_log2;
+      const bool need = mc > m_run[rt] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+        // rows that keep their reference scale by exactly 1 (also rows still
+        // at -inf, where the difference of references would be NaN)
+        const float alpha = need ? fast_exp2(m_run[rt] - mc) : 1.0f;  // 0 from -inf
+        l_run[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha;
+        m_run[rt] = need ? mc : m_run[rt];
+      }
+      const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+      float ps = 0.0f;
+      float pv[2 * kKT][4];
+#pragma unroll
+      for (int h = 0; h < 2 * kKT; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[h][i] = fast_exp2(fmaf(sv[rt][h][i], scale_log2, neg_m));
+          ps += pv[h][i];
+        }
+      l_run[rt] += ps;
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // fragment elements 2e, 2e + 1: quarter 2 kt + e / 2, keys 4 lg + 2 (e % 2) + 0, 1
+          const float a0 = pv[2 * kt + e / 2][2 * (e % 2)];
+          const float a1 = pv[2 * kt + e / 2][2 * (e % 2) + 1];
+          const f32x2_t f = {a0, a1};
+          hw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+          const f32x2_t r = {a0 - __uint_as_float(hw[e] << 16), a1 - __uint_as_float(hw[e] & 0xffff0000u)};
+          lw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+        }
+        ph[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        pl[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+      }
+    }
+  };
+
+  // O^T += V^T P^T for stage `it`, one 32-key tile at a time: the value
+  // fragments of a column tile feed all row tiles; reads run two steps ahead
+  auto pv_product = [&](int it) __attribute__((always_inline)) {
+    const unsigned char* Vs = vring + (it % kSlots) * kSB;
+    const int vrow = 4 * lg + (lr >> 2);
+    const int vcol = 8 * (lr & 3);
+    constexpr int kSteps = C::kDT * kKT;  // (column tile, key tile) pairs
+    constexpr int kVA = 2;
+    s16x4_t vlo[kVA + 1], vhi[kVA + 1];
+    auto vread = [&](int st, s16x4_t& lo, s16x4_t& hi) __attribute__((always_inline)) {
+      const int dt = st / kKT, kt = st % kKT;
+      const unsigned char* Vt = Vs + kt * C::kTileBytes;
+      lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
+      hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+    };
+#pragma unroll
+    for (int st = 0; st < kVA; ++st) vread(st, vlo[st], vhi[st]);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      if (st + kVA < kSteps) vread(st + kVA, vlo[(st + kVA) % (kVA + 1)], vhi[(st + kVA) % (kVA + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int dt = st / kKT, kt = st % kKT;
+      const s16x4_t lo = vlo[st % (kVA + 1)];
+      const s16x4_t hi = vhi[st % (kVA + 1)];
+      const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt][kt], acc[rt][dt], 0, 0, 0);
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt][kt], acc[rt][dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (ntiles > 0) {
+    // Loads go out in the order K(0) V(0) K(1) V(1) ...: the prologue takes
+    // K(0 .. kSlots - 1) and V(0 .. kSlots - 2); iteration i refills V(i - 2 +
+    // kSlots), then K(i - 1 + kSlots).
+    for (int i = 0; i < kSlots && i < ntiles; ++i) refill(i >= 1 ? i - 1 : ntiles, i);
+    if (ntiles <= kSlots - 1) refill(ntiles - 1, ntiles);  // a short stream: its last values too
+    // the start of iteration it: K(it) and V(it - 1) have landed (later loads
+    // may stay in flight), then the freed slots are refilled
+    auto sync = [&](int it) __attribute__((always_inline)) {
+      if (grp != 0) {
+        // no loads of its own: the barrier covers group 0's
+      } else if (it < ntiles) {
+        if (it >= 2 && it - 2 + kSlots < ntiles) {
+          wait_vmem<kIPW * 2 * (kSlots - 2)>();
+        } else {
+          const int kmax = min(ntiles - 1, it >= 2 ? it - 2 + kSlots : kSlots - 1);
+          const int vmax = min(ntiles - 1, it >= 2 ? it - 3 + kSlots : kSlots - 2);
+          wait_vm_upto(kIPW * (max(0, kmax - it) + max(0, vmax - it + 1)));
+        }
+      } else {
+        wait_vmem<0>();  // V(ntiles - 1), the last load
+      }
+      lds_barrier();
+      if (it >= 1 && it - 2 + kSlots < ntiles) refill(it - 2 + kSlots, it - 1 + kSlots);
+    };
+    // one loop per group, so that only the probabilities (group 0) or only the
+    // scores (group 1) stay live from one iteration to the next
+    if (grp == 0) {
+      for (int it = 0; it <= ntiles; ++it) {
+        sync(it);
+        if (it >= 1) pv_product(it - 1);
+        if (it < ntiles) {
+          scores(it);
+          softmax(it);
+        }
+      }
+    } else {
+      for (int it = 0; it <= ntiles; ++it) {
+        sync(it);
+        if (it >= 1) {
+          softmax(it - 1);
+          pv_product(it - 1);
+        }
+        if (it < ntiles) scores(it);
       }
     }
   }
@@ -1534,11 +1590,11 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
   if constexpr (sizeof(T) == 2) {
     if (pl.rows > kRows) {
       // wide query tiles: 16 kRT rows per wave
-      constexpr int kRowsW = 16 * wide_tiles<D>() * wide_waves<D>();
+      constexpr int kRowsW = 16 * wide_tiles<D>() * kWideWaves;
       const int rgw = (pl.rows + kRowsW - 1) / kRowsW;
       const long long gridw = (units + 7) / 8 * 8 * rgw;
       hipLaunchKernelGGL((attn_wide_kernel<TO, D>), dim3(static_cast<unsigned>(gridw)),
-                         dim3(64 * wide_waves<D>()), 0, stream, static_cast<const T*>(q),
+                         dim3(64 * kWideWaves), 0, stream, static_cast<const T*>(q),
                          static_cast<const T*>(k_node), static_cast<const T*>(v_node),
                          static_cast<const T*>(k_cache), static_cast<const T*>(v_cache),
                          block_table, max_blocks, num_blocks, ctx_len, max_ctx, anc, pos, N, Hq,
