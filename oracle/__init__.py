@@ -17,9 +17,15 @@ Modules and the passage each follows:
 * ``gdn``   Gated DeltaNet outputs along each node's root path, with no state
   written back (DFlash-TfM summary, "3. Rollback-vrije Boom-verificatie voor
   GDN"); also the masked triangular-solve form of the same computation.
+* ``kvcommit``  the accepted path's keys and values written into the paged
+  cache at positions ctx_len + s (serve-integration spec, layout contract).
+* ``treebuild``  draft-tree construction: per-depth top-k of the draft
+  distribution and best-first growth on cumulative log-probability (DDTree
+  validation post, "The Failed First Attempt"; DFlash-TfM summary,
+  "2. Boomconstructie").
 
 Every function is pinned by tests under ``tests/`` that check it against
 values printed on the pages, closed forms, invariants, brute force on tiny
 inputs or library routines.
 """
-from . import attn, gdn, mask, walk  # noqa: F401
+from . import attn, gdn, kvcommit, mask, treebuild, walk  # noqa: F401
