@@ -40,8 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-curve", action="store_true",
-                    help="skip the cost curve over tree sizes (its attention calls share kernel "
-                         "names with the step's, which muddles a kernel trace of the step)")
+                    help="skip the cost curve over tree sizes and the tree-construction timing "
+                         "(the curve's attention calls share kernel names with the step's, which "
+                         "muddles a kernel trace of the step)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=2)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per global-layer attention call (rocprofv3 --pmc)")
@@ -204,6 +205,41 @@ def next_rows(step: Step, dev, reps: int) -> dict:
             "gdn_commit": {"ms": round(gms, 4), "bytes": gbytes, "GBps": round(gbytes / (gms * 1e-3) / 1e9, 1),
                            "frac_of_8TBps": round(gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "kv_commit": {"ms": round(kms, 4), "bytes": kbytes}}
+
+
+def tree_construction(step: Step, dev, reps: int) -> dict:
+    """Draft-tree construction at the DDTree workload's shape, outside the
+    step: 64 sequences x 8 depths of 262144-entry bf16 draft logits (sigma 8,
+    seeded on the device), top 8 per depth, then best-first growth to 64
+    nodes (one candidate per round, and 8 per round).  Event-timed averages."""
+    tv = step.tv
+    from synth import workloads as W
+    B, L, V, K, N = 64, 8, 262144, 8, 64
+    x = W.draft_logits(4, B, L, V, torch.bfloat16, device=dev, on_device=True)
+    cand = tv.tree_draft_topk(x, K)
+    tree = tv.tree_build(cand["cand_tokens"], cand["cand_logprob"], N, 1)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / reps
+
+    tk = timed(lambda: tv.tree_draft_topk(x, K, out=cand))
+    b1 = timed(lambda: tv.tree_build(cand["cand_tokens"], cand["cand_logprob"], N, 1, out=tree))
+    b8 = timed(lambda: tv.tree_build(cand["cand_tokens"], cand["cand_logprob"], N, 8, out=tree))
+    nbytes = x.numel() * x.element_size()
+    del x
+    return {"workload": "B=64, 8 depths x 262144 bf16 draft logits, top 8, budget 64",
+            "topk_ms": round(tk, 4), "topk_GBps": round(nbytes / (tk * 1e-3) / 1e9, 1),
+            "topk_frac_of_8TBps": round(nbytes / (tk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "build_ms_w1": round(b1, 4), "build_ms_w8": round(b8, 4)}
 
 
 CURVE_NODES = (1, 2, 4, 8, 16, 32, 64, 128)
@@ -396,6 +432,7 @@ def main():
     out["next_rows"] = next_rows(step, dev, args.steps)
     if not args.no_curve:
         out["next_rows"]["cost_curve"] = cost_curve(step, dev, min(args.steps, 20))
+        out["next_rows"]["tree_construction"] = tree_construction(step, dev, min(args.steps, 20))
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

@@ -58,6 +58,8 @@ typedef void* tv_stream;
 #define TV_MAX_NODES 128     /* draft nodes per tree (mask, attention, walk, KV commit) */
 #define TV_GDN_MAX_NODES 64  /* draft nodes per tree for the Gated DeltaNet calls       */
 #define TV_BLOCK_SIZE 16     /* tokens per KV-cache page                                */
+#define TV_TREE_MAX_TOPK 16  /* candidates per depth for tree construction             */
+#define TV_TREE_MAX_DEPTH 16 /* depths of a constructed tree                           */
 /* 64-bit words of one node's ancestor set: node j is bit j % 64 of word j / 64 */
 #define TV_ANC_WORDS(N) (((N) + 63) / 64)
 
@@ -256,6 +258,63 @@ tv_status tree_kv_commit(const void* k_node, const void* v_node,
                          int32_t max_blocks_per_seq, int32_t num_blocks, int32_t B,
                          int32_t N, int32_t Hkv, int32_t D, int32_t block_size,
                          tv_dtype dtype, void* k_cache, void* v_cache, tv_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tree_draft_topk — the candidates of each depth of a factorised draft.
+ *
+ * DDTree validation post ("From Linear to Tree-Walk"), section "The Failed
+ * First Attempt": the tree starts from the top-k tokens of the first
+ * position, and every depth offers its top-k tokens with their draft
+ * log-probabilities.  For each (sequence b, depth d) row of draft logits the
+ * call returns the K largest logits' token ids (ties to the lower id) in
+ * decreasing order and their log-softmax values over the whole row.
+ *
+ *   logits        [B, L, V]   dtype, row (b, d) = draft logits of depth d + 1
+ *   cand_tokens   int32 [B, L, K]  out
+ *   cand_logprob  float [B, L, K]  out: logit - log(sum over the row of exp(logit))
+ * Logits must be finite (otherwise the result is unspecified).
+ * Supported: B >= 1, 1 <= L <= TV_TREE_MAX_DEPTH, 1 <= K <= TV_TREE_MAX_TOPK,
+ * K <= V, dtype TV_F32 or TV_BF16.
+ * ------------------------------------------------------------------------ */
+tv_status tree_draft_topk(const void* logits, int32_t B, int32_t L, int32_t V, int32_t K,
+                          tv_dtype dtype, int32_t* cand_tokens, float* cand_logprob,
+                          tv_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tree_build — best-first growth of the draft tree from per-depth candidates.
+ *
+ * DDTree validation post, section "The Failed First Attempt": a priority
+ * queue on cumulative log-probability starts with the depth-1 candidates as
+ * roots; each popped node joins the tree and its sibling and child are
+ * queued, until the budget N is spent or the maximum depth L stops growth.
+ * DFlash-TfM summary, section "2. Boomconstructie": each round takes the w
+ * best candidates at once and expands them together (ceil(N / w) rounds).
+ * Precisely: the queue starts with the K depth-1 candidates in rank order; a
+ * node's value is its parent's value plus its candidate's log-probability,
+ * one float32 addition; the queue orders by value, higher first, equal
+ * values in push order; a round pops min(w, N - nodes so far, queued)
+ * candidates in queue order, then pushes, for each popped node in pop order,
+ * its next sibling (same parent, next rank; depth >= 2 only, depth-1
+ * siblings are queued from the start) and its first child (rank 0 of the
+ * next depth, below depth L).  Output order: pop order stable-sorted by
+ * depth (the best node of each depth first), parents renumbered; parent -1 is
+ * a child of the last accepted token, depth 1 its depth (the layout contract
+ * of tree_mask_build).
+ *
+ *   cand_tokens   int32 [B, L, K], cand_logprob float [B, L, K]  (as from
+ *                 tree_draft_topk; log-probabilities in decreasing order per depth)
+ *   tokens        int32 [B, N]  out: node tokens (-1 past the tree)
+ *   parent        int32 [B, N]  out: parent node (-1 for depth 1 and past the tree)
+ *   depth         int32 [B, N]  out: 1-based depth (0 past the tree)
+ *   score         float [B, N]  optional out (NULL = skip): cumulative log-probability
+ *   num_nodes     int32 [B]     out: nodes built (N unless the K-ary tree of depth L is smaller)
+ * Supported: B >= 1, 1 <= L <= TV_TREE_MAX_DEPTH, 1 <= K <= TV_TREE_MAX_TOPK,
+ * 1 <= N <= TV_MAX_NODES, w >= 1.
+ * ------------------------------------------------------------------------ */
+tv_status tree_build(const int32_t* cand_tokens, const float* cand_logprob, int32_t B,
+                     int32_t L, int32_t K, int32_t N, int32_t w, int32_t* tokens,
+                     int32_t* parent, int32_t* depth, float* score, int32_t* num_nodes,
+                     tv_stream stream);
 
 /* Static description of a status code. */
 const char* tv_status_string(tv_status s);

@@ -26,6 +26,7 @@ BLOCK = 16  # tokens per KV page
 TAG_TREE, TAG_CTX, TAG_PERM, TAG_Q, TAG_KN, TAG_VN, TAG_KC, TAG_VC, TAG_LOGIT, TAG_PLANT = range(10)
 TAG_GQ, TAG_GK, TAG_GV, TAG_GA, TAG_GB, TAG_GS = range(20, 26)
 TAG_ACC = 30
+TAG_DRAFT, TAG_CAND = 40, 41
 
 
 @dataclasses.dataclass
@@ -278,3 +279,34 @@ def accepted_paths(config: int, parent: np.ndarray, *, tag: int = TAG_ACC, p_non
         acc[b, :len(path)] = path
         na[b] = len(path)
     return acc, na
+
+
+# ---------------------------------------------------------------- draft distributions
+
+def draft_logits(config: int, B: int, L: int, V: int, dtype: torch.dtype, *, sigma: float = 8.0,
+                 device="cpu", on_device: bool = False) -> torch.Tensor:
+    """Draft logits [B, L, V] of a factorised drafter: sigma * N(0, 1) per
+    entry (the DDTree workload's recipe).  On the device the bulk comes from a
+    seeded torch generator; otherwise from the per-sequence NumPy streams."""
+    if on_device:
+        out = _device_normal(config * 1000 + TAG_DRAFT, (B, L, V), torch.float32, device)
+        return (out * sigma).to(dtype)
+    xs = [_normal(config, TAG_DRAFT, b, (L, V), torch.float32, std=sigma) for b in range(B)]
+    return torch.stack(xs).to(dtype).to(device)
+
+
+def draft_candidates(config: int, B: int, L: int, K: int, *, ties: bool = False, scale: float = 1.5):
+    """Per-depth candidates as a top-k step hands them over: distinct token ids
+    [B, L, K] (int32) and log-probabilities [B, L, K] (float32, decreasing per
+    depth, all negative).  With ties the values are multiples of 1/4, so that
+    equal cumulative values occur."""
+    tok = np.empty((B, L, K), dtype=np.int32)
+    lp = np.empty((B, L, K), dtype=np.float32)
+    for b in range(B):
+        r = T.rng_for(config, TAG_CAND, b)
+        tok[b] = r.permutation(100000)[:L * K].reshape(L, K)
+        v = -np.sort(r.exponential(scale, size=(L, K)), axis=1)
+        if ties:
+            v = -np.ceil(-v * 4) / 4
+        lp[b] = v.astype(np.float32)
+    return tok, lp

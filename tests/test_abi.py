@@ -174,3 +174,27 @@ def test_kv_commit_validation(lib):
     assert call(a12=32) == tv.TV_ERR_UNSUPPORTED     # block size
     assert call(a9=129) == tv.TV_ERR_UNSUPPORTED
     assert call(a0=ctypes.c_void_p(0x1008)) == tv.TV_ERR_UNSUPPORTED   # not 16-byte aligned
+
+
+def test_tree_construction_validation(lib):
+    f = lib.tree_draft_topk
+    assert f(None, 2, 8, 1000, 8, tv.TV_BF16, FAKE, FAKE, None) == tv.TV_ERR_NULL
+    assert f(FAKE, 0, 8, 1000, 8, tv.TV_BF16, FAKE, FAKE, None) == tv.TV_ERR_SHAPE
+    assert f(FAKE, 2, 17, 1000, 8, tv.TV_BF16, FAKE, FAKE, None) == tv.TV_ERR_UNSUPPORTED   # depth
+    assert f(FAKE, 2, 8, 1000, 17, tv.TV_BF16, FAKE, FAKE, None) == tv.TV_ERR_UNSUPPORTED   # top-k
+    assert f(FAKE, 2, 8, 4, 8, tv.TV_BF16, FAKE, FAKE, None) == tv.TV_ERR_UNSUPPORTED       # K > V
+    assert f(FAKE, 2, 8, 1000, 8, 9, FAKE, FAKE, None) == tv.TV_ERR_UNSUPPORTED             # dtype
+    g = lib.tree_build
+    args = [FAKE, FAKE, 4, 8, 8, 64, 1, FAKE, FAKE, FAKE, None, FAKE, None]
+    bad = list(args); bad[0] = None
+    assert g(*bad) == tv.TV_ERR_NULL
+    bad = list(args); bad[11] = None
+    assert g(*bad) == tv.TV_ERR_NULL                  # num_nodes
+    bad = list(args); bad[6] = 0
+    assert g(*bad) == tv.TV_ERR_SHAPE                 # w
+    bad = list(args); bad[5] = 129
+    assert g(*bad) == tv.TV_ERR_UNSUPPORTED           # N
+    bad = list(args); bad[4] = 17
+    assert g(*bad) == tv.TV_ERR_UNSUPPORTED           # K
+    bad = list(args); bad[3] = 17
+    assert g(*bad) == tv.TV_ERR_UNSUPPORTED           # L

@@ -33,7 +33,7 @@ BLOCK_SIZE = 16
 EXPORTS = (
     "tree_mask_build", "tree_verify_attn_workspace_size", "tree_verify_attn",
     "tree_gdn_verify", "tree_walk_accept_workspace_size", "tree_walk_accept",
-    "tree_gdn_commit", "tree_kv_commit", "tv_status_string",
+    "tree_gdn_commit", "tree_kv_commit", "tree_draft_topk", "tree_build", "tv_status_string",
 )
 
 _lib = None
@@ -71,6 +71,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tree_gdn_commit.restype = S
     lib.tree_kv_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, S, P, P, P]
     lib.tree_kv_commit.restype = S
+    lib.tree_draft_topk.argtypes = [P, I, I, I, I, S, P, P, P]
+    lib.tree_draft_topk.restype = S
+    lib.tree_build.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P]
+    lib.tree_build.restype = S
     lib.tv_status_string.argtypes = [S]
     lib.tv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -298,3 +302,49 @@ def tree_kv_commit(k_node, v_node, accepted_nodes, num_accepted, ctx_len, block_
                               D, BLOCK_SIZE, _dtype_code(dt), _ptr(k_cache), _ptr(v_cache),
                               _stream(dev))
     _check("tree_kv_commit", code)
+
+
+# ---------------------------------------------------------------- tree construction
+
+TREE_MAX_TOPK = 16
+TREE_MAX_DEPTH = 16
+
+
+def tree_draft_topk(logits: torch.Tensor, K: int, out: Optional[dict] = None) -> dict:
+    """Per (sequence, depth) the K largest draft logits' tokens (ties to the
+    lower id) and their log-softmax values: logits [B, L, V] bf16 or fp32 ->
+    cand_tokens int32 [B, L, K], cand_logprob float32 [B, L, K]."""
+    lib = load()
+    dev = logits.device
+    B, L, V = logits.shape
+    _need(logits, "logits", logits.dtype, dev, (B, L, V))
+    if out is None:
+        out = dict(cand_tokens=torch.empty(B, L, K, dtype=torch.int32, device=dev),
+                   cand_logprob=torch.empty(B, L, K, dtype=torch.float32, device=dev))
+    code = lib.tree_draft_topk(_ptr(logits), B, L, V, int(K), _dtype_code(logits.dtype),
+                               _ptr(out["cand_tokens"]), _ptr(out["cand_logprob"]), _stream(dev))
+    _check("tree_draft_topk", code)
+    return out
+
+
+def tree_build(cand_tokens: torch.Tensor, cand_logprob: torch.Tensor, N: int, w: int = 1,
+               out: Optional[dict] = None, with_score: bool = True) -> dict:
+    """Best-first growth of the draft tree (budget N, w candidates per round):
+    tokens, parent, depth int32 [B, N], score float32 [B, N] (optional),
+    num_nodes int32 [B], in the layout tree_mask_build takes."""
+    lib = load()
+    dev = cand_tokens.device
+    B, L, K = cand_tokens.shape
+    _need(cand_tokens, "cand_tokens", torch.int32, dev, (B, L, K))
+    _need(cand_logprob, "cand_logprob", torch.float32, dev, (B, L, K))
+    if out is None:
+        out = dict(tokens=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   parent=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   depth=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   score=torch.empty(B, N, dtype=torch.float32, device=dev) if with_score else None,
+                   num_nodes=torch.empty(B, dtype=torch.int32, device=dev))
+    code = lib.tree_build(_ptr(cand_tokens), _ptr(cand_logprob), B, L, K, int(N), int(w),
+                          _ptr(out["tokens"]), _ptr(out["parent"]), _ptr(out["depth"]),
+                          _ptr(out.get("score")), _ptr(out["num_nodes"]), _stream(dev))
+    _check("tree_build", code)
+    return out

@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtreeverify.so")
-SOURCES = ["tv_api.hip", "tv_mask.hip", "tv_walk.hip", "tv_attn.hip", "tv_gdn.hip", "tv_commit.hip"]
+SOURCES = ["tv_api.hip", "tv_mask.hip", "tv_walk.hip", "tv_attn.hip", "tv_gdn.hip", "tv_commit.hip",
+           "tv_tree.hip"]
 ARCH = os.environ.get("TV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -135,6 +135,29 @@ tv_status tree_kv_commit(const void* k_node, const void* v_node, const int32_t* 
                                        dtype, k_cache, v_cache, as_stream(stream)));
 }
 
+tv_status tree_draft_topk(const void* logits, int32_t B, int32_t L, int32_t V, int32_t K,
+                          tv_dtype dtype, int32_t* cand_tokens, float* cand_logprob,
+                          tv_stream stream) {
+  if (!logits || !cand_tokens || !cand_logprob) return TV_ERR_NULL;
+  if (B < 1 || L < 1 || V < 1 || K < 1) return TV_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return TV_ERR_UNSUPPORTED;
+  if (L > TV_TREE_MAX_DEPTH || K > TV_TREE_MAX_TOPK || K > V) return TV_ERR_UNSUPPORTED;
+  if (static_cast<long long>(B) * L > 0x7fffffffLL) return TV_ERR_UNSUPPORTED;
+  return launched(tv::launch_draft_topk(logits, B, L, V, K, dtype, cand_tokens, cand_logprob,
+                                        as_stream(stream)));
+}
+
+tv_status tree_build(const int32_t* cand_tokens, const float* cand_logprob, int32_t B, int32_t L,
+                     int32_t K, int32_t N, int32_t w, int32_t* tokens, int32_t* parent,
+                     int32_t* depth, float* score, int32_t* num_nodes, tv_stream stream) {
+  if (!cand_tokens || !cand_logprob || !tokens || !parent || !depth || !num_nodes)
+    return TV_ERR_NULL;
+  if (B < 1 || L < 1 || K < 1 || N < 1 || w < 1) return TV_ERR_SHAPE;
+  if (L > TV_TREE_MAX_DEPTH || K > TV_TREE_MAX_TOPK || N > TV_MAX_NODES) return TV_ERR_UNSUPPORTED;
+  return launched(tv::launch_tree_build(cand_tokens, cand_logprob, B, L, K, N, w, tokens, parent,
+                                        depth, score, num_nodes, as_stream(stream)));
+}
+
 size_t tree_walk_accept_workspace_size(int32_t B, int32_t N) {
   if (B < 1 || N < 1) return 0;
   return static_cast<size_t>(B) * (N + 1) * sizeof(int32_t);

@@ -47,6 +47,13 @@ hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void*
                        int N, int V, tv_dtype dtype, int32_t* acc_tok, int32_t* acc_node,
                        int32_t* num_acc, int32_t* argmax_ws, hipStream_t stream);
 
+hipError_t launch_draft_topk(const void* logits, int B, int L, int V, int K, tv_dtype dtype,
+                             int32_t* cand_tok, float* cand_lp, hipStream_t stream);
+
+hipError_t launch_tree_build(const int32_t* cand_tok, const float* cand_lp, int B, int L, int K,
+                             int N, int w, int32_t* tokens, int32_t* parent, int32_t* depth,
+                             float* score, int32_t* num_nodes, hipStream_t stream);
+
 struct AttnPlan {
   int G;            // query heads per kv head
   int rows;         // G * N query rows per (sequence, kv head)
