@@ -985,6 +985,40 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     asm volatile("" ::: "memory");
   };
 
+  // The same loads, prepared (page lookups and addresses) right after the
+  // barrier and issued one by one between the products of P.V, so that no
+  // issue stalls on a full memory pipeline: load q of the prepared set is
+  // value load q (q < kIPW), then key load q - kIPW.
+  const unsigned char* pre_src[2 * kIPW];
+  bool pre_on[2];  // per half: the stage lies inside the stream
+  int pre_dst[2];  // LDS byte offset of the half's slot (+ the wave's blocks)
+  auto prepare = [&](int sv, int sk) __attribute__((always_inline)) {
+    const int st[2] = {sv, sk};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bool is_node = st[q] >= nctx;
+      const int base = is_node ? (st[q] - nctx) * kSK : k0 + st[q] * kSK;
+      const int lim = is_node ? N : k1;
+      const unsigned char* src = is_node ? (q == 0 ? vnb : knb) : (q == 0 ? vcb : kcb);
+      pre_on[q] = st[q] < ntiles;
+      pre_dst[q] = (st[q] % kSlots) * kSB;
+#pragma unroll
+      for (int j = 0; j < kIPW; ++j) {
+        const int key = min(base + ld_row[j], lim - 1);
+        const int page = s_pages[min(max((key >> 4) - p0, 0), kSplitPages - 1)];
+        const size_t off = is_node ? ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes
+                                   : ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes;
+        pre_src[q * kIPW + j] = src + off + ld_part[j] * 16;
+      }
+    }
+  };
+  auto issue_prepared = [&](int q) __attribute__((always_inline)) {
+    const int half = q / kIPW, j = q % kIPW;
+    if (!pre_on[half]) return;
+    unsigned char* dst = (half == 0 ? vring : kring) + pre_dst[half] + (lwave * kIPW + j) * 1024;
+    lds_dma16(pre_src[q], dst);
+  };
+
   f32x4_t S[kRT][2 * kKT];               // scores of a stage, from its products to its softmax
   bf16x8_t ph[kRT][kKT], pl[kRT][kKT];  // its probabilities, from the softmax to P.V
 
@@ -1130,12 +1164,14 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
 
   // O^T += V^T P^T for stage `it`, one 32-key tile at a time: the value
   // fragments of a column tile feed all row tiles; reads run two steps ahead
-  auto pv_product = [&](int it) __attribute__((always_inline)) {
+  auto pv_product = [&](int it, bool with_loads) __attribute__((always_inline)) {
     const unsigned char* Vs = vring + (it % kSlots) * kSB;
     const int vrow = 4 * lg + (lr >> 2);
     const int vcol = 8 * (lr & 3);
     constexpr int kSteps = C::kDT * kKT;  // (column tile, key tile) pairs
     constexpr int kVA = 2;
+    constexpr int kEvery = kSteps / (2 * kIPW);  // steps per prepared load
+    static_assert(kEvery >= 1 && kEvery * 2 * kIPW == kSteps, "prepared loads spread over the steps");
     s16x4_t vlo[kVA + 1], vhi[kVA + 1];
     auto vread = [&](int st, s16x4_t& lo, s16x4_t& hi) __attribute__((always_inline)) {
       const int dt = st / kKT, kt = st % kKT;
@@ -1159,8 +1195,10 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt][kt], acc[rt][dt], 0, 0, 0);
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt][kt], acc[rt][dt], 0, 0, 0);
       }
+      if (with_loads && st % kEvery == kEvery - 1) issue_prepared(st / kEvery);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (with_loads) asm volatile("" ::: "memory");
   };
 
   if (ntiles > 0) {
@@ -1186,14 +1224,17 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
         wait_vmem<0>();  // V(ntiles - 1), the last load
       }
       lds_barrier();
-      if (it >= 1 && it - 2 + kSlots < ntiles) refill(it - 2 + kSlots, it - 1 + kSlots);
     };
     // one loop per group, so that only the probabilities (group 0) or only the
     // scores (group 1) stay live from one iteration to the next
     if (grp == 0) {
       for (int it = 0; it <= ntiles; ++it) {
         sync(it);
-        if (it >= 1) pv_product(it - 1);
+        // the refills of this iteration (the slots of K(it - 1) and V(it - 2)
+        // are free past the barrier) go out during P.V
+        const bool loads = it >= 1 && it - 2 + kSlots < ntiles;
+        if (loads) prepare(it - 2 + kSlots, it - 1 + kSlots);
+        if (it >= 1) pv_product(it - 1, loads);
         if (it < ntiles) {
           scores(it);
           softmax(it);
@@ -1204,7 +1245,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
         sync(it);
         if (it >= 1) {
           softmax(it - 1);
-          pv_product(it - 1);
+          pv_product(it - 1, false);
         }
         if (it < ntiles) scores(it);
       }
