@@ -20,7 +20,7 @@ namespace tv {
 
 namespace {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 512;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKMax = TV_TREE_MAX_TOPK;  // per-thread candidate list length
 
@@ -52,7 +52,7 @@ __device__ __forceinline__ float elem(const T* p, size_t i) {
 }
 
 // Row r = (sequence, depth) of V logits: K candidates and their log-softmax
-// values.  Each thread scans 16-byte chunks c = tid, tid + 256, ... keeping a
+// values.  Each thread scans 16-byte chunks c = tid, tid + 512, ... keeping a
 // running (max, sum of exp2).  Each wave keeps one sorted list of its K best
 // (lane k < K holds entry k): an element is a candidate only if it beats the
 // list's last entry, which the whole wave knows, so after the first few
@@ -194,22 +194,33 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_kernel(const T* __res
   for (int w = 0; w < kTopkThreads / 64; ++w)
     gs += s_m[w] == -INFINITY ? 0.0f : s_s[w] * __builtin_amdgcn_exp2f((s_m[w] - gm) * kLog2e);
   const float lse = gm + __builtin_amdgcn_logf(gs) * 0.6931471805599453f;
-  // merge the four waves' lists: lane j holds entry j % K of wave j / K
-  const int nw = kTopkThreads / 64;
-  float hv = -INFINITY;
-  int hi = 0x7fffffff;
-  if (lane < nw * K) {
-    hv = s_lv[lane / K][lane % K];
-    hi = s_li[lane / K][lane % K];
+  // merge the waves' lists: lane j holds entries j and j + 64 of the
+  // concatenated lists (entry e = entry e % K of wave e / K), offering the
+  // better of the two it still has
+  constexpr int nw = kTopkThreads / 64;
+  static_assert(nw * kKMax <= 128, "two merge entries per lane");
+  float ev[2];
+  int ei[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = lane + 64 * q;
+    ev[q] = e < nw * K ? s_lv[e / K][e % K] : -INFINITY;
+    ei[q] = e < nw * K ? s_li[e / K][e % K] : 0x7fffffff;
   }
   for (int k = 0; k < K; ++k) {
-    float v = hv;
-    int i = hi;
+    const bool second = cand_before(ev[1], ei[1], ev[0], ei[0]);
+    float v = second ? ev[1] : ev[0];
+    int i = second ? ei[1] : ei[0];
     int owner;
     wave_best(v, i, owner);
     if (lane == owner) {
-      hv = -INFINITY;
-      hi = 0x7fffffff;
+      if (second) {
+        ev[1] = -INFINITY;
+        ei[1] = 0x7fffffff;
+      } else {
+        ev[0] = -INFINITY;
+        ei[0] = 0x7fffffff;
+      }
     }
     if (lane == 0) {
       cand_tok[row * K + k] = i;
