@@ -298,6 +298,13 @@ __device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
 
 constexpr int kUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
 
+// bytes of one bf16 half of S0, later [Q; K] S0 (fp32, 2NP rows of 128)
+__host__ __device__ inline size_t gdn_r1_bytes(int np) {
+  const size_t half = static_cast<size_t>(kDk) * kRowB;
+  const size_t qks = 2 * static_cast<size_t>(np) * kDk * 4;
+  return half > qks ? half : qks;
+}
+
 // bytes of the [Q; K] rows, later X and Y (row pitch NP + 4)
 __host__ __device__ inline size_t gdn_r2_bytes(int np) {
   const size_t qk = 2 * static_cast<size_t>(np) * kRowB;
@@ -307,10 +314,11 @@ __host__ __device__ inline size_t gdn_r2_bytes(int np) {
 
 size_t gdn_mfma_lds_bytes(int N) {
   const int np = (N + 15) / 16 * 16;
-  // S0 hi + lo (bf16), later [Q; K] S0 (fp32); [Q; K] (bf16), later X and Y
-  // (fp32); V, later the right-hand side (fp32); alpha, beta, gamma, log2
-  // gamma, depth, ancestor words
-  return 2 * 128 * kRowB + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 + 64 * 4 * 5 + 64 * 8;
+  // S0 hi, then S0 lo (bf16), later [Q; K] S0 (fp32); [Q; K] (bf16), later X
+  // and Y (fp32); V, later the right-hand side (fp32); alpha, beta, gamma,
+  // log2 gamma, depth, ancestor words.  Up to 32 nodes this is 68 KB, so two
+  // workgroups share a CU.
+  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 + 64 * 4 * 5 + 64 * 8;
 }
 
 // C = A B (+ D), NP x NP fp32 matrices of row pitch mp in LDS, on
@@ -341,15 +349,15 @@ __device__ __forceinline__ void gdn_mm(const float* A, const float* B, const flo
 }
 
 template <typename TO>
-__global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int NP = (N + 15) / 16 * 16;
-  unsigned char* r1 = smem;                      // S0 hi | S0 lo, then [Q; K] S0 fp32 [2NP][128]
+  unsigned char* r1 = smem;                      // S0 hi, S0 lo, then [Q; K] S0 fp32 [2NP][128]
   const int MP = NP + 4;                         // row pitch of the NP x NP matrices (floats)
-  unsigned char* r2 = smem + 2 * 128 * kRowB;    // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][MP]
+  unsigned char* r2 = smem + gdn_r1_bytes(NP);   // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][MP]
   float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V, then the right-hand side
   float* s_alpha = s_u + NP * kUP;
   float* s_beta = s_alpha + 64;
@@ -405,6 +413,8 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
     gb = beta[nh];
     gw = anc[static_cast<size_t>(b) * N + tid];
   }
+  // the low halves wait, packed, in registers until the high half has been used
+  uint2 s0lo[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int e = tid + u * kMThreads;
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
                           static_cast<__bf16>(f[u].z - static_cast<float>(hv[2])),
                           static_cast<__bf16>(f[u].w - static_cast<float>(hv[3]))};
     *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, hv);
-    *reinterpret_cast<uint2*>(r1 + 128 * kRowB + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, lv);
+    s0lo[u] = __builtin_bit_cast(uint2, lv);
   }
 #pragma unroll
   for (int u = 0; u < kQKPer; ++u) {
@@ -470,37 +480,37 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
     if (t < N) atomicMax(&s_maxdepth, dpt);
   }
 
-  // ---- phase 1: [Q; K] S0 (transposed) and the Gram products on MFMA
+  // ---- phase 1: [Q; K] S0 (transposed) and the Gram products on MFMA.
+  // The half of S0 in LDS times the [Q; K] rows, added into qks.
   const int nqks = NP;          // 8 column tiles x 2NP / 16 node tiles
   const int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
   mf32x4_t qks[8], gram[4];
+  auto s0_product = [&]() {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int u = wave + 8 * m;
-    qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (u < nqks) {
-      const int ct = u & 7, nt = u >> 3;
-      const int row = 16 * nt + lr;
+    for (int m = 0; m < 8; ++m) {
+      const int u = wave + 8 * m;
+      if (u < nqks) {
+        const int ct = u & 7, nt = u >> 3;
+        const int row = 16 * nt + lr;
 #pragma unroll
-      for (int ks = 0; ks < kDk / 32; ++ks) {
-        const int vrow = 32 * ks + 4 * lg + (lr >> 2);
-        const int vcol = ct * 32 + 8 * (lr & 3);
-        const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
-        const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
-        const ms16x4_t l0 = tr_read(r1 + 128 * kRowB + gswz(vrow, vcol));
-        const ms16x4_t l1 = tr_read(r1 + 128 * kRowB + gswz(vrow + 16, vcol));
-        const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
-        const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
-        const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-        const ms16x8_t al = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-        const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
-        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
-                                                          qks[m], 0, 0, 0);
-        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, al), bb,
-                                                          qks[m], 0, 0, 0);
+        for (int ks = 0; ks < kDk / 32; ++ks) {
+          const int vrow = 32 * ks + 4 * lg + (lr >> 2);
+          const int vcol = ct * 32 + 8 * (lr & 3);
+          const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
+          const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
+          const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
+          const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
+          const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
+          qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
+                                                            qks[m], 0, 0, 0);
+        }
       }
     }
-  }
+  };
+#pragma unroll
+  for (int m = 0; m < 8; ++m) qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+  s0_product();  // high half
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int u = wave + 8 * m;
@@ -517,6 +527,15 @@ __global__ __launch_bounds__(kMThreads) void gdn_mfma_kernel(
       }
     }
   }
+  __syncthreads();  // every read of S0's high half is done
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * kMThreads;
+    const int d = e >> 5, c = (e & 31) * 4;
+    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = s0lo[u];
+  }
+  __syncthreads();
+  s0_product();  // low half
   __syncthreads();  // every read of S0 and of the q / k rows is done
 
   // results into LDS: [Q; K] S0 rows, and X, Y with their masks and gates
