@@ -1350,8 +1350,7 @@ __device__ __forceinline__ ShareSizes share_sizes(int nwg, int total, int pm, in
 }
 
 // share of workgroup w: tiles [x, y) of `total`
-__device__ __forceinline__ int2 stream_share(int w, int nwg, int total, int pm, int xm) {
-  const ShareSizes z = share_sizes(nwg, total, pm, xm);
+__device__ __forceinline__ int2 share_at(const ShareSizes& z, int w, int total) {
   int r0, len;
   if (!z.weighted) {
     r0 = w * z.eq;
@@ -1369,8 +1368,7 @@ __device__ __forceinline__ int2 stream_share(int w, int nwg, int total, int pm, 
 }
 
 // workgroup whose share holds tile x (0 <= x < total)
-__device__ __forceinline__ int stream_owner(int x, int nwg, int total, int pm, int xm) {
-  const ShareSizes z = share_sizes(nwg, total, pm, xm);
+__device__ __forceinline__ int owner_of(const ShareSizes& z, int x) {
   if (!z.weighted) return x / z.eq;
   const int first = (z.H >> 1) * (z.fe + z.fo);  // tiles of the first workgroups of the pairs
   if (x < first) {
@@ -1411,7 +1409,7 @@ __global__ __launch_bounds__(kThreads, (stream_min_wg<T, D>())) void attn_stream
   const int tb_all = s_pref[B];  // tiles of one kv head over all sequences
   const int total = tb_all * Hkv;
   const int w = blockIdx.x;
-  const int2 share = stream_share(w, gridDim.x, total, pm, xm);
+  const int2 share = share_at(share_sizes(gridDim.x, total, pm, xm), w, total);
   int cur = share.x;
   const int r1 = share.y;
 
@@ -1484,8 +1482,9 @@ __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
   const int total = tb_all * Hkv;
   const int tiles_b = s_pref[b + 1] - s_pref[b];
   const int us = g * tb_all + s_pref[b];
-  const int w_lo = stream_owner(us, nwg, total, pm, xm);
-  const int w_hi = stream_owner(us + tiles_b - 1, nwg, total, pm, xm);
+  const ShareSizes z = share_sizes(nwg, total, pm, xm);
+  const int w_lo = owner_of(z, us);
+  const int w_hi = owner_of(z, us + tiles_b - 1);
   if (w_lo == w_hi) return;
   const int R = chunk * kMergeRows + threadIdx.x / 16;
   if (R >= rows) return;
@@ -1494,28 +1493,41 @@ __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
   float4 o[kV];
 #pragma unroll
   for (int k = 0; k < kV; ++k) o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 2
-  for (int w = w_lo; w <= w_hi; ++w) {
-    const int2 sh = stream_share(w, nwg, total, pm, xm);
-    if (sh.x == sh.y) continue;  // an empty share left no partial
-    const size_t ub = (static_cast<size_t>(w) + j) * rows + R;
-    const float2 ml = ws_ml[ub];
-    float4 a[kV];
+  // partials four at a time: every load of a group is issued before any is used
+  constexpr int kP = 4;
+  for (int w0 = w_lo; w0 <= w_hi; w0 += kP) {
+    float2 ml[kP];
+    float4 a[kP][kV];
 #pragma unroll
-    for (int k = 0; k < kV; ++k) a[k] = *reinterpret_cast<const float4*>(ws_acc + ub * D + c0 + 64 * k);
-    if (ml.x == -INFINITY) continue;  // this segment saw no key of the row
-    const float m_new = fmaxf(mx, ml.x);
-    const float c_old = fast_exp2(mx - m_new);
-    const float c_new = fast_exp2(ml.x - m_new);
-    L = L * c_old + ml.y * c_new;
+    for (int p = 0; p < kP; ++p) {
+      const int w = w0 + p;
+      ml[p] = make_float2(-INFINITY, 0.f);
+      if (w <= w_hi) {
+        const int2 sh = share_at(z, w, total);
+        if (sh.x < sh.y) {  // an empty share left no partial
+          const size_t ub = (static_cast<size_t>(w) + j) * rows + R;
+          ml[p] = ws_ml[ub];
 #pragma unroll
-    for (int k = 0; k < kV; ++k) {
-      o[k].x = o[k].x * c_old + a[k].x * c_new;
-      o[k].y = o[k].y * c_old + a[k].y * c_new;
-      o[k].z = o[k].z * c_old + a[k].z * c_new;
-      o[k].w = o[k].w * c_old + a[k].w * c_new;
+          for (int k = 0; k < kV; ++k) a[p][k] = *reinterpret_cast<const float4*>(ws_acc + ub * D + c0 + 64 * k);
+        }
+      }
     }
-    mx = m_new;
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      if (ml[p].x == -INFINITY) continue;  // no partial, or it saw no key of the row
+      const float m_new = fmaxf(mx, ml[p].x);
+      const float c_old = fast_exp2(mx - m_new);
+      const float c_new = fast_exp2(ml[p].x - m_new);
+      L = L * c_old + ml[p].y * c_new;
+#pragma unroll
+      for (int k = 0; k < kV; ++k) {
+        o[k].x = o[k].x * c_old + a[p][k].x * c_new;
+        o[k].y = o[k].y * c_old + a[p][k].y * c_new;
+        o[k].z = o[k].z * c_old + a[p][k].z * c_new;
+        o[k].w = o[k].w * c_old + a[p][k].w * c_new;
+      }
+      mx = m_new;
+    }
   }
   const float inv = 1.0f / L;
   const int t = R / G, hl = R % G;
