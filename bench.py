@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--cpu-sample-seqs", type=int, default=2)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per global-layer attention call (rocprofv3 --pmc)")
+    ap.add_argument("--attn-only", type=int, default=0, choices=[0, 2, 4],
+                    help="instead of the verify step, time tree_verify_attn alone on the full-size "
+                         "shapes of this attention workload (2: batch 8 leaf-sibling trees, "
+                         "4: DDTree-shaped batch 64) and print one JSON line for that kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -354,6 +358,44 @@ def cpu_baseline(step: Step, nseq: int):
                        f"{dt:.1f} s on {len(os.sched_getaffinity(0))} host cores")
 
 
+def attn_only(args, dev) -> dict:
+    """tree_verify_attn alone on one full-size attention workload, inputs
+    resident in HBM: K warm calls timed with events on the current stream."""
+    import tree_verify_attention_amd as tv
+    from synth import configs as CF
+    from synth import workloads as W
+    c = CF.reduced(args.attn_only)
+    c.pop("windows")
+    c.pop("vocab")
+    x = W.attn_inputs(args.attn_only, device=dev, kv_on_device=True, **c)
+    m = tv.tree_mask_build(torch.from_numpy(x.trees.parent).to(dev), x.ctx_len)
+    out = torch.empty_like(x.q)
+    n = tv.tree_verify_attn_workspace_size(x.B, x.N, x.Hq, x.Hkv, x.D, x.max_ctx_len, 0)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    call = lambda: tv.tree_verify_attn(x.q, x.k_node, x.v_node, x.k_cache, x.v_cache, x.block_table,
+                                       x.ctx_len, x.max_ctx_len, m["anc"], m["pos"], 0, x.scale,
+                                       out=out, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        call()
+    z.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(z) / args.steps
+    ctx = x.ctx_len.cpu().numpy().astype(np.int64)
+    kv = int(ctx.sum()) * 2 * x.Hkv * x.D * x.k_cache.element_size()
+    # QK^T and P.V over the context keys: 2 products x 2 flops per multiply-add
+    flops = 4.0 * float(ctx.sum()) * x.Hq * x.N * x.D
+    return {"attn_only_config": args.attn_only, "B": x.B, "N": x.N, "Hq": x.Hq, "Hkv": x.Hkv, "D": x.D,
+            "sum_ctx": int(ctx.sum()), "steps": args.steps, "warmup": args.warmup, "ms_per_call": round(ms, 4),
+            "kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1), "kv_frac_of_8TBps": round(kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_bf16_mfma_2500TFLOPs": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -364,6 +406,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.attn_only:
+        print(json.dumps(attn_only(args, dev)), flush=True)
+        return
     step = Step(dev)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
