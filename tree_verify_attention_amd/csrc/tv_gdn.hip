@@ -348,8 +348,10 @@ __device__ __forceinline__ void gdn_mm(const float* A, const float* B, const flo
   }
 }
 
-template <typename TO>
-__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) void gdn_mfma_kernel(
+// kM: node tiles of 16 rows in [Q; K] (2 NP / 16, NP <= 16 kM / 2).  Up to
+// 32 nodes (kM = 4) the kernel fits two workgroups per CU, registers included.
+template <typename TO, int kM>
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <= 4 ? 4 : 2))) void gdn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
@@ -484,23 +486,23 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   // The half of S0 in LDS times the [Q; K] rows, added into qks.
   const int nqks = NP;          // 8 column tiles x 2NP / 16 node tiles
   const int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
-  mf32x4_t qks[8], gram[4];
+  mf32x4_t qks[kM], gram[kM / 2];
+  // Tile u = wave + 8 m is column tile `wave` of node tile m: a wave keeps one
+  // column tile, so each k-step reads its S0 fragment once for all node tiles.
   auto s0_product = [&]() {
+    const int vcol = wave * 32 + 8 * (lr & 3);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int u = wave + 8 * m;
-      if (u < nqks) {
-        const int ct = u & 7, nt = u >> 3;
-        const int row = 16 * nt + lr;
+    for (int ks = 0; ks < kDk / 32; ++ks) {
+      const int vrow = 32 * ks + 4 * lg + (lr >> 2);
+      const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
+      const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
+      const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
 #pragma unroll
-        for (int ks = 0; ks < kDk / 32; ++ks) {
-          const int vrow = 32 * ks + 4 * lg + (lr >> 2);
-          const int vcol = ct * 32 + 8 * (lr & 3);
-          const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
-          const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
+      for (int m = 0; m < kM; ++m) {
+        if (wave + 8 * m < nqks) {
+          const int row = 16 * m + lr;
           const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
           const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
-          const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
           const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
           qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
                                                             qks[m], 0, 0, 0);
@@ -509,10 +511,10 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     }
   };
 #pragma unroll
-  for (int m = 0; m < 8; ++m) qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < kM; ++m) qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
   s0_product();  // high half
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kM / 2; ++m) {
     const int u = wave + 8 * m;
     gram[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
     if (u < ngram) {
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   float* s_x = reinterpret_cast<float*>(r2);     // [NP][MP]
   float* s_y = s_x + NP * MP;                    // [NP][MP]
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int u = wave + 8 * m;
     if (u < nqks) {
       const int ct = u & 7, nt = u >> 3;
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
     }
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kM / 2; ++m) {
     const int u = wave + 8 * m;
     if (u < ngram) {
       const int kt = u % (NP / 16), rt = u / (NP / 16);
@@ -656,19 +658,27 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 }
 
-template <typename TO>
-hipError_t launch_gdn_mfma(const void* q, const void* k, const void* v, const float* alpha,
-                           const float* beta, const float* S0, const uint64_t* anc, int B, int N,
-                           int H, void* out, hipStream_t stream) {
+template <typename TO, int kM>
+hipError_t launch_gdn_mfma_m(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                             int H, void* out, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gdn_mfma_kernel<TO>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gdn_mfma_lds_bytes(64)));
+      reinterpret_cast<const void*>(&gdn_mfma_kernel<TO, kM>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gdn_mfma_lds_bytes(8 * kM)));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gdn_mfma_kernel<TO>), dim3(static_cast<unsigned>(B) * H), dim3(kMThreads),
+  hipLaunchKernelGGL((gdn_mfma_kernel<TO, kM>), dim3(static_cast<unsigned>(B) * H), dim3(kMThreads),
                      gdn_mfma_lds_bytes(N), stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta, S0,
                      anc, N, H, static_cast<TO*>(out));
   return hipGetLastError();
+}
+
+template <typename TO>
+hipError_t launch_gdn_mfma(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                           int H, void* out, hipStream_t stream) {
+  if (N <= 32) return launch_gdn_mfma_m<TO, 4>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+  return launch_gdn_mfma_m<TO, 8>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
 }
 
 template <typename T, typename TO>
