@@ -25,6 +25,8 @@
 // masked by the ancestor word of each row's node.  A split writes fp32
 // partials (acc, m, l); a second kernel merges them by log-sum-exp.  A
 // sequence whose keys fit one split writes its output directly.
+#include <atomic>
+
 #include "tv_internal.h"
 
 #ifndef TV_ATTN_LDS_BUDGET
@@ -1701,22 +1703,18 @@ static_assert(TV_ATTN_XCD_PM >= 500 && TV_ATTN_XCD_PM <= 1500, "XCD weight");
 #define TV_ATTN_STREAM_MIN_TILES 16  // key tiles per stream workgroup at least
 #endif
 
-namespace {
-// compute units of the current device (256 on an MI355X; that value also
-// when no device can be queried, e.g. for a size query on a host without one)
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // zero-initialised (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
-}  // namespace
 
 AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int window) {
   AttnPlan p{};

@@ -324,20 +324,22 @@ size_t gdn_mfma_lds_bytes(int N) {
 // C = A B (+ D), NP x NP fp32 matrices of row pitch mp in LDS, on
 // v_mfma_f32_16x16x4f32; B's entries are scaled by `sb`.  Tiles are dealt to
 // the 8 waves; a lane holds column lr of rows 4 lg .. 4 lg + 3 of its tile.
-template <bool kAdd>
+// kNT = NP / 16 tiles per side.
+template <bool kAdd, int kNT>
 __device__ __forceinline__ void gdn_mm(const float* A, const float* B, const float* Dm, float* C, int mp,
-                                       int nt, int wave, int lr, int lg, float sb) {
+                                       int wave, int lr, int lg, float sb) {
 #pragma unroll
   for (int mm = 0; mm < 2; ++mm) {
     const int u = wave + 8 * mm;
-    if (u < nt * nt) {
-      const int rt = u / nt, ct = u % nt;
+    if (u < kNT * kNT) {
+      const int rt = u / kNT, ct = u % kNT;
       mf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (kAdd) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] = Dm[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr];
       }
-      for (int ks = 0; ks < 4 * nt; ++ks) {
+#pragma unroll
+      for (int ks = 0; ks < 4 * kNT; ++ks) {
         const float a = A[(16 * rt + lr) * mp + 4 * ks + lg];
         const float bv = sb * B[(4 * ks + lg) * mp + 16 * ct + lr];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
@@ -348,17 +350,18 @@ __device__ __forceinline__ void gdn_mm(const float* A, const float* B, const flo
   }
 }
 
-// kM: node tiles of 16 rows in [Q; K] (2 NP / 16, NP <= 16 kM / 2).  Up to
-// 32 nodes (kM = 4) the kernel fits two workgroups per CU, registers included.
+// kM: node tiles of 16 rows in [Q; K], 2 NP / 16 for NP = N rounded up to 16.
+// Up to 32 nodes (kM <= 4) the kernel fits two workgroups per CU, registers
+// included.
 template <typename TO, int kM>
 __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <= 4 ? 4 : 2))) void gdn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int NP = (N + 15) / 16 * 16;
+  constexpr int NP = 8 * kM;  // N rounded up to 16 (the launch picks kM)
   unsigned char* r1 = smem;                      // S0 hi, S0 lo, then [Q; K] S0 fp32 [2NP][128]
-  const int MP = NP + 4;                         // row pitch of the NP x NP matrices (floats)
+  constexpr int MP = NP + 4;                     // row pitch of the NP x NP matrices (floats)
   unsigned char* r2 = smem + gdn_r1_bytes(NP);   // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][MP]
   float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V, then the right-hand side
   float* s_alpha = s_u + NP * kUP;
@@ -484,8 +487,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 
   // ---- phase 1: [Q; K] S0 (transposed) and the Gram products on MFMA.
   // The half of S0 in LDS times the [Q; K] rows, added into qks.
-  const int nqks = NP;          // 8 column tiles x 2NP / 16 node tiles
-  const int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
+  constexpr int nqks = NP;              // 8 column tiles x 2NP / 16 node tiles
+  constexpr int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
   mf32x4_t qks[kM], gram[kM / 2];
   // Tile u = wave + 8 m is column tile `wave` of node tile m: a wave keeps one
   // column tile, so each k-step reads its S0 fragment once for all node tiles.
@@ -608,18 +611,18 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     float* bm = s_y;                                   // M
     float* bp = s_x;                                   // the power of X
     float* bf = s_qks + NP * kDk;                      // free (the K S0 rows)
-    const int nt = NP / 16;
+    constexpr int nt = NP / 16;
     for (int j = 0; j < steps; ++j) {
       if (j > 0) {
         // next power: bf = bp bp
-        gdn_mm<false>(bp, bp, nullptr, bf, MP, nt, wave, lr, lg, 1.0f);
+        gdn_mm<false, nt>(bp, bp, nullptr, bf, MP, wave, lr, lg, 1.0f);
         __syncthreads();
         float* tmp = bp;
         bp = bf;
         bf = tmp;  // the old power is free
       }
       // M <- M + M (-X)^(2^j): the power is X negated for j = 0, else as stored
-      gdn_mm<true>(bm, bp, bm, bf, MP, nt, wave, lr, lg, j == 0 ? -1.0f : 1.0f);
+      gdn_mm<true, nt>(bm, bp, bm, bf, MP, wave, lr, lg, j == 0 ? -1.0f : 1.0f);
       __syncthreads();
       float* tmp = bm;
       bm = bf;
@@ -638,6 +641,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
         const float gt = s_gam[t];
         const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + 16 * ct + 4 * lg);
         mf32x4_t acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
+#pragma unroll
         for (int ks = 0; ks < NP / 4; ++ks) {
           const float a = s_u[(4 * ks + lg) * kUP + 16 * ct + lr];
           const float bv = bm[t * MP + 4 * ks + lg];
@@ -658,16 +662,23 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   }
 }
 
+// A grid that fits the CUs one workgroup each asks for more LDS than half a
+// CU's, so that no two of its workgroups share a CU.
+constexpr size_t kGdnSpreadLds = 81 * 1024;
+
 template <typename TO, int kM>
 hipError_t launch_gdn_mfma_m(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                              int H, void* out, hipStream_t stream) {
+  const size_t most = gdn_mfma_lds_bytes(8 * kM);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gdn_mfma_kernel<TO, kM>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gdn_mfma_lds_bytes(8 * kM)));
+      reinterpret_cast<const void*>(&gdn_mfma_kernel<TO, kM>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(most > kGdnSpreadLds ? most : kGdnSpreadLds));
   if (attr != hipSuccess) return attr;
+  size_t lds = gdn_mfma_lds_bytes(N);
+  if (static_cast<long long>(B) * H <= device_cus() && lds < kGdnSpreadLds) lds = kGdnSpreadLds;
   hipLaunchKernelGGL((gdn_mfma_kernel<TO, kM>), dim3(static_cast<unsigned>(B) * H), dim3(kMThreads),
-                     gdn_mfma_lds_bytes(N), stream, static_cast<const uint16_t*>(q),
+                     lds, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta, S0,
                      anc, N, H, static_cast<TO*>(out));
   return hipGetLastError();
@@ -677,8 +688,13 @@ template <typename TO>
 hipError_t launch_gdn_mfma(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                            int H, void* out, hipStream_t stream) {
-  if (N <= 32) return launch_gdn_mfma_m<TO, 4>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
-  return launch_gdn_mfma_m<TO, 8>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+  switch ((N + 15) / 16) {
+    case 1: return launch_gdn_mfma_m<TO, 2>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 2: return launch_gdn_mfma_m<TO, 4>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 3: return launch_gdn_mfma_m<TO, 6>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 4: return launch_gdn_mfma_m<TO, 8>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T, typename TO>

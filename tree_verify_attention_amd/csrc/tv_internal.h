@@ -28,6 +28,10 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// compute units of the current device (256 on an MI355X; that value also
+// when no device can be queried, e.g. for a size query on a host without one)
+int device_cus();
+
 // ---- launchers (one per kernel family); return the launch error
 hipError_t launch_mask(const int32_t* parent, const int32_t* depth_in, const int32_t* ctx_len,
                        int B, int N, uint64_t* anc, int32_t* depth_out, int32_t* pos,
