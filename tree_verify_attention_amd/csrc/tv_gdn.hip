@@ -298,27 +298,26 @@ __device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
 
 constexpr int kUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
 
-// bytes of one bf16 half of S0, later [Q; K] S0 (fp32, 2NP rows of 128)
+// bytes of region 1: X, Y and a third NP x NP matrix for the solve, then one
+// bf16 half of S0 at a time, then [Q; K] S0 (fp32, 2NP rows of 128)
 __host__ __device__ inline size_t gdn_r1_bytes(int np) {
   const size_t half = static_cast<size_t>(kDk) * kRowB;
   const size_t qks = 2 * static_cast<size_t>(np) * kDk * 4;
-  return half > qks ? half : qks;
+  const size_t solve = 3 * static_cast<size_t>(np) * (np + 4) * 4;
+  const size_t m = half > qks ? half : qks;
+  return m > solve ? m : solve;
 }
 
-// bytes of the [Q; K] rows, later X and Y (row pitch NP + 4)
-__host__ __device__ inline size_t gdn_r2_bytes(int np) {
-  const size_t qk = 2 * static_cast<size_t>(np) * kRowB;
-  const size_t xy = 2 * static_cast<size_t>(np) * (np + 4) * 4;
-  return qk > xy ? qk : xy;
-}
+// bytes of the [Q; K] rows (bf16)
+__host__ __device__ inline size_t gdn_r2_bytes(int np) { return 2 * static_cast<size_t>(np) * kRowB; }
 
 size_t gdn_mfma_lds_bytes(int N) {
   const int np = (N + 15) / 16 * 16;
-  // S0 hi, then S0 lo (bf16), later [Q; K] S0 (fp32); [Q; K] (bf16), later X
-  // and Y (fp32); V, later the right-hand side (fp32); alpha, beta, gamma,
-  // log2 gamma, depth, ancestor words.  Up to 32 nodes this is 68 KB, so two
-  // workgroups share a CU.
-  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 + 64 * 4 * 5 + 64 * 8;
+  // region 1; [Q; K]; V, later the right-hand side (fp32); M (fp32); alpha,
+  // beta, gamma, log2 gamma, depth, ancestor words.  Up to 32 nodes this is
+  // 72 KB, so two workgroups fit a CU.
+  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 +
+         static_cast<size_t>(np) * (np + 4) * 4 + 64 * 4 * 5 + 64 * 8;
 }
 
 // C = A B (+ D), NP x NP fp32 matrices of row pitch mp in LDS, on
@@ -360,11 +359,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NP = 8 * kM;  // N rounded up to 16 (the launch picks kM)
-  unsigned char* r1 = smem;                      // S0 hi, S0 lo, then [Q; K] S0 fp32 [2NP][128]
   constexpr int MP = NP + 4;                     // row pitch of the NP x NP matrices (floats)
-  unsigned char* r2 = smem + gdn_r1_bytes(NP);   // [Q; K] bf16 [2NP][128], then X, Y fp32 [NP][MP]
+  unsigned char* r1 = smem;                      // X, Y, third; then S0 hi, S0 lo; then [Q; K] S0 fp32
+  unsigned char* r2 = smem + gdn_r1_bytes(NP);   // [Q; K] bf16 [2NP][128]
   float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V, then the right-hand side
-  float* s_alpha = s_u + NP * kUP;
+  float* s_m = s_u + NP * kUP;                   // M [NP][MP]
+  float* s_alpha = s_m + NP * MP;
   float* s_beta = s_alpha + 64;
   float* s_gam = s_beta + 64;
   float* s_lgam = s_gam + 64;
@@ -380,13 +380,9 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const uint64_t live = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
 
-  // ---- phase 0: S0 (split into bf16 hi and lo), q and k rows, v, gates.
-  // Every global load is issued before the first conversion or LDS store.
+  // ---- phase 0: q and k rows, v and the gates, then S0.  S0's loads stay in
+  // flight through the Gram products and the solve, which do not need it.
   if (tid == 0) s_maxdepth = 1;
-  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk;
-  float4 f[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) f[u] = reinterpret_cast<const float4*>(s0)[tid + u * kMThreads];
   constexpr int kQKPer = 2 * 64 * (kRowB / 16) / kMThreads;  // q / k granules per thread (at most)
   constexpr int kVPer = 64 * (kDk / 8) / kMThreads;           // v granules per thread (at most)
   uint4 gq[kQKPer], gv[kVPer];
@@ -417,22 +413,6 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     ga = alpha[nh];
     gb = beta[nh];
     gw = anc[static_cast<size_t>(b) * N + tid];
-  }
-  // the low halves wait, packed, in registers until the high half has been used
-  uint2 s0lo[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + u * kMThreads;
-    const int d = e >> 5, c = (e & 31) * 4;
-    // hi = bf16(x) (round to nearest even, the hardware conversion), lo = bf16(x - hi)
-    const mbf16x4_t hv = {static_cast<__bf16>(f[u].x), static_cast<__bf16>(f[u].y),
-                          static_cast<__bf16>(f[u].z), static_cast<__bf16>(f[u].w)};
-    const mbf16x4_t lv = {static_cast<__bf16>(f[u].x - static_cast<float>(hv[0])),
-                          static_cast<__bf16>(f[u].y - static_cast<float>(hv[1])),
-                          static_cast<__bf16>(f[u].z - static_cast<float>(hv[2])),
-                          static_cast<__bf16>(f[u].w - static_cast<float>(hv[3]))};
-    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, hv);
-    s0lo[u] = __builtin_bit_cast(uint2, lv);
   }
 #pragma unroll
   for (int u = 0; u < kQKPer; ++u) {
@@ -465,6 +445,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     s_anc[t] = t < N ? ((gw & live & below) | (1ull << t)) : 0ull;
   }
   __syncthreads();
+  // S0 goes out once the small loads are in (issued with them, it would
+  // delay them: every workgroup's S0 competes for HBM at the same moment)
+  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk;
+  float4 f[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) f[u] = reinterpret_cast<const float4*>(s0)[tid + u * kMThreads];
   if (tid < 64) {
     // gamma_t = product of alpha over t's root path; its log2 gives the gate
     // ratio gamma_t / gamma_i of any ancestor i without a path walk (and
@@ -485,37 +471,10 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     if (t < N) atomicMax(&s_maxdepth, dpt);
   }
 
-  // ---- phase 1: [Q; K] S0 (transposed) and the Gram products on MFMA.
-  // The half of S0 in LDS times the [Q; K] rows, added into qks.
+  // ---- phase 1: the Gram products [Q; K] K^T on MFMA (exact bf16 products)
   constexpr int nqks = NP;              // 8 column tiles x 2NP / 16 node tiles
   constexpr int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
   mf32x4_t qks[kM], gram[kM / 2];
-  // Tile u = wave + 8 m is column tile `wave` of node tile m: a wave keeps one
-  // column tile, so each k-step reads its S0 fragment once for all node tiles.
-  auto s0_product = [&]() {
-    const int vcol = wave * 32 + 8 * (lr & 3);
-#pragma unroll
-    for (int ks = 0; ks < kDk / 32; ++ks) {
-      const int vrow = 32 * ks + 4 * lg + (lr >> 2);
-      const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
-      const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
-      const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-#pragma unroll
-      for (int m = 0; m < kM; ++m) {
-        if (wave + 8 * m < nqks) {
-          const int row = 16 * m + lr;
-          const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
-          const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
-          const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
-          qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
-                                                            qks[m], 0, 0, 0);
-        }
-      }
-    }
-  };
-#pragma unroll
-  for (int m = 0; m < kM; ++m) qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
-  s0_product();  // high half
 #pragma unroll
   for (int m = 0; m < kM / 2; ++m) {
     const int u = wave + 8 * m;
@@ -532,30 +491,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
       }
     }
   }
-  __syncthreads();  // every read of S0's high half is done
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + u * kMThreads;
-    const int d = e >> 5, c = (e & 31) * 4;
-    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = s0lo[u];
-  }
-  __syncthreads();
-  s0_product();  // low half
-  __syncthreads();  // every read of S0 and of the q / k rows is done
+  __syncthreads();  // gamma and the depths are in
 
-  // results into LDS: [Q; K] S0 rows, and X, Y with their masks and gates
-  float* s_qks = reinterpret_cast<float*>(r1);   // [2NP][128]
-  float* s_x = reinterpret_cast<float*>(r2);     // [NP][MP]
-  float* s_y = s_x + NP * MP;                    // [NP][MP]
-#pragma unroll
-  for (int m = 0; m < kM; ++m) {
-    const int u = wave + 8 * m;
-    if (u < nqks) {
-      const int ct = u & 7, nt = u >> 3;
-      *reinterpret_cast<float4*>(s_qks + (16 * nt + lr) * kDk + 16 * ct + 4 * lg) =
-          make_float4(qks[m][0], qks[m][1], qks[m][2], qks[m][3]);
-    }
-  }
+  // X and Y with their masks and gate ratios, into region 1
+  float* s_x = reinterpret_cast<float*>(r1);  // [NP][MP]
+  float* s_y = s_x + NP * MP;                 // [NP][MP]
+  float* s_t = s_y + NP * MP;                 // [NP][MP], a third matrix for the solve
 #pragma unroll
   for (int m = 0; m < kM / 2; ++m) {
     const int u = wave + 8 * m;
@@ -585,21 +526,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   }
   __syncthreads();
 
-  // ---- phase 2: right-hand side beta_t (v_t - gamma_t (K S0)_t), in place of V
-  for (int e = tid; e < N * (kDk / 4); e += kMThreads) {
-    const int t = e / (kDk / 4), c = (e % (kDk / 4)) * 4;
-    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kUP + c);
-    const float4 ks = *reinterpret_cast<const float4*>(s_qks + (NP + t) * kDk + c);
-    const float bt = s_beta[t], gt = s_gam[t];
-    uu.x = bt * (uu.x - gt * ks.x);
-    uu.y = bt * (uu.y - gt * ks.y);
-    uu.z = bt * (uu.z - gt * ks.z);
-    uu.w = bt * (uu.w - gt * ks.w);
-    *reinterpret_cast<float4*>(s_u + t * kUP + c) = uu;
-  }
-  __syncthreads();  // K S0 is no longer needed: its rows hold a third matrix below
-
-  // ---- phase 3: M = Y (I + X)^-1.  X only couples a node to its strict
+  // ---- phase 2: M = Y (I + X)^-1.  X only couples a node to its strict
   // ancestors, so X^d = 0 past the tree's depth and (I + X)^-1 is the finite
   // product of (I + (-X)^(2^j)), j < ceil(log2 depth): M starts as Y and takes
   // one factor per step, the power by repeated squaring.  Three NP x NP
@@ -608,9 +535,9 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     const int maxdepth = s_maxdepth;
     int steps = 0;
     while ((1 << steps) < maxdepth) ++steps;
-    float* bm = s_y;                                   // M
-    float* bp = s_x;                                   // the power of X
-    float* bf = s_qks + NP * kDk;                      // free (the K S0 rows)
+    float* bm = s_y;  // M
+    float* bp = s_x;  // the power of X
+    float* bf = s_t;  // free
     constexpr int nt = NP / 16;
     for (int j = 0; j < steps; ++j) {
       if (j > 0) {
@@ -628,34 +555,122 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
       bm = bf;
       bf = tmp;
     }
+    // M out of region 1, which S0 takes next
+    for (int e = tid; e < NP * MP / 4; e += kMThreads)
+      reinterpret_cast<float4*>(s_m)[e] = reinterpret_cast<const float4*>(bm)[e];
+  }
+  __syncthreads();
 
-    // ---- phase 4: O^T = (right-hand side)^T M^T + gamma (Q S0)^T, tiles of
-    // 16 state columns x 16 nodes; a lane ends with 4 consecutive columns of
-    // one node's output
+  // ---- phase 3: [Q; K] S0 on MFMA, formed transposed (S0^T [Q; K]^T).  S0
+  // is split into bf16 hi = bf16(S0) (round to nearest even, the hardware
+  // conversion) and lo = bf16(S0 - hi); the halves pass one after the other
+  // through region 1, lo waiting packed in registers.
+  uint2 s0lo[8];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const int u = wave + 8 * mm;
-      if (u < 8 * nt) {
-        const int ct = u & 7, ntile = u >> 3;
-        const int t = 16 * ntile + lr;
-        const float gt = s_gam[t];
-        const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + 16 * ct + 4 * lg);
-        mf32x4_t acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * kMThreads;
+    const int d = e >> 5, c = (e & 31) * 4;
+    const mbf16x4_t hv = {static_cast<__bf16>(f[u].x), static_cast<__bf16>(f[u].y),
+                          static_cast<__bf16>(f[u].z), static_cast<__bf16>(f[u].w)};
+    const mbf16x4_t lv = {static_cast<__bf16>(f[u].x - static_cast<float>(hv[0])),
+                          static_cast<__bf16>(f[u].y - static_cast<float>(hv[1])),
+                          static_cast<__bf16>(f[u].z - static_cast<float>(hv[2])),
+                          static_cast<__bf16>(f[u].w - static_cast<float>(hv[3]))};
+    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, hv);
+    s0lo[u] = __builtin_bit_cast(uint2, lv);
+  }
+  __syncthreads();
+  // Tile u = wave + 8 m is column tile `wave` of node tile m: a wave keeps one
+  // column tile, so each k-step reads its S0 fragment once for all node tiles.
+  auto s0_product = [&]() {
+    const int vcol = wave * 32 + 8 * (lr & 3);
 #pragma unroll
-        for (int ks = 0; ks < NP / 4; ++ks) {
-          const float a = s_u[(4 * ks + lg) * kUP + 16 * ct + lr];
-          const float bv = bm[t * MP + 4 * ks + lg];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+    for (int ks = 0; ks < kDk / 32; ++ks) {
+      const int vrow = 32 * ks + 4 * lg + (lr >> 2);
+      const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
+      const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
+      const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+#pragma unroll
+      for (int m = 0; m < kM; ++m) {
+        if (wave + 8 * m < nqks) {
+          const int row = 16 * m + lr;
+          const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
+          const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
+          const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
+          qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
+                                                            qks[m], 0, 0, 0);
         }
-        if (t < N) {
-          const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * ct + 4 * lg;
-          if constexpr (sizeof(TO) == 2) {
-            const mbf16x4_t w = {static_cast<__bf16>(acc[0]), static_cast<__bf16>(acc[1]),
-                                 static_cast<__bf16>(acc[2]), static_cast<__bf16>(acc[3])};
-            *reinterpret_cast<uint2*>(out + off) = __builtin_bit_cast(uint2, w);
-          } else {
-            *reinterpret_cast<float4*>(out + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-          }
+      }
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < kM; ++m) qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+  s0_product();  // high half
+  __syncthreads();  // every read of S0's high half is done
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + u * kMThreads;
+    const int d = e >> 5, c = (e & 31) * 4;
+    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = s0lo[u];
+  }
+  __syncthreads();
+  s0_product();  // low half
+  __syncthreads();  // every read of S0 is done
+
+  // [Q; K] S0 rows into region 1
+  float* s_qks = reinterpret_cast<float*>(r1);  // [2NP][128]
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    const int u = wave + 8 * m;
+    if (u < nqks) {
+      const int ct = u & 7, nt = u >> 3;
+      *reinterpret_cast<float4*>(s_qks + (16 * nt + lr) * kDk + 16 * ct + 4 * lg) =
+          make_float4(qks[m][0], qks[m][1], qks[m][2], qks[m][3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 4: right-hand side beta_t (v_t - gamma_t (K S0)_t), in place of V
+  for (int e = tid; e < N * (kDk / 4); e += kMThreads) {
+    const int t = e / (kDk / 4), c = (e % (kDk / 4)) * 4;
+    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kUP + c);
+    const float4 ks = *reinterpret_cast<const float4*>(s_qks + (NP + t) * kDk + c);
+    const float bt = s_beta[t], gt = s_gam[t];
+    uu.x = bt * (uu.x - gt * ks.x);
+    uu.y = bt * (uu.y - gt * ks.y);
+    uu.z = bt * (uu.z - gt * ks.z);
+    uu.w = bt * (uu.w - gt * ks.w);
+    *reinterpret_cast<float4*>(s_u + t * kUP + c) = uu;
+  }
+  __syncthreads();
+
+  // ---- phase 5: O^T = (right-hand side)^T M^T + gamma (Q S0)^T, tiles of
+  // 16 state columns x 16 nodes; a lane ends with 4 consecutive columns of
+  // one node's output
+  constexpr int nt = NP / 16;
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) {
+    const int u = wave + 8 * mm;
+    if (u < 8 * nt) {
+      const int ct = u & 7, ntile = u >> 3;
+      const int t = 16 * ntile + lr;
+      const float gt = s_gam[t];
+      const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + 16 * ct + 4 * lg);
+      mf32x4_t acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
+#pragma unroll
+      for (int ks = 0; ks < NP / 4; ++ks) {
+        const float a = s_u[(4 * ks + lg) * kUP + 16 * ct + lr];
+        const float bv = s_m[t * MP + 4 * ks + lg];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+      }
+      if (t < N) {
+        const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * ct + 4 * lg;
+        if constexpr (sizeof(TO) == 2) {
+          const mbf16x4_t w = {static_cast<__bf16>(acc[0]), static_cast<__bf16>(acc[1]),
+                               static_cast<__bf16>(acc[2]), static_cast<__bf16>(acc[3])};
+          *reinterpret_cast<uint2*>(out + off) = __builtin_bit_cast(uint2, w);
+        } else {
+          *reinterpret_cast<float4*>(out + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
       }
     }
