@@ -272,8 +272,10 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
 // parts S0 = hi + lo (hi its round-to-nearest bf16, lo that of the remainder),
 // so two bf16 products with fp32 accumulation carry S0 to ~16 mantissa bits
 // while q and k are used exactly.  The Gram products [Q; K] K^T are exact bf16
-// products.  Their masks and gate ratios are applied in registers; the small
-// forward substitution and the outputs then run as vectorised LDS loops.
+// products; their masks and gate ratios are applied in registers.  The solve
+// (I + X)^-1 is a short product of matrix powers on fp32 MFMA.  Gram products
+// and solve need neither S0 nor v, so they run first, while S0's loads are in
+// flight; the state products, the right-hand side and the outputs follow.
 constexpr int kMThreads = 512;
 constexpr int kRowB = kDk * 2;  // bytes of one bf16 row of 128
 
