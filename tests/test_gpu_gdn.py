@@ -49,6 +49,15 @@ def test_c5_full(lib):
     check(lib, x, "c5")
 
 
+def test_step_batch_two_per_cu(lib):
+    """The verify step's GDN shape: 32 sequences x 16 heads = 512 workgroups,
+    more than the CUs, so two share a CU (the launch the benchmark times);
+    the trees are the step's spine-first trees."""
+    x = W.gdn_inputs(3, B=32, N=32, H=16, Dk=128, Dv=128, tree="spine_first", dtype=torch.bfloat16,
+                     device=DEV)
+    check(lib, x, "step batch")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("tree,N", [("chain", 64), ("star", 17), ("random_parent", 64),
                                     ("random_parent", 1), ("leaf_sibling", 32), ("spine_first", 40)])
