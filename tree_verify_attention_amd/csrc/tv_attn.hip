@@ -624,11 +624,14 @@ __device__ __forceinline__ void attn_segment(
     const float2 o = mb_ml[wt * 64 + lane];
     const float m_new = fmaxf(m_run, o.x);  // finite: every row sees its own node
     const float c0 = fast_exp2(m_run - m_new), c1 = fast_exp2(o.x - m_new);
-    l_tot = l_tot * c0 + o.y * c1;
+    // explicit fmaf: both output types' instantiations round alike
+    l_tot = __builtin_fmaf(o.y, c1, l_tot * c0);
 #pragma unroll
-    for (int dt = 0; dt < C::kDT; ++dt)
-      acc[dt] = acc[dt] * c0 +
-                *reinterpret_cast<const f32x4_t*>(mb_acc + ((wt * C::kDT + dt) * 64 + lane) * 4) * c1;
+    for (int dt = 0; dt < C::kDT; ++dt) {
+      const f32x4_t t1 = *reinterpret_cast<const f32x4_t*>(mb_acc + ((wt * C::kDT + dt) * 64 + lane) * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dt][r] = __builtin_fmaf(t1[r], c1, acc[dt][r] * c0);
+    }
     m_run = m_new;
   }
   if (!row_ok) return;
@@ -1520,13 +1523,14 @@ __global__ __launch_bounds__(256) void attn_merge_stream_kernel(
       const float m_new = fmaxf(mx, ml[p].x);
       const float c_old = fast_exp2(mx - m_new);
       const float c_new = fast_exp2(ml[p].x - m_new);
-      L = L * c_old + ml[p].y * c_new;
+      // explicit fmaf: both output types' instantiations round alike
+      L = __builtin_fmaf(ml[p].y, c_new, L * c_old);
 #pragma unroll
       for (int k = 0; k < kV; ++k) {
-        o[k].x = o[k].x * c_old + a[p][k].x * c_new;
-        o[k].y = o[k].y * c_old + a[p][k].y * c_new;
-        o[k].z = o[k].z * c_old + a[p][k].z * c_new;
-        o[k].w = o[k].w * c_old + a[p][k].w * c_new;
+        o[k].x = __builtin_fmaf(a[p][k].x, c_new, o[k].x * c_old);
+        o[k].y = __builtin_fmaf(a[p][k].y, c_new, o[k].y * c_old);
+        o[k].z = __builtin_fmaf(a[p][k].z, c_new, o[k].z * c_old);
+        o[k].w = __builtin_fmaf(a[p][k].w, c_new, o[k].w * c_old);
       }
       mx = m_new;
     }
@@ -1585,11 +1589,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     const float m_new = fmaxf(mx, ml.x);
     const float c_old = fast_exp2(mx - m_new);  // 0 while mx is still -inf
     const float c_new = fast_exp2(ml.x - m_new);
-    L = L * c_old + ml.y * c_new;
-    o.x = o.x * c_old + a.x * c_new;
-    o.y = o.y * c_old + a.y * c_new;
-    o.z = o.z * c_old + a.z * c_new;
-    o.w = o.w * c_old + a.w * c_new;
+    // explicit fmaf: both output types' instantiations round alike
+    L = __builtin_fmaf(ml.y, c_new, L * c_old);
+    o.x = __builtin_fmaf(a.x, c_new, o.x * c_old);
+    o.y = __builtin_fmaf(a.y, c_new, o.y * c_old);
+    o.z = __builtin_fmaf(a.z, c_new, o.z * c_old);
+    o.w = __builtin_fmaf(a.w, c_new, o.w * c_old);
     mx = m_new;
   }
   const float inv = 1.0f / L;
