@@ -399,8 +399,8 @@ def attn_only(args, dev) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is "
-              f"described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
+              f"multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
