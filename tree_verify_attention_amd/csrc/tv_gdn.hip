@@ -448,11 +448,17 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   }
   __syncthreads();
   // S0 goes out once the small loads are in (issued with them, it would
-  // delay them: every workgroup's S0 competes for HBM at the same moment)
+  // delay them: every workgroup's S0 competes for HBM at the same moment),
+  // in three batches between the phases that do not need it, so that no
+  // wave stalls long on a full memory pipeline
   const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk;
   float4 f[8];
+  auto s0_issue = [&](int u0, int u1) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) f[u] = reinterpret_cast<const float4*>(s0)[tid + u * kMThreads];
+    for (int u = 0; u < 8; ++u)
+      if (u >= u0 && u < u1) f[u] = reinterpret_cast<const float4*>(s0)[tid + u * kMThreads];
+  };
+  s0_issue(0, 3);
   if (tid < 64) {
     // gamma_t = product of alpha over t's root path; its log2 gives the gate
     // ratio gamma_t / gamma_i of any ancestor i without a path walk (and
@@ -493,6 +499,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
       }
     }
   }
+  s0_issue(3, 6);
   __syncthreads();  // gamma and the depths are in
 
   // X and Y with their masks and gate ratios, into region 1
@@ -527,6 +534,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     }
   }
   __syncthreads();
+
+  s0_issue(6, 8);
 
   // ---- phase 2: M = Y (I + X)^-1.  X only couples a node to its strict
   // ancestors, so X^d = 0 past the tree's depth and (I + X)^-1 is the finite
