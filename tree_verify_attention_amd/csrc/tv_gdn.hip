@@ -21,6 +21,8 @@
 // 32 output columns), every product as fp32 FMAs from LDS; the columns of U
 // and O are independent, so the state S0 is read once in total while the
 // (small) Gram terms are recomputed per column block.
+#include <atomic>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -688,6 +690,20 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   }
 }
 
+// Raises a kernel's dynamic LDS limit once per device (the attribute is held
+// per device); `done` holds one flag per device id.
+constexpr int kMaxDevices = 64;
+hipError_t max_lds_once(std::atomic<int>* done, const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && cached) done[dev].store(1, std::memory_order_release);
+  return e;
+}
+
 // A grid that fits the CUs one workgroup each asks for more LDS than half a
 // CU's, so that no two of its workgroups share a CU.
 constexpr size_t kGdnSpreadLds = 81 * 1024;
@@ -697,9 +713,9 @@ hipError_t launch_gdn_mfma_m(const void* q, const void* k, const void* v, const 
                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                              int H, void* out, hipStream_t stream) {
   const size_t most = gdn_mfma_lds_bytes(8 * kM);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gdn_mfma_kernel<TO, kM>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(most > kGdnSpreadLds ? most : kGdnSpreadLds));
+  static std::atomic<int> lds_set[kMaxDevices];
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_mfma_kernel<TO, kM>),
+                                       static_cast<int>(most > kGdnSpreadLds ? most : kGdnSpreadLds));
   if (attr != hipSuccess) return attr;
   size_t lds = gdn_mfma_lds_bytes(N);
   if (static_cast<long long>(B) * H <= device_cus() && lds < kGdnSpreadLds) lds = kGdnSpreadLds;
@@ -728,9 +744,9 @@ hipError_t launch_gdn_typed(const void* q, const void* k, const void* v, const f
                             const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                             int H, int Dv, void* out, hipStream_t stream) {
   const size_t lds = gdn_lds_bytes(N);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gdn_tree_kernel<T, TO>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(gdn_lds_bytes(64)));
+  static std::atomic<int> lds_set[kMaxDevices];
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_tree_kernel<T, TO>),
+                                       static_cast<int>(gdn_lds_bytes(64)));
   if (attr != hipSuccess) return attr;
   const unsigned grid = static_cast<unsigned>(B) * H * (Dv / kCB);
   hipLaunchKernelGGL((gdn_tree_kernel<T, TO>), dim3(grid), dim3(kThreads), lds, stream,
