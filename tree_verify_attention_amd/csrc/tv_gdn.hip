@@ -302,12 +302,12 @@ __device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
 
 constexpr int kUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
 
-// bytes of region 1: X, Y and a third NP x NP matrix for the solve, then one
+// bytes of region 1: X, Y and two more NP x NP matrices for the solve, then one
 // bf16 half of S0 at a time, then [Q; K] S0 (fp32, 2NP rows of 128)
 __host__ __device__ inline size_t gdn_r1_bytes(int np) {
   const size_t half = static_cast<size_t>(kDk) * kRowB;
   const size_t qks = 2 * static_cast<size_t>(np) * kDk * 4;
-  const size_t solve = 3 * static_cast<size_t>(np) * (np + 4) * 4;
+  const size_t solve = 4 * static_cast<size_t>(np) * (np + 4) * 4;
   const size_t m = half > qks ? half : qks;
   return m > solve ? m : solve;
 }
@@ -324,31 +324,42 @@ size_t gdn_mfma_lds_bytes(int N) {
          static_cast<size_t>(np) * (np + 4) * 4 + 64 * 4 * 5 + 64 * 8;
 }
 
-// C = A B (+ D), NP x NP fp32 matrices of row pitch mp in LDS, on
-// v_mfma_f32_16x16x4f32; B's entries are scaled by `sb`.  Tiles are dealt to
-// the 8 waves; a lane holds column lr of rows 4 lg .. 4 lg + 3 of its tile.
-// kNT = NP / 16 tiles per side.
+// One 16 x 16 tile (row tile rt, column tile ct) of C = A B (+ D), NP x NP
+// fp32 matrices of row pitch mp in LDS, on v_mfma_f32_16x16x4f32; B's
+// entries are scaled by `sb`.  A lane holds column lr of rows 4 lg .. 4 lg + 3.
 template <bool kAdd, int kNT>
-__device__ __forceinline__ void gdn_mm(const float* A, const float* B, const float* Dm, float* C, int mp,
-                                       int wave, int lr, int lg, float sb) {
+__device__ __forceinline__ void gdn_mm_tile(const float* A, const float* B, const float* Dm, float* C, int mp,
+                                            int rt, int ct, int lr, int lg, float sb) {
+  mf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kAdd) {
 #pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
+    for (int r = 0; r < 4; ++r) acc[r] = Dm[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr];
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4 * kNT; ++ks) {
+    const float a = A[(16 * rt + lr) * mp + 4 * ks + lg];
+    const float bv = sb * B[(4 * ks + lg) * mp + 16 * ct + lr];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) C[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr] = acc[r];
+}
+
+// One step of the solve as a single phase: Mo = M + M (sb P) and, when Po is
+// given, Po = P P.  Both read only M and P, so their 2 kNT^2 tiles are dealt
+// to the 8 waves together.  kNT = NP / 16 tiles per side.
+template <int kNT>
+__device__ __forceinline__ void gdn_solve_step(const float* M, const float* P, float* Mo, float* Po, int mp,
+                                               int wave, int lr, int lg, float sb) {
+  constexpr int kT = kNT * kNT;
+#pragma unroll
+  for (int mm = 0; mm < (2 * kT + 7) / 8; ++mm) {
     const int u = wave + 8 * mm;
-    if (u < kNT * kNT) {
-      const int rt = u / kNT, ct = u % kNT;
-      mf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (kAdd) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = Dm[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr];
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4 * kNT; ++ks) {
-        const float a = A[(16 * rt + lr) * mp + 4 * ks + lg];
-        const float bv = sb * B[(4 * ks + lg) * mp + 16 * ct + lr];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) C[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr] = acc[r];
+    if (u < kT) {
+      gdn_mm_tile<true, kNT>(M, P, M, Mo, mp, u / kNT, u % kNT, lr, lg, sb);
+    } else if (u < 2 * kT && Po != nullptr) {
+      const int v = u - kT;
+      gdn_mm_tile<false, kNT>(P, P, nullptr, Po, mp, v / kNT, v % kNT, lr, lg, 1.0f);
     }
   }
 }
@@ -507,7 +518,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   // X and Y with their masks and gate ratios, into region 1
   float* s_x = reinterpret_cast<float*>(r1);  // [NP][MP]
   float* s_y = s_x + NP * MP;                 // [NP][MP]
-  float* s_t = s_y + NP * MP;                 // [NP][MP], a third matrix for the solve
+  float* s_t = s_y + NP * MP;                 // [NP][MP], two more matrices for the solve
+  float* s_t2 = s_t + NP * MP;                // [NP][MP]
 #pragma unroll
   for (int m = 0; m < kM / 2; ++m) {
     const int u = wave + 8 * m;
@@ -542,31 +554,31 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   // ---- phase 2: M = Y (I + X)^-1.  X only couples a node to its strict
   // ancestors, so X^d = 0 past the tree's depth and (I + X)^-1 is the finite
   // product of (I + (-X)^(2^j)), j < ceil(log2 depth): M starts as Y and takes
-  // one factor per step, the power by repeated squaring.  Three NP x NP
-  // buffers rotate (current M, current power, free); fp32 MFMA throughout.
+  // one factor per step, while the power is squared for the next step (both
+  // products in one phase, one barrier per step).  Four NP x NP buffers
+  // rotate; fp32 MFMA throughout.
   {
     const int maxdepth = s_maxdepth;
     int steps = 0;
     while ((1 << steps) < maxdepth) ++steps;
-    float* bm = s_y;  // M
-    float* bp = s_x;  // the power of X
-    float* bf = s_t;  // free
+    float* bm = s_y;   // M
+    float* bp = s_x;   // the power of X, stored as X^(2^j) ((-X)^(2^j) for j > 0 is the same)
+    float* fm = s_t;   // free, for the next M
+    float* fp = s_t2;  // free, for the next power
     constexpr int nt = NP / 16;
     for (int j = 0; j < steps; ++j) {
-      if (j > 0) {
-        // next power: bf = bp bp
-        gdn_mm<false, nt>(bp, bp, nullptr, bf, MP, wave, lr, lg, 1.0f);
-        __syncthreads();
-        float* tmp = bp;
-        bp = bf;
-        bf = tmp;  // the old power is free
-      }
+      const bool more = j + 1 < steps;
       // M <- M + M (-X)^(2^j): the power is X negated for j = 0, else as stored
-      gdn_mm<true, nt>(bm, bp, bm, bf, MP, wave, lr, lg, j == 0 ? -1.0f : 1.0f);
+      gdn_solve_step<nt>(bm, bp, fm, more ? fp : nullptr, MP, wave, lr, lg, j == 0 ? -1.0f : 1.0f);
       __syncthreads();
       float* tmp = bm;
-      bm = bf;
-      bf = tmp;
+      bm = fm;
+      fm = tmp;
+      if (more) {
+        tmp = bp;
+        bp = fp;
+        fp = tmp;
+      }
     }
     // M out of region 1, which S0 takes next
     for (int e = tid; e < NP * MP / 4; e += kMThreads)
