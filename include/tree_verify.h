@@ -164,6 +164,9 @@ tv_status tree_verify_attn(const void* q, const void* k_node, const void* v_node
  *   S0        float [B, H, Dk, Dv] committed state (read only)
  *   anc_mask  uint64 [B, N]   from tree_mask_build (one word per node: N <= 64)
  *   out       [B, N, H, Dv]   out_dtype (TV_F32, or TV_BF16 with bf16 inputs)
+ * Gates may be any finite values, 0 included (a gate exp(g) that underflowed):
+ * a zero gate cuts the path's decay products to exactly 0.
+ * q, k, v, S0 and out must be 16-byte aligned.
  * Supported: 1 <= N <= TV_GDN_MAX_NODES, Dk == Dv == 128.
  * ------------------------------------------------------------------------ */
 tv_status tree_gdn_verify(const void* q, const void* k, const void* v,

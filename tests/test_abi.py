@@ -117,6 +117,10 @@ def test_gdn_validation(lib):
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
     bad = list(args); bad[12] = tv.TV_F32; bad[13] = tv.TV_BF16
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
+    # q, k, v, S0 and out must be 16-byte aligned
+    for i in (0, 1, 2, 5, 14):
+        bad = list(args); bad[i] = ctypes.c_void_p(0x1008)
+        assert f(*bad) == tv.TV_ERR_UNSUPPORTED, i
 
 
 def test_walk_validation(lib):

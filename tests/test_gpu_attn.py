@@ -216,3 +216,46 @@ def test_c4_shape_at_128_nodes(lib):
     1024 query rows per kv head."""
     x, _ = make(4, B=2, N=128, ctx_lo=1500, ctx_hi=2100, tree="ddtree")
     check_full(lib, x, 0, "c4-shape N=128")
+
+
+def _nsplit_host(x, window, rows_per_wg=64, min_split=2048, target_wg=4096, tile=32):
+    """Splits the library plans for a split-layout launch, recomputed on the
+    host from the documented planning rule (at least 2048 keys per split,
+    about 4096 workgroups): used only to assert that a case reaches several
+    splits."""
+    rows = (x.Hq // x.Hkv) * x.N
+    rg = -(-rows // rows_per_wg)
+    rng = min(x.max_ctx_len, window) if window > 0 else x.max_ctx_len
+    want = max(1, min(-(-target_wg // (x.B * x.Hkv * rg)), max(1, -(-rng // min_split))))
+    st = max(tile, -(-(-(-rng // want)) // tile) * tile)
+    return -(-rng // st) if rng > 0 else 1
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("window,D", [(2049, 256), (4096, 128), (8192, 256)])
+def test_split_layout_several_splits(lib, dtype, window, D):
+    """Sliding windows wider than one split (serve-integration spec, "2. Verify:
+    tree attention mask": the per-layer window): the split kernel writes fp32
+    partials per split, hands the second team's state over in LDS, and the
+    merge kernel combines them.  G * N = 64 rows per kv head; contexts up to
+    12k, one shorter than the window and one empty."""
+    trees = W.make_trees(56, "spine_first", 3, 32, 1000)
+    x, _ = make(3, B=3, N=32, Hq=4, Hkv=2, D=D, trees=trees, dtype=dtype,
+                ctx_len=np.array([12000, 3000, 0], dtype=np.int32))
+    ws = lib.tree_verify_attn_workspace_size(x.B, x.N, x.Hq, x.Hkv, x.D, x.max_ctx_len, window)
+    assert ws > 0, "partials in use"
+    assert _nsplit_host(x, window) >= 2
+    check_full(lib, x, window, f"split W={window} D={D} {dtype}")
+
+
+def test_split_layout_fp32_many_rows(lib):
+    """fp32 with G * N > 64 (two row groups of the split kernel) over contexts
+    longer than one split, global and windowed."""
+    trees = W.make_trees(57, "random_parent", 3, 20, 1000)
+    x, _ = make(1, B=3, N=20, Hq=8, Hkv=2, D=128, trees=trees, dtype=torch.float32,
+                ctx_len=np.array([5000, 2100, 17], dtype=np.int32))
+    for window in (0, 4500):
+        ws = lib.tree_verify_attn_workspace_size(x.B, x.N, x.Hq, x.Hkv, x.D, x.max_ctx_len, window)
+        assert ws > 0, "partials in use"
+        assert _nsplit_host(x, window) >= 2
+        check_full(lib, x, window, f"fp32 rows=80 W={window}")

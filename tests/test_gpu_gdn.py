@@ -84,3 +84,84 @@ def test_deterministic(lib):
     a = run(lib, x)
     b = run(lib, x)
     assert torch.equal(a, b)
+
+
+def _gate_nodes(parent_b):
+    """A root (parent -1) with children, an interior node (parent >= 0, with
+    children) and a leaf, the deepest of each kind."""
+    N = len(parent_b)
+    kids = np.zeros(N, dtype=int)
+    for t in range(N):
+        if parent_b[t] >= 0:
+            kids[parent_b[t]] += 1
+    depth = np.zeros(N, dtype=int)
+    for t in range(N):
+        depth[t] = 1 if parent_b[t] < 0 else depth[parent_b[t]] + 1
+    roots = [t for t in range(N) if parent_b[t] < 0 and kids[t] > 0]
+    inner = [t for t in range(N) if parent_b[t] >= 0 and kids[t] > 0]
+    leaves = [t for t in range(N) if kids[t] == 0 and parent_b[t] >= 0]
+    pick = lambda s: max(s, key=lambda t: (depth[t], t))
+    return pick(roots), pick(inner), pick(leaves)
+
+
+def _root_path(parent_b, t):
+    path = []
+    while t >= 0:
+        path.append(t)
+        t = int(parent_b[t])
+    return path[::-1]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("where", ["root", "interior", "leaf", "all", "underflow"])
+def test_zero_and_underflowing_gates(lib, dtype, where):
+    """Gates exactly 0 (a gate exp(g) that underflowed) at a root, an interior
+    node and a leaf, and gates of 1e-30 along deep paths so that the gate
+    products underflow fp32: every output stays finite and within tolerance
+    of the recurrence, and the commit over a path through those nodes agrees
+    with the oracle too (DFlash-TfM summary, section 3: the state follows the
+    recurrence whatever the gate)."""
+    x = W.gdn_inputs(54, B=3, N=40, H=4, Dk=128, Dv=128, tree="spine_first", dtype=dtype,
+                     device=DEV, s0_std=0.5)
+    alpha = x.alpha.cpu().numpy()
+    acc = np.full((x.B, x.N), -1, dtype=np.int32)
+    na = np.zeros(x.B, dtype=np.int32)
+    for b in range(x.B):
+        par = x.trees.parent[b]
+        root, inner, leaf = _gate_nodes(par)
+        if where == "underflow":
+            # three tiny gates on the leaf's path (product 1e-90), heads 0 and 2
+            for t in _root_path(par, leaf)[-3:]:
+                alpha[b, t, 0::2] = 1e-30
+            alpha[b, ::5, 1] = 1e-30
+            target = leaf
+        else:
+            chosen = {"root": [root], "interior": [inner], "leaf": [leaf],
+                      "all": [root, inner, leaf]}[where]
+            for t in chosen:
+                alpha[b, t, :] = 0.0
+            # one head keeps one nonzero gate per chosen node: mixed heads
+            alpha[b, chosen[0], 3] = 0.5
+            # the commit follows the deepest path through the first chosen node
+            through = [t for t in range(x.N) if chosen[0] in _root_path(par, t)]
+            target = max(through, key=lambda t: (len(_root_path(par, t)), t))
+        path = _root_path(par, target)
+        acc[b, :len(path)] = path
+        na[b] = len(path)
+    x.alpha.copy_(torch.from_numpy(alpha).to(DEV))
+    say(f"gdn gates {where} dtype={dtype}")
+    out = run_checked(lib, x)
+    assert torch.isfinite(out).all()
+    ref = OG.gdn_tree(np64(x.q), np64(x.k), np64(x.v), np64(x.alpha), np64(x.beta), np64(x.S0),
+                      x.trees.parent)
+    err = rel_err(np64(out), ref)
+    say(f"   verify err={err:.3e}")
+    assert err <= tol_for(dtype), err
+    S = lib.tree_gdn_commit(x.k, x.v, x.alpha, x.beta, x.S0, torch.from_numpy(acc).to(DEV),
+                            torch.from_numpy(na).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(S).all()
+    refS = OG.gdn_commit(np64(x.k), np64(x.v), np64(x.alpha), np64(x.beta), np64(x.S0), acc, na)
+    serr = rel_err(np64(S), refS)
+    say(f"   commit err={serr:.3e}")
+    assert serr <= 1e-4, serr

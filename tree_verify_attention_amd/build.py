@@ -27,28 +27,52 @@ def hipcc() -> str:
 
 def flags() -> list:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Wall", "-Wno-unused-result",
         # keep the compiler from emitting packed fp32 arithmetic
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     ]
 
 
+def _compile(src: str, obj: str, verbose: bool):
+    cmd = [hipcc(), *flags(), "-c", "-o", obj, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel, one process per file),
+    then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
+    # only show warnings that are not the host pass ignoring the target feature
+    noise = "is not a recognized feature for this target"
+    failed = False
+    for r in results:
+        msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and noise not in ln]
+        if r.returncode != 0:
+            failed = True
+            sys.stderr.write("\n".join(msgs) + "\n")
+        elif msgs and verbose:
+            print("\n".join(msgs))
+    if failed:
+        raise RuntimeError("HIP build failed")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), "-o", tmp, *srcs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("HIP build failed")
-    # only show warnings that are not the host pass ignoring the target feature
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and noise not in ln]
-    if msgs and verbose:
-        print("\n".join(msgs))
+        raise RuntimeError("HIP link failed")
     os.replace(tmp, LIB)
     return LIB
 

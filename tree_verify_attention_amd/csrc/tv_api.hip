@@ -92,6 +92,11 @@ tv_status tree_gdn_verify(const void* q, const void* k, const void* v, const flo
   if (B < 1 || N < 1 || H < 1 || Dk < 1 || Dv < 1) return TV_ERR_SHAPE;
   if (!dtype_ok(dtype) || !out_dtype_ok(dtype, out_dtype)) return TV_ERR_UNSUPPORTED;
   if (N > TV_GDN_MAX_NODES || Dk != 128 || Dv != 128) return TV_ERR_UNSUPPORTED;
+  // rows of q, k, v, the state and the output move in 16-byte pieces
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(S0) |
+                          reinterpret_cast<uintptr_t>(out);
+  if (align & 15u) return TV_ERR_UNSUPPORTED;
   return launched(tv::launch_gdn(q, k, v, alpha, beta, S0, anc_mask, B, N, H, Dk, Dv, dtype,
                                  out_dtype, out, as_stream(stream)));
 }

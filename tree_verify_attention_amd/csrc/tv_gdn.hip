@@ -265,6 +265,45 @@ __global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
   }
 }
 
+// Product of the gates over an ancestor set, exact at zero gates and free of
+// underflow: the number of zero gates, and the product of the others as
+// mant * 2^ex with |mant| in [0.5, 1).  Gates are multiplied in increasing node
+// order, so a node's running product passes through its ancestors' products
+// bit for bit and a ratio of two of them is the segment's product to within
+// a few ulp.
+struct GateProd {
+  int zeros;
+  int ex;
+  float mant;
+  __device__ float value() const { return zeros ? 0.0f : ldexpf(mant, ex); }
+};
+
+__device__ __forceinline__ GateProd gate_product(const float* alpha, uint64_t set) {
+  GateProd g{0, 0, 1.0f};
+  while (set) {
+    const float a = alpha[__ffsll(static_cast<unsigned long long>(set)) - 1];
+    set &= set - 1;
+    if (a == 0.0f) {
+      ++g.zeros;
+    } else {
+      int ea, em;
+      g.mant *= frexpf(a, &ea);
+      g.mant = frexpf(g.mant, &em);
+      g.ex += ea + em;
+    }
+  }
+  return g;
+}
+
+// gamma_t / gamma_i for i an ancestor of t (or t): the product of the gates
+// strictly below i down to t; 0 when one of them is 0
+__device__ __forceinline__ float gate_ratio(const int* zc, const float* mant, const float* rmant,
+                                            const int* ex, int t, int i) {
+  if (t == i) return 1.0f;
+  if (zc[t] != zc[i]) return 0.0f;
+  return ldexpf(mant[t] * rmant[i], ex[t] - ex[i]);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 inputs: the dense products on MFMA, one workgroup per (sequence, head).
 //
@@ -318,10 +357,11 @@ __host__ __device__ inline size_t gdn_r2_bytes(int np) { return 2 * static_cast<
 size_t gdn_mfma_lds_bytes(int N) {
   const int np = (N + 15) / 16 * 16;
   // region 1; [Q; K]; V, later the right-hand side (fp32); M (fp32); alpha,
-  // beta, gamma, log2 gamma, depth, ancestor words.  Up to 32 nodes this is
-  // 72 KB, so two workgroups fit a CU.
+  // beta, gamma, the gate-product mantissa and its reciprocal, depth, zero
+  // count, exponent, ancestor words.  Up to 32 nodes this is 73 KB, so two
+  // workgroups fit a CU.
   return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 +
-         static_cast<size_t>(np) * (np + 4) * 4 + 64 * 4 * 5 + 64 * 8;
+         static_cast<size_t>(np) * (np + 4) * 4 + 64 * 4 * 8 + 64 * 8;
 }
 
 // One 16 x 16 tile (row tile rt, column tile ct) of C = A B (+ D), NP x NP
@@ -382,9 +422,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   float* s_alpha = s_m + NP * MP;
   float* s_beta = s_alpha + 64;
   float* s_gam = s_beta + 64;
-  float* s_lgam = s_gam + 64;
-  int* s_depth = reinterpret_cast<int*>(s_lgam + 64);
-  uint64_t* s_anc = reinterpret_cast<uint64_t*>(s_depth + 64);
+  float* s_mant = s_gam + 64;   // gate product over nonzero gates: mantissa,
+  float* s_rmant = s_mant + 64; // its reciprocal,
+  int* s_depth = reinterpret_cast<int*>(s_rmant + 64);
+  int* s_zc = s_depth + 64;     // zero gates on the root path,
+  int* s_ex = s_zc + 64;        // and the binary exponent of the product
+  uint64_t* s_anc = reinterpret_cast<uint64_t*>(s_ex + 64);
   __shared__ int s_maxdepth;
 
   const int bh = blockIdx.x;
@@ -473,20 +516,15 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   };
   s0_issue(0, 3);
   if (tid < 64) {
-    // gamma_t = product of alpha over t's root path; its log2 gives the gate
-    // ratio gamma_t / gamma_i of any ancestor i without a path walk (and
-    // without underflow when the product is tiny)
+    // gamma_t = product of alpha over t's root path, kept as a count of zero
+    // gates and the product of the others as mantissa * 2^exponent
     const int t = tid;
-    uint64_t m = s_anc[t];
-    float gm = 1.0f, lg2 = 0.0f;
-    while (m) {
-      const float a = s_alpha[__ffsll(static_cast<unsigned long long>(m)) - 1];
-      gm *= a;
-      lg2 += __log2f(a);
-      m &= m - 1;
-    }
-    s_gam[t] = gm;
-    s_lgam[t] = lg2;
+    const GateProd gp = gate_product(s_alpha, s_anc[t]);
+    s_gam[t] = gp.value();
+    s_mant[t] = gp.mant;
+    s_rmant[t] = 1.0f / gp.mant;
+    s_zc[t] = gp.zeros;
+    s_ex[t] = gp.ex;
     const int dpt = __popcll(s_anc[t]);
     s_depth[t] = dpt;
     if (t < N) atomicMax(&s_maxdepth, dpt);
@@ -534,14 +572,14 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
           const int t = row;
           float y = 0.0f;
           if (t < N && i < N && ((s_anc[t] >> i) & 1ull))
-            y = __builtin_amdgcn_exp2f(s_lgam[t] - s_lgam[i]) * gram[m][r];
+            y = gate_ratio(s_zc, s_mant, s_rmant, s_ex, t, i) * gram[m][r];
           s_y[t * MP + i] = y;
         } else {
           // a key row: X over strict ancestors
           const int t = row - NP;
           float x = 0.0f;
           if (t < N && i < N && i != t && ((s_anc[t] >> i) & 1ull))
-            x = s_beta[t] * __builtin_amdgcn_exp2f(s_lgam[t] - s_lgam[i]) * gram[m][r];
+            x = s_beta[t] * gate_ratio(s_zc, s_mant, s_rmant, s_ex, t, i) * gram[m][r];
           s_x[t * MP + i] = x;
         }
       }
