@@ -40,7 +40,8 @@ typedef enum {
   TV_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes              */
   TV_ERR_UNSUPPORTED = 3, /* sizes or dtype outside the supported set        */
   TV_ERR_WORKSPACE = 4,   /* workspace pointer NULL or smaller than required */
-  TV_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch        */
+  TV_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch        */
+  TV_ERR_SCRATCH = 6      /* input larger than the library's static scratch  */
 } tv_status;
 
 typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -204,6 +205,31 @@ tv_status tree_walk_accept(const int32_t* tokens, const int32_t* parent,
                            int32_t* accepted_nodes, int32_t* num_accepted,
                            void* workspace, size_t workspace_bytes,
                            tv_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tree_walk_accept_noalloc — tree_walk_accept for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.
+ *
+ * Same arguments (without the workspace) and the same results as
+ * tree_walk_accept.  The per-row argmax goes to a static device array of
+ * TV_WALK_NOALLOC_MAX_ROWS int32 (1 MiB) inside the library; each GPU the
+ * library runs on holds its own copy until the process ends.  The call
+ * allocates nothing: its first call on a device only looks up that array's
+ * device address (hipGetSymbolAddress) and keeps it.  Every row is written
+ * before it is read, so the array's contents from earlier calls do not
+ * matter.  Calls that overlap on one GPU (other streams, other host threads)
+ * share the array and race: serialise them.
+ * B * (N + 1) > TV_WALK_NOALLOC_MAX_ROWS returns TV_ERR_SCRATCH before
+ * anything is launched.
+ * ------------------------------------------------------------------------ */
+#define TV_WALK_NOALLOC_MAX_ROWS 262144
+
+tv_status tree_walk_accept_noalloc(const int32_t* tokens, const int32_t* parent,
+                                   const void* logits, int32_t B, int32_t N, int32_t V,
+                                   tv_dtype dtype, int32_t* accepted_tokens,
+                                   int32_t* accepted_nodes, int32_t* num_accepted,
+                                   tv_stream stream);
 
 /* ------------------------------------------------------------------------
  * tree_gdn_commit — the Gated DeltaNet state after the walk.

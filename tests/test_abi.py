@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert tv.status_string(code)
     assert tv.status_string(99) == "unknown status"
 
@@ -140,6 +140,30 @@ def test_walk_validation(lib):
     assert f(*bad) == tv.TV_ERR_WORKSPACE
     bad = list(base); bad[10] = None
     assert f(*bad) == tv.TV_ERR_WORKSPACE
+
+
+def test_walk_noalloc_validation(lib):
+    """The allocation-free walk checks its arguments like tree_walk_accept and
+    rejects inputs larger than its static scratch before any HIP call."""
+    f = lib.tree_walk_accept_noalloc
+    base = [FAKE, FAKE, FAKE, 4, 32, 1000, tv.TV_F32, FAKE, FAKE, FAKE, None]
+    bad = list(base); bad[0] = None
+    assert f(*bad) == tv.TV_ERR_NULL
+    bad = list(base); bad[9] = None
+    assert f(*bad) == tv.TV_ERR_NULL
+    bad = list(base); bad[3] = 0
+    assert f(*bad) == tv.TV_ERR_SHAPE
+    bad = list(base); bad[4] = 129
+    assert f(*bad) == tv.TV_ERR_UNSUPPORTED
+    bad = list(base); bad[6] = 5
+    assert f(*bad) == tv.TV_ERR_UNSUPPORTED
+    # B * (N + 1) one past the scratch's rows, and far past it
+    bad = list(base); bad[3] = tv.WALK_NOALLOC_MAX_ROWS // 33 + 1; bad[4] = 32
+    assert bad[3] * 33 > tv.WALK_NOALLOC_MAX_ROWS
+    assert f(*bad) == tv.TV_ERR_SCRATCH
+    bad = list(base); bad[3] = 1 << 30; bad[4] = 128
+    assert f(*bad) == tv.TV_ERR_SCRATCH
+    assert tv.status_string(tv.TV_ERR_SCRATCH) != "unknown status"
 
 
 def test_gdn_commit_validation(lib):

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtreeverify.so")
 
-TV_OK, TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_LAUNCH = range(6)
+TV_OK, TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_LAUNCH, TV_ERR_SCRATCH = range(7)
 TV_F32, TV_BF16 = 0, 1
 TV_TREE_OK, TV_TREE_BAD_PARENT, TV_TREE_BAD_DEPTH, TV_TREE_BAD_CTX = range(4)
 MAX_NODES = 128      # mask, attention, walk, KV commit
@@ -34,7 +34,9 @@ EXPORTS = (
     "tree_mask_build", "tree_verify_attn_workspace_size", "tree_verify_attn",
     "tree_gdn_verify", "tree_walk_accept_workspace_size", "tree_walk_accept",
     "tree_gdn_commit", "tree_kv_commit", "tree_draft_topk", "tree_build", "tv_status_string",
+    "tree_walk_accept_noalloc",
 )
+WALK_NOALLOC_MAX_ROWS = 262144  # B * (N + 1) at most for tree_walk_accept_noalloc
 
 _lib = None
 
@@ -67,6 +69,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tree_walk_accept_workspace_size.restype = Z
     lib.tree_walk_accept.argtypes = [P, P, P, I, I, I, S, P, P, P, P, Z, P]
     lib.tree_walk_accept.restype = S
+    lib.tree_walk_accept_noalloc.argtypes = [P, P, P, I, I, I, S, P, P, P, P]
+    lib.tree_walk_accept_noalloc.restype = S
     lib.tree_gdn_commit.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, S, P, P]
     lib.tree_gdn_commit.restype = S
     lib.tree_kv_commit.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, S, P, P, P]
@@ -248,6 +252,29 @@ def tree_walk_accept(tokens, parent, logits, out=None, workspace=None) -> dict:
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(dev))
     _check("tree_walk_accept", code)
+    return out
+
+
+def tree_walk_accept_noalloc(tokens, parent, logits, out=None) -> dict:
+    """tree_walk_accept with the library's static scratch instead of a
+    workspace (B * (N + 1) <= WALK_NOALLOC_MAX_ROWS); the library allocates
+    nothing.  Outputs are allocated here only when `out` is not given."""
+    lib = load()
+    dev = tokens.device
+    B, N = tokens.shape
+    V = logits.shape[-1]
+    _need(tokens, "tokens", torch.int32, dev)
+    _need(parent, "parent", torch.int32, dev, (B, N))
+    _need(logits, "logits", logits.dtype, dev, (B, N + 1, V))
+    if out is None:
+        out = dict(accepted_tokens=torch.empty(B, N + 1, dtype=torch.int32, device=dev),
+                   accepted_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
+                   num_accepted=torch.empty(B, dtype=torch.int32, device=dev))
+    code = lib.tree_walk_accept_noalloc(_ptr(tokens), _ptr(parent), _ptr(logits), B, N, V,
+                                        _dtype_code(logits.dtype), _ptr(out["accepted_tokens"]),
+                                        _ptr(out["accepted_nodes"]), _ptr(out["num_accepted"]),
+                                        _stream(dev))
+    _check("tree_walk_accept_noalloc", code)
     return out
 
 

@@ -29,6 +29,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_UNSUPPORTED: return "sizes or dtype outside the supported set";
     case TV_ERR_WORKSPACE: return "workspace missing or too small";
     case TV_ERR_LAUNCH: return "kernel launch failed";
+    case TV_ERR_SCRATCH: return "input larger than the library's static scratch";
   }
   return "unknown status";
 }
@@ -184,6 +185,21 @@ tv_status tree_walk_accept(const int32_t* tokens, const int32_t* parent, const v
   return launched(tv::launch_walk(tokens, parent, logits, B, N, V, dtype, accepted_tokens,
                                   accepted_nodes, num_accepted, static_cast<int32_t*>(workspace),
                                   as_stream(stream)));
+}
+
+tv_status tree_walk_accept_noalloc(const int32_t* tokens, const int32_t* parent,
+                                   const void* logits, int32_t B, int32_t N, int32_t V,
+                                   tv_dtype dtype, int32_t* accepted_tokens,
+                                   int32_t* accepted_nodes, int32_t* num_accepted,
+                                   tv_stream stream) {
+  if (!tokens || !parent || !logits || !accepted_tokens || !accepted_nodes || !num_accepted)
+    return TV_ERR_NULL;
+  if (B < 1 || N < 1 || V < 1) return TV_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return TV_ERR_UNSUPPORTED;
+  if (N > TV_MAX_NODES) return TV_ERR_UNSUPPORTED;
+  if (static_cast<long long>(B) * (N + 1) > TV_WALK_NOALLOC_MAX_ROWS) return TV_ERR_SCRATCH;
+  return launched(tv::launch_walk_noalloc(tokens, parent, logits, B, N, V, dtype, accepted_tokens,
+                                          accepted_nodes, num_accepted, as_stream(stream)));
 }
 
 }  // extern "C"

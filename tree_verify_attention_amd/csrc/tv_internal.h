@@ -51,6 +51,10 @@ hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void*
                        int N, int V, tv_dtype dtype, int32_t* acc_tok, int32_t* acc_node,
                        int32_t* num_acc, int32_t* argmax_ws, hipStream_t stream);
 
+hipError_t launch_walk_noalloc(const int32_t* tokens, const int32_t* parent, const void* logits,
+                               int B, int N, int V, tv_dtype dtype, int32_t* acc_tok,
+                               int32_t* acc_node, int32_t* num_acc, hipStream_t stream);
+
 hipError_t launch_draft_topk(const void* logits, int B, int L, int V, int K, tv_dtype dtype,
                              int32_t* cand_tok, float* cand_lp, hipStream_t stream);
 

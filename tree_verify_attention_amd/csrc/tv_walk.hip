@@ -6,6 +6,8 @@
 // matches.  Two kernels: a row argmax over the vocabulary (an HBM stream, one
 // workgroup per logits row), then one wave per tree that walks the parent
 // pointers (lanes = nodes; ballots find the matching child each step).
+#include <atomic>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -180,6 +182,42 @@ __global__ __launch_bounds__(64) void walk_kernel(const int32_t* __restrict__ to
 
 }  // namespace
 
+namespace {
+
+// Argmax scratch of the allocation-free walk: one int32 per logits row.  Each
+// GPU holds its own copy until the process ends.  Host code never passes this
+// name to a kernel (on the host it is a stand-in, not a device address); it
+// uses the per-device address from hipGetSymbolAddress below.
+static __device__ __align__(256) int32_t scratch[TV_WALK_NOALLOC_MAX_ROWS];
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> scratch_ptr[kMaxDevices];  // device address per device id
+
+// The device address of this device's scratch, looked up once per device
+// (with that device current) and kept.
+hipError_t scratch_address(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    int32_t* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) {
+      *out = p;
+      return hipSuccess;
+    }
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (ptr == nullptr) return hipErrorInvalidSymbol;
+  if (cached) scratch_ptr[dev].store(static_cast<int32_t*>(ptr), std::memory_order_release);
+  *out = static_cast<int32_t*>(ptr);
+  return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void* logits, int B,
                        int N, int V, tv_dtype dtype, int32_t* acc_tok, int32_t* acc_node,
                        int32_t* num_acc, int32_t* argmax_ws, hipStream_t stream) {
@@ -195,6 +233,18 @@ hipError_t launch_walk(const int32_t* tokens, const int32_t* parent, const void*
   hipLaunchKernelGGL(walk_kernel, dim3(B), dim3(64), 0, stream, tokens, parent, argmax_ws, N,
                      acc_tok, acc_node, num_acc);
   return hipGetLastError();
+}
+
+// The walk with the static scratch: every row's argmax is written before the
+// walk reads it, so the array's earlier contents do not matter.  The caller
+// has checked B * (N + 1) <= TV_WALK_NOALLOC_MAX_ROWS.
+hipError_t launch_walk_noalloc(const int32_t* tokens, const int32_t* parent, const void* logits,
+                               int B, int N, int V, tv_dtype dtype, int32_t* acc_tok,
+                               int32_t* acc_node, int32_t* num_acc, hipStream_t stream) {
+  int32_t* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_walk(tokens, parent, logits, B, N, V, dtype, acc_tok, acc_node, num_acc, ws, stream);
 }
 
 }  // namespace tv
