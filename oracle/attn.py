@@ -22,15 +22,12 @@ BLOCK = 16
 
 
 def context_kv(k_cache, v_cache, block_table_b, g, ctx):
-    """Gather the ctx context keys/values of one sequence and kv head by
-    following the block table page by page."""
-    D = k_cache.shape[-1]
-    K = np.empty((ctx, D), dtype=np.float64)
-    V = np.empty((ctx, D), dtype=np.float64)
-    for j in range(ctx):
-        page = int(block_table_b[j // BLOCK])
-        K[j] = k_cache[page, g, j % BLOCK]
-        V[j] = v_cache[page, g, j % BLOCK]
+    """Gather the ctx context keys/values of one sequence and kv head: position
+    j lives in page block_table_b[j // 16], slot j % 16."""
+    j = np.arange(ctx)
+    pages = np.asarray(block_table_b)[j // BLOCK].astype(np.int64)
+    K = np.asarray(k_cache[pages, g, j % BLOCK], dtype=np.float64).reshape(ctx, -1)
+    V = np.asarray(v_cache[pages, g, j % BLOCK], dtype=np.float64).reshape(ctx, -1)
     return K, V
 
 
@@ -46,29 +43,33 @@ def visible_keys(p, ctx, vis_t, pos_nodes, window):
     return ctx_vis, node_vis
 
 
-def attend(qvec, K, V, visible, scale):
-    """softmax(scale * K q) over the visible keys, then the weighted sum of V."""
-    s = scale * (K[visible] @ qvec)
-    s = s - s.max()
-    w = np.exp(s)
-    w = w / w.sum()
-    return w @ V[visible]
-
-
 def tree_attn_group(q_g, Kc, Vc, Kn, Vn, vis, pos, window, scale, nodes=None):
     """One (sequence, kv head): q_g [N, G, D] (the G query heads of the
     group), Kc/Vc [ctx, D] context, Kn/Vn [N, D] node keys/values, vis [N, N],
-    pos [N].  Returns [N, G, D]; rows not in ``nodes`` are left as NaN."""
+    pos [N].  Returns [N, G, D]; rows not in ``nodes`` are left as NaN.
+
+    Every query row (node t, head) takes the softmax of scale * <q, k> over
+    the keys visible to t (``visible_keys``) and the weighted sum of their
+    values; all rows of the group are written as one score matrix with the
+    invisible keys at -inf.  Keys that no row sees are left out of it."""
     N, G, D = q_g.shape
     ctx = Kc.shape[0]
     out = np.full((N, G, D), np.nan)
+    rows = list(range(N)) if nodes is None else list(nodes)
+    if not rows:
+        return out
     K = np.concatenate([Kc, Kn], axis=0)
     V = np.concatenate([Vc, Vn], axis=0)
-    for t in (range(N) if nodes is None else nodes):
-        cv, nv = visible_keys(int(pos[t]), ctx, vis[t], pos, window)
-        visible = np.concatenate([cv, nv])
-        for hl in range(G):
-            out[t, hl] = attend(q_g[t, hl], K, V, visible, scale)
+    allowed = np.stack([np.concatenate(visible_keys(int(pos[t]), ctx, vis[t], pos, window))
+                        for t in rows])                            # [R, ctx + N]
+    cols = np.flatnonzero(allowed.any(axis=0))
+    Q = np.asarray(q_g, dtype=np.float64)[rows].reshape(len(rows) * G, D)
+    s = scale * (Q @ K[cols].T)                                    # [R * G, C]
+    s = np.where(np.repeat(allowed[:, cols], G, axis=0), s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    w = np.exp(s)
+    w = w / w.sum(axis=1, keepdims=True)
+    out[rows] = (w @ V[cols]).reshape(len(rows), G, D)
     return out
 
 
