@@ -1,19 +1,26 @@
-"""Benchmark of one tree-verify step on one MI355X.
+"""Benchmark of the tree-verify path on one MI355X.
 
-A step is one pass of the whole verify path over one batch: tree_mask_build,
-tree_verify_attn for a 512-token sliding-window layer and for a global layer,
-tree_walk_accept and tree_gdn_verify.  The batch is the mixed workload: 32
-sequences with context lengths uniform in [1024, 32768], random spine-first
-trees of N = 32 nodes (max depth 8), Hq = 16, Hkv = 8, D = 256, bf16, paged
-KV in 16-token pages under a random block table.  That workload states no
-vocabulary or GDN shape, so the walk runs over [32, 33, 262144] bf16 logits
-(the DDTree workload's vocabulary) and the GDN layer uses H = 16,
-Dk = Dv = 128 over the same trees.
+Headline step: one pass of every step of the verify path over the mixed
+workload (32 sequences with context lengths uniform in [1024, 32768], random
+spine-first trees of N = 32 nodes of max depth 8, Hq = 16, Hkv = 8, D = 256,
+bf16, paged KV in 16-token pages under a random block table):
+tree_mask_build, tree_verify_attn for a 512-token sliding-window layer and for
+a global layer, tree_walk_accept over [32, 33, 262144] bf16 logits (the DDTree
+workload's vocabulary; the mixed workload names none) and tree_gdn_verify with
+H = 16, Dk = Dv = 128 over the same trees.  `value` is verified tree nodes per
+second (B * N per step) over K back-to-back steps with inputs resident in HBM.
 
-Prints one JSON line: verified tree nodes per second (B * N per step), the
-roofline of the dominant kernel (the global-layer attention: context K/V bytes
-over its event-timed duration against 8 TB/s) and the CPU oracle on a bounded
-sample of the same step.
+`configs` times each of the five workloads as its own step (c1: mask +
+attention + walk; c2: mask + attention; c3: mask + window layer + global layer;
+c4: mask + attention + walk; c5: mask + GDN), every call separately: a 1 GiB
+buffer is written and a 512 MiB one read before each repetition (outside the
+timed region, so that L2 and the 256 MB last-level cache hold none of the
+call's inputs and no dirty lines), and the
+median, 10th and 90th percentile of the event-timed durations are reported,
+with each workload's roofline.  `stream_ceiling` is the read rate a plain
+streaming kernel reaches on the device, printed beside the vendor's 8 TB/s.
+`cpu_baseline` is the oracle on a bounded sample of the headline step on the
+host's cores, and with one thread.
 """
 from __future__ import annotations
 
@@ -31,6 +38,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of the MI355X
+
+
+def log(msg: str):
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -43,7 +56,15 @@ def parse():
                     help="skip the cost curve over tree sizes and the tree-construction timing "
                          "(the curve's attention calls share kernel names with the step's, which "
                          "muddles a kernel trace of the step)")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16,
+                    help="sequences of the headline step the oracle runs on all host cores")
+    ap.add_argument("--cpu-1t-seqs", type=int, default=8,
+                    help="sequences of the headline step the oracle runs on one thread")
+    ap.add_argument("--reps", type=int, default=50, help="timed repetitions per call in `configs`")
+    ap.add_argument("--rep-warmup", type=int, default=10, help="untimed repetitions per call in `configs`")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB written before each repetition in `configs` (0: no flush)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload timing")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per global-layer attention call (rocprofv3 --pmc)")
     ap.add_argument("--attn-only", type=int, default=0, choices=[0, 2, 4],
@@ -311,51 +332,325 @@ def cost_curve(step: Step, dev, reps: int) -> dict:
     return res
 
 
-def cpu_baseline(step: Step, nseq: int):
-    """The oracle on the first `nseq` sequences of the same step (mask, both
-    attention layers, walk, GDN), timed on this host's cores."""
-    from oracle import attn as OA, gdn as OG, mask as OM, walk as OW
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+def _probe_lib():
+    import ctypes
+    from tree_verify_attention_amd.build import PROBE_LIB
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.tv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.tv_probe_stream_read.restype = ctypes.c_int
+    return lib
+
+
+class Flusher:
+    """Run before each timed repetition, on the same stream and outside the
+    timed events: write a 1 GiB (by default) buffer, then read another half
+    as large.  The write evicts the call's inputs from L2 and the 256 MB
+    last-level cache; the read replaces the write's dirty lines with clean
+    ones, so that the timed call does not pay for writing them back."""
+
+    def __init__(self, dev, mib: int):
+        import ctypes
+        self.buf = torch.empty(max(mib, 0) << 20, dtype=torch.uint8, device=dev) if mib > 0 else None
+        if self.buf is not None:
+            self.rd = torch.empty(max(mib, 0) << 19, dtype=torch.uint8, device=dev).fill_(5)
+            self.sink = torch.empty(1 << 14, dtype=torch.int32, device=dev)
+            self.lib = _probe_lib()
+            self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+            self.args = (ctypes.c_void_p(self.rd.data_ptr()), self.rd.numel(), ctypes.c_void_p(self.sink.data_ptr()),
+                         1 << 14, self.stream)
+        self.k = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.k ^= 1
+            self.buf.fill_(self.k)
+            assert self.lib.tv_probe_stream_read(*self.args) == 0
+
+
+def time_calls(calls, reps: int, warmup: int, flush: Flusher) -> dict:
+    """calls: [(name, fn)] issued in order as one step.  Each repetition
+    flushes before every call and brackets the call with events on the
+    current stream.  Returns median, p10, p90 and mean per call in ms."""
+    for _ in range(warmup):
+        for _, fn in calls:
+            flush()
+            fn()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(reps)]
+    for r in range(reps):
+        for c, (_, fn) in enumerate(calls):
+            flush()
+            ev[r][c][0].record()
+            fn()
+            ev[r][c][1].record()
+    torch.cuda.synchronize()
+    out = {}
+    for c, (name, _) in enumerate(calls):
+        t = np.array([ev[r][c][0].elapsed_time(ev[r][c][1]) for r in range(reps)])
+        out[name] = {"median_ms": round(float(np.median(t)), 5), "p10_ms": round(float(np.percentile(t, 10)), 5),
+                     "p90_ms": round(float(np.percentile(t, 90)), 5), "mean_ms": round(float(t.mean()), 5)}
+    return out
+
+
+def _kv_bytes(x, window: int) -> int:
+    """Algorithmic context K+V bytes of one attention call: the union of the
+    context positions the nodes can see (all of them without a window; the
+    last window - 1 with one), 2 * Hkv * D elements each."""
+    ctx = x.ctx_len.cpu().numpy().astype(np.int64)
+    seen = np.minimum(ctx, window - 1) if window > 0 else ctx
+    return int(seen.sum()) * 2 * x.Hkv * x.D * x.k_cache.element_size()
+
+
+def _attn_flops(x) -> float:
+    """QK^T and P.V over the context keys: 4 flops per (key, query row, dim)."""
+    return 4.0 * float(x.ctx_len.cpu().numpy().astype(np.int64).sum()) * x.Hq * x.N * x.D
+
+
+def _gbps(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def _hbm_roof(kernel, nbytes, ms, ceiling):
+    a = _gbps(nbytes, ms)
+    r = {"kernel": kernel, "bound": "hbm", "algorithmic_bytes": int(nbytes), "achieved": round(a, 1),
+         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4)}
+    if ceiling:
+        r["frac_of_measured_ceiling"] = round(a / ceiling, 4)
+    return r
+
+
+def _mask_call(tv, parent, ctx_len, B, N, dev):
+    mo = dict(anc=torch.empty(B, N, tv.anc_words(N), dtype=torch.int64, device=dev),
+              depth=torch.empty(B, N, dtype=torch.int32, device=dev),
+              pos=torch.empty(B, N, dtype=torch.int32, device=dev),
+              status=torch.empty(B, dtype=torch.int32, device=dev), dense_bias=None)
+    tv.tree_mask_build(parent, ctx_len, out=mo)
+    return mo, (lambda: tv.tree_mask_build(parent, ctx_len, out=mo))
+
+
+def _attn_call(tv, x, mo, window, dev):
+    out = torch.empty_like(x.q)
+    n = tv.tree_verify_attn_workspace_size(x.B, x.N, x.Hq, x.Hkv, x.D, x.max_ctx_len, window)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    return lambda: tv.tree_verify_attn(x.q, x.k_node, x.v_node, x.k_cache, x.v_cache, x.block_table,
+                                       x.ctx_len, x.max_ctx_len, mo["anc"], mo["pos"], window, x.scale,
+                                       out=out, workspace=ws)
+
+
+def _walk_call(tv, trees, logits, dev):
+    B, N = trees.parent.shape
+    tok = torch.from_numpy(trees.tokens).to(dev)
+    par = torch.from_numpy(trees.parent).to(dev)
+    wo = dict(accepted_tokens=torch.empty(B, N + 1, dtype=torch.int32, device=dev),
+              accepted_nodes=torch.empty(B, N, dtype=torch.int32, device=dev),
+              num_accepted=torch.empty(B, dtype=torch.int32, device=dev))
+    ws = torch.empty(tv.tree_walk_accept_workspace_size(B, N), dtype=torch.uint8, device=dev)
+    return lambda: tv.tree_walk_accept(tok, par, logits, out=wo, workspace=ws)
+
+
+def _summary(name, workload, B, N, calls, timing):
+    step = sum(timing[c]["median_ms"] for c, _ in calls)
+    return {"workload": workload, "B": B, "N": N, "calls": timing, "step_ms": round(step, 5),
+            "nodes_per_s": round(B * N / (step * 1e-3), 1)}
+
+
+def per_config(step: Step, dev, args, ceiling) -> dict:
+    """Each workload as its own step, timed call by call (see time_calls)."""
+    import tree_verify_attention_amd as tv
+    from synth import configs as CF
+    from synth import workloads as W
+    flush = Flusher(dev, args.flush_mib)
+    reps, warm = args.reps, args.rep_warmup
+    res = {}
+
+    def attn_cfg(cid, kv_on_device):
+        c = dict(CF.ATTN[cid])
+        wins = c.pop("windows")
+        vocab = c.pop("vocab")
+        x = W.attn_inputs(cid, device=dev, kv_on_device=kv_on_device, vocab=vocab, **c)
+        return x, wins, vocab
+
+    # c1: tiny fp32 step (launch-bound)
+    x, wins, vocab = attn_cfg(1, False)
+    par = torch.from_numpy(x.trees.parent).to(dev)
+    mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
+    logits = W.walk_inputs(1, x.trees, vocab, torch.float32, device=dev).logits
+    calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev)), ("walk", _walk_call(tv, x.trees, logits, dev))]
+    t = time_calls(calls, reps, warm, flush)
+    r = _summary("c1", "B=1, N=16 random-parent tree, Hq=8, Hkv=2, D=64, ctx 512, fp32; logits [1,17,1000] fp32",
+                 x.B, x.N, calls, t)
+    kv = _kv_bytes(x, 0)
+    r["roofline"] = {"bound": "launch", "note": f"{kv} B of context K+V and a 68 KB logits row set: the "
+                     "calls are launch-latency bound", "attn_achieved_GBps": round(_gbps(kv, t["attn"]["median_ms"]), 1)}
+    res["c1"] = r
+    del x, logits, calls
+
+    # c2: leaf-sibling batch, HBM-bound
+    x, wins, vocab = attn_cfg(2, True)
+    par = torch.from_numpy(x.trees.parent).to(dev)
+    mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
+    calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev))]
+    t = time_calls(calls, reps, warm, flush)
+    r = _summary("c2", "B=8, N=32 leaf-sibling trees, Hq=16, Hkv=8, D=256, ctx 4096, bf16", x.B, x.N, calls, t)
+    r["roofline"] = _hbm_roof("tree_verify_attn", _kv_bytes(x, 0), t["attn"]["median_ms"], ceiling)
+    res["c2"] = r
+    del x, calls
+    torch.cuda.empty_cache()
+
+    # c3: the headline step's layers, mask + window layer + global layer
+    xw, xg = step.layers
+    mo, mask = _mask_call(tv, step.parent, step.ctx_len, step.B, step.N, dev)
+    calls = [("mask", mask), ("attn_window", _attn_call(tv, xw, mo, xw.window, dev)),
+             ("attn_global", _attn_call(tv, xg, mo, xg.window, dev))]
+    t = time_calls(calls, reps, warm, flush)
+    r = _summary("c3", "B=32, N=32 spine-first trees, ctx U[1024,32768], Hq=16, Hkv=8, D=256, bf16; "
+                 "W=512 layer + global layer", step.B, step.N, calls, t)
+    bw, bg = _kv_bytes(xw, xw.window), _kv_bytes(xg, 0)
+    tw, tg = t["attn_window"]["median_ms"], t["attn_global"]["median_ms"]
+    r["roofline"] = {"pair": _hbm_roof("tree_verify_attn, window + global layer", bw + bg, tw + tg, ceiling),
+                     "window": _hbm_roof("tree_verify_attn, W=512", bw, tw, ceiling),
+                     "global": _hbm_roof("tree_verify_attn, global", bg, tg, ceiling)}
+    res["c3"] = r
+    del calls
+
+    # c4: DDTree batch, MFMA-bound attention and a 2.18 GB walk
+    x, wins, vocab = attn_cfg(4, True)
+    par = torch.from_numpy(x.trees.parent).to(dev)
+    mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
+    logits = W.walk_inputs(4, x.trees, vocab, torch.bfloat16, device=dev, on_device=True).logits
+    calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev)), ("walk", _walk_call(tv, x.trees, logits, dev))]
+    t = time_calls(calls, reps, warm, flush)
+    r = _summary("c4", "B=64, N=64 DDTree trees, Hq=64, Hkv=8, D=128, ctx 32768, bf16; logits [64,65,262144] bf16",
+                 x.B, x.N, calls, t)
+    fl = _attn_flops(x)
+    ta = t["attn"]["median_ms"]
+    tfl = fl / (ta * 1e-3) / 1e12
+    r["roofline"] = {"attn": {"kernel": "tree_verify_attn (wide-tile)", "bound": "mfma", "algorithmic_flops": fl,
+                              "achieved": round(tfl, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tfl / BF16_MFMA_PEAK_TFLOPS, 4),
+                              "kv_GBps": round(_gbps(_kv_bytes(x, 0), ta), 1)},
+                     "walk": _hbm_roof("tree_walk_accept", logits.numel() * logits.element_size(),
+                                       t["walk"]["median_ms"], ceiling)}
+    res["c4"] = r
+    del x, logits, calls
+    torch.cuda.empty_cache()
+
+    # c5: GDN tree verify
+    g = dict(CF.GDN[5])
+    gx = W.gdn_inputs(5, device=dev, **g)
+    par = torch.from_numpy(gx.trees.parent).to(dev)
+    ctx = torch.full((gx.B,), 1, dtype=torch.int32, device=dev)
+    mo, mask = _mask_call(tv, par, ctx, gx.B, gx.N, dev)
+    gout = torch.empty_like(gx.v)
+    calls = [("mask", mask),
+             ("gdn", lambda: tv.tree_gdn_verify(gx.q, gx.k, gx.v, gx.alpha, gx.beta, gx.S0, mo["anc"], out=gout))]
+    t = time_calls(calls, reps, warm, flush)
+    r = _summary("c5", "B=16, H=16, Dk=Dv=128, N=32 spine-first trees, bf16 q/k/v, fp32 gates and state",
+                 gx.B, gx.N, calls, t)
+    gbytes = sum(z.numel() * z.element_size() for z in (gx.q, gx.k, gx.v, gx.alpha, gx.beta, gx.S0, gout, mo["anc"]))
+    r["roofline"] = _hbm_roof("tree_gdn_verify", gbytes, t["gdn"]["median_ms"], ceiling)
+    res["c5"] = r
+    res["protocol"] = (f"per call: {warm} untimed then {reps} timed repetitions, each after writing "
+                       f"{args.flush_mib} MiB and reading {args.flush_mib // 2} MiB on the same stream "
+                       f"(outside the events); median, p10, p90 of the event-timed durations; "
+                       f"step_ms = sum of the calls' medians")
+    return res
+
+
+def stream_ceiling(dev) -> dict:
+    """The read rate of a plain streaming kernel over 4 GiB (best of a few
+    grid sizes, 10 timed passes each)."""
+    import ctypes
+    lib = _probe_lib()
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev).fill_(3)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    best = None
+    for grid in (1024, 2048, 4096, 8192, 16384):
+        call = lambda: lib.tv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), n,
+                                                ctypes.c_void_p(sink.data_ptr()), grid, stream)
+        for _ in range(2):
+            assert call() == 0
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            call()
+        z.record()
+        torch.cuda.synchronize()
+        gb = _gbps(n, a.elapsed_time(z) / 10)
+        if best is None or gb > best[0]:
+            best = (gb, grid)
+    del buf
+    return {"GBps": round(best[0], 1), "grid": best[1], "bytes": n, "frac_of_8TBps": round(best[0] / HBM_PEAK_GBS, 4),
+            "kernel": "16-byte non-temporal loads, 8 in flight per lane, grid-stride, 256 threads per workgroup"}
+
+
+def _oracle_sample(step: Step, nseq: int):
+    """Host copies of the first nseq sequences of the headline step."""
     b_idx = list(range(nseq))
-    par = step.trees.parent[b_idx]
-    toks = step.trees.tokens[b_idx]
-    # bring the sample's inputs to the host (outside the timed region)
     host = []
     for x in step.layers:
-        G = x.Hq // x.Hkv
         per = []
         for b in b_idx:
             ctx = int(x.ctx_len[b])
             pages = x.block_table[b, :(ctx + 15) // 16].long()
-            kc = x.k_cache[pages].double().cpu().numpy()   # [pages, Hkv, 16, D]
-            vc = x.v_cache[pages].double().cpu().numpy()
+            kc = x.k_cache[pages].float().cpu().numpy()   # [pages, Hkv, 16, D], exact
+            vc = x.v_cache[pages].float().cpu().numpy()
             table = np.arange(len(pages), dtype=np.int64)
             per.append((ctx, kc, vc, table, x.q[b].double().cpu().numpy(), x.k_node[b].double().cpu().numpy(),
                         x.v_node[b].double().cpu().numpy()))
-        host.append((x, G, per))
-    logits = step.logits[b_idx].double().cpu().numpy()
+        host.append((x, per))
     g = step.gdn
-    gin = [t[b_idx].double().cpu().numpy() for t in (g.q, g.k, g.v, g.alpha, g.beta, g.S0)]
-    ctx_np = step.ctx_len.cpu().numpy()[b_idx]
+    return dict(par=step.trees.parent[b_idx], toks=step.trees.tokens[b_idx],
+                ctx=step.ctx_len.cpu().numpy()[b_idx], host=host,
+                logits=step.logits[b_idx].double().cpu().numpy(),
+                gin=[t[b_idx].double().cpu().numpy() for t in (g.q, g.k, g.v, g.alpha, g.beta, g.S0)])
 
+
+def _oracle_step(sm) -> float:
+    """The oracle over the sample: mask, both attention layers, walk, GDN."""
+    from oracle import attn as OA, gdn as OG, mask as OM, walk as OW
     t0 = time.perf_counter()
-    m = OM.tree_mask(par, ctx_np)
-    for x, G, per in host:
+    m = OM.tree_mask(sm["par"], sm["ctx"])
+    for x, per in sm["host"]:
         for i, (ctx, kc, vc, table, q, kn, vn) in enumerate(per):
             OA.tree_attn(q[None], kn[None], vn[None], kc, vc, table[None], np.array([ctx]),
                          m["vis"][i:i + 1], m["pos"][i:i + 1], x.window, x.scale)
-    OW.tree_walk(toks, par, logits)
-    OG.gdn_tree(*gin, par)
-    dt = time.perf_counter() - t0
-    nodes = nseq * step.N
-    return dict(value=nodes / dt, unit="nodes/s", cores=int(threads), kind="oracle",
-                sample=f"first {nseq} of {step.B} sequences of the step (all {step.N} nodes; mask, "
-                       f"window and global attention, walk over 262144-entry rows, GDN), "
-                       f"{dt:.1f} s on {len(os.sched_getaffinity(0))} host cores")
+    OW.tree_walk(sm["toks"], sm["par"], sm["logits"])
+    OG.gdn_tree(*sm["gin"], sm["par"])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(step: Step, nseq: int, nseq_1t: int) -> dict:
+    """The oracle (unchanged) on the first sequences of the headline step, on
+    all host cores and on one thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threadpool_limits = None
+        threads = 1
+    host_cores = len(os.sched_getaffinity(0))
+    sm = _oracle_sample(step, nseq)
+    dt = _oracle_step(sm)
+    what = (f"sequences of the headline step ({step.N} nodes each; mask, window and global attention, "
+            f"walk over 262144-entry rows, GDN)")
+    res = dict(value=round(nseq * step.N / dt, 2), unit="nodes/s", cores=int(threads), kind="oracle",
+               sample=f"first {nseq} of {step.B} {what}: {dt:.1f} s on {threads} BLAS threads "
+                      f"({host_cores} host cores)")
+    if threadpool_limits is not None and 0 < nseq_1t <= nseq:
+        n1 = nseq_1t
+        sm1 = dict(par=sm["par"][:n1], toks=sm["toks"][:n1], ctx=sm["ctx"][:n1], logits=sm["logits"][:n1],
+                   host=[(x, per[:n1]) for x, per in sm["host"]], gin=[t[:n1] for t in sm["gin"]])
+        with threadpool_limits(limits=1):
+            dt1 = _oracle_step(sm1)
+        res["single_thread"] = dict(value=round(nseq_1t * step.N / dt1, 2), unit="nodes/s", cores=1,
+                                    sample=f"first {nseq_1t} of {step.B} {what}: {dt1:.1f} s on one thread")
+    return res
 
 
 def attn_only(args, dev) -> dict:
@@ -409,8 +704,10 @@ def main():
     if args.attn_only:
         print(json.dumps(attn_only(args, dev)), flush=True)
         return
+    log("building the headline step's inputs")
     step = Step(dev)
     torch.cuda.synchronize()
+    log("timing the headline step")
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -474,6 +771,14 @@ def main():
                      "bytes_per_unit": "8192 B of K+V per (context token, sequence): 2 x Hkv 8 x D 256 x 2 B",
                      "call_ms": round(per_call["attn1"], 4)},
     }
+    log("streaming-read ceiling")
+    ceiling = stream_ceiling(dev)
+    out["stream_ceiling"] = ceiling
+    out["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceiling["GBps"], 4)
+    if not args.no_configs:
+        log("per-workload steps c1..c5")
+        out["configs"] = per_config(step, dev, args, ceiling["GBps"])
+    log("commits, cost curve, tree construction")
     out["next_rows"] = next_rows(step, dev, args.steps)
     if not args.no_curve:
         out["next_rows"]["cost_curve"] = cost_curve(step, dev, min(args.steps, 20))
@@ -488,7 +793,8 @@ def main():
         torch.cuda.synchronize()
         out["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_seqs)
+        log("oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_seqs, args.cpu_1t_seqs)
     print(json.dumps(out), flush=True)
 
 

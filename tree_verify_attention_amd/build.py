@@ -13,6 +13,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtreeverify.so")
+# the benchmark's streaming-read probe (not part of the library)
+PROBE_SRC = os.path.join(CSRC, "probe", "tv_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libtvprobe.so")
 SOURCES = ["tv_api.hip", "tv_mask.hip", "tv_walk.hip", "tv_attn.hip", "tv_gdn.hip", "tv_commit.hip",
            "tv_tree.hip"]
 ARCH = os.environ.get("TV_OFFLOAD_ARCH", "gfx950")
@@ -74,6 +77,15 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("HIP link failed")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *flags(), "-shared", "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("probe build failed")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
