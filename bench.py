@@ -276,11 +276,12 @@ def cost_curve(step: Step, dev, reps: int) -> dict:
     N nodes (depth <= 8) and fresh seeded queries and node keys/values for
     each N.  Per N: event-timed mask + window-layer + global-layer attention
     (the verify calls of that workload), averaged over `reps` passes; the
-    least-squares slope gives the cost per extra candidate."""
+    least-squares slope gives the cost per extra candidate.  The GDN layer's
+    tree_gdn_verify over the same trees is timed alongside (gdn_ms)."""
     tv = step.tv
     from synth import workloads as W
     B = step.B
-    res = {"N": [], "ms": [], "mask_ms": [], "window_ms": [], "global_ms": []}
+    res = {"N": [], "ms": [], "mask_ms": [], "window_ms": [], "global_ms": [], "gdn_ms": []}
     for N in CURVE_NODES:
         trees = W.make_trees(3, "spine_first", B, N, 1000, max_depth=min(8, N), tag=1000 + N)
         parent = torch.from_numpy(trees.parent).to(dev)
@@ -322,13 +323,30 @@ def cost_curve(step: Step, dev, reps: int) -> dict:
         res["global_ms"].append(round(float(parts[2]), 4))
         res["ms"].append(round(float(parts.sum()), 4))
         del calls
+        # the GDN layer (H = 16, Dk = Dv = 128, bf16) over the same trees
+        g = W.gdn_inputs(3, B=B, N=N, H=16, Dk=128, Dv=128, tree="spine_first", dtype=torch.bfloat16,
+                         trees=trees, device=dev)
+        gout = torch.empty_like(g.v)
+        gcall = lambda: tv.tree_gdn_verify(g.q, g.k, g.v, g.alpha, g.beta, g.S0, mo["anc"], out=gout)
+        for _ in range(10):
+            gcall()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            gcall()
+        z.record()
+        torch.cuda.synchronize()
+        res["gdn_ms"].append(round(a.elapsed_time(z) / reps, 4))
+        del g, gout
     n = np.array(res["N"], dtype=np.float64)
     t = np.array(res["ms"])
     small = n <= 32
     res["ms_per_candidate_N_le_32"] = round(float(np.polyfit(n[small], t[small], 1)[0]), 5)
     res["ms_per_candidate_all"] = round(float(np.polyfit(n, t, 1)[0]), 5)
     res["workload"] = ("mixed batch (B=32, ctx U[1024,32768], Hq=16, Hkv=8, D=256, bf16) with "
-                       "spine-first trees of N nodes; mask + W=512 layer + global layer")
+                       "spine-first trees of N nodes; ms = mask + W=512 layer + global layer; gdn_ms = "
+                       "tree_gdn_verify with H=16, Dk=Dv=128, bf16, over the same trees (warm calls)")
     return res
 
 

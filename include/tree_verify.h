@@ -57,7 +57,7 @@ enum {
 typedef void* tv_stream;
 
 #define TV_MAX_NODES 128     /* draft nodes per tree (mask, attention, walk, KV commit) */
-#define TV_GDN_MAX_NODES 64  /* draft nodes per tree for the Gated DeltaNet calls       */
+#define TV_GDN_MAX_NODES 128 /* draft nodes per tree for the Gated DeltaNet calls       */
 #define TV_BLOCK_SIZE 16     /* tokens per KV-cache page                                */
 #define TV_TREE_MAX_TOPK 16  /* candidates per depth for tree construction             */
 #define TV_TREE_MAX_DEPTH 16 /* depths of a constructed tree                           */
@@ -163,7 +163,7 @@ tv_status tree_verify_attn(const void* q, const void* k_node, const void* v_node
  *   alpha     float [B, N, H] gates
  *   beta      float [B, N, H] write strengths
  *   S0        float [B, H, Dk, Dv] committed state (read only)
- *   anc_mask  uint64 [B, N]   from tree_mask_build (one word per node: N <= 64)
+ *   anc_mask  uint64 [B, N, TV_ANC_WORDS(N)]  from tree_mask_build
  *   out       [B, N, H, Dv]   out_dtype (TV_F32, or TV_BF16 with bf16 inputs)
  * Gates may be any finite values, 0 included (a gate exp(g) that underflowed):
  * a zero gate cuts the path's decay products to exactly 0.

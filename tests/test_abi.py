@@ -111,7 +111,7 @@ def test_gdn_validation(lib):
     assert f(*bad) == tv.TV_ERR_SHAPE
     bad = list(args); bad[10] = 64
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
-    bad = list(args); bad[8] = 65
+    bad = list(args); bad[8] = 129
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
     bad = list(args); bad[12] = 3
     assert f(*bad) == tv.TV_ERR_UNSUPPORTED
@@ -179,7 +179,7 @@ def test_gdn_commit_validation(lib):
     assert call(a6=None) == tv.TV_ERR_NULL          # num_accepted
     assert call(a13=None) == tv.TV_ERR_NULL         # S_out
     assert call(a7=0) == tv.TV_ERR_SHAPE
-    assert call(a8=65) == tv.TV_ERR_UNSUPPORTED
+    assert call(a8=129) == tv.TV_ERR_UNSUPPORTED
     assert call(a10=64) == tv.TV_ERR_UNSUPPORTED     # Dk
     assert call(a12=5) == tv.TV_ERR_UNSUPPORTED      # dtype
     assert call(a4=ctypes.c_void_p(0x1004)) == tv.TV_ERR_UNSUPPORTED   # S0 not 16-byte aligned

@@ -61,14 +61,17 @@ def test_gdn_commit_in_place(lib):
     _gdn_check(lib, x, acc, na, "in place", in_place=True)
 
 
-def test_gdn_commit_deep_chain_strong_state(lib):
-    """N = 64 chain fully accepted, gates down to 0.05, S0 ~ N(0, 1)."""
-    x, _, _ = _gdn(52, B=3, N=64, H=4, Dk=128, Dv=128, tree="chain", dtype=torch.float32, s0_std=1.0)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N", [64, 128])
+def test_gdn_commit_deep_chain_strong_state(lib, dtype, N):
+    """A chain of N nodes fully accepted (more than one staged chunk at 128),
+    gates down to 0.05, S0 ~ N(0, 1)."""
+    x, _, _ = _gdn(52, B=3, N=N, H=4, Dk=128, Dv=128, tree="chain", dtype=dtype, s0_std=1.0)
     g = torch.Generator().manual_seed(5)
     x.alpha.copy_(torch.rand(x.alpha.shape, generator=g).mul(0.95).add(0.05).to(DEV))
-    acc = np.tile(np.arange(64, dtype=np.int32), (3, 1))
-    na = np.array([64, 1, 33], dtype=np.int32)
-    _gdn_check(lib, x, acc, na, "deep chain")
+    acc = np.tile(np.arange(N, dtype=np.int32), (3, 1))
+    na = np.array([N, 1, N // 2 + 1], dtype=np.int32)
+    _gdn_check(lib, x, acc, na, f"deep chain N={N}")
 
 
 def test_gdn_commit_matches_verify_output(lib):

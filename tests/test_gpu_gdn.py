@@ -60,17 +60,20 @@ def test_step_batch_two_per_cu(lib):
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("tree,N", [("chain", 64), ("star", 17), ("random_parent", 64),
-                                    ("random_parent", 1), ("leaf_sibling", 32), ("spine_first", 40)])
+                                    ("random_parent", 1), ("leaf_sibling", 32), ("spine_first", 40),
+                                    ("random_parent", 65), ("spine_first", 100), ("chain", 128),
+                                    ("random_parent", 128), ("spine_first", 128), ("star", 128)])
 def test_trees(lib, dtype, tree, N):
     x = W.gdn_inputs(51, B=3, N=N, H=4, Dk=128, Dv=128, tree=tree, dtype=dtype, device=DEV)
     check(lib, x, tree)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_strong_state_and_gates(lib, dtype):
+@pytest.mark.parametrize("N", [64, 128])
+def test_strong_state_and_gates(lib, dtype, N):
     """Larger committed state and gates spread over (0, 1] on deep random trees
     (gate products far below 1, so the gate ratios of distant ancestors matter)."""
-    x = W.gdn_inputs(52, B=2, N=64, H=3, Dk=128, Dv=128, tree="random_parent", dtype=dtype,
+    x = W.gdn_inputs(52, B=2, N=N, H=3, Dk=128, Dv=128, tree="random_parent", dtype=dtype,
                      device=DEV, s0_std=1.0)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(7)
@@ -113,16 +116,17 @@ def _root_path(parent_b, t):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("where", ["root", "interior", "leaf", "all", "underflow"])
-def test_zero_and_underflowing_gates(lib, dtype, where):
+@pytest.mark.parametrize("where,N", [("root", 40), ("interior", 40), ("leaf", 40), ("all", 40),
+                                     ("underflow", 40), ("all", 128), ("underflow", 128)])
+def test_zero_and_underflowing_gates(lib, dtype, where, N):
     """Gates exactly 0 (a gate exp(g) that underflowed) at a root, an interior
     node and a leaf, and gates of 1e-30 along deep paths so that the gate
     products underflow fp32: every output stays finite and within tolerance
     of the recurrence, and the commit over a path through those nodes agrees
     with the oracle too (DFlash-TfM summary, section 3: the state follows the
     recurrence whatever the gate)."""
-    x = W.gdn_inputs(54, B=3, N=40, H=4, Dk=128, Dv=128, tree="spine_first", dtype=dtype,
-                     device=DEV, s0_std=0.5)
+    x = W.gdn_inputs(54, B=3, N=N, H=4, Dk=128, Dv=128, tree="spine_first", dtype=dtype,
+                     device=DEV, s0_std=0.5, max_depth=8 if N <= 64 else 24)
     alpha = x.alpha.cpu().numpy()
     acc = np.full((x.B, x.N), -1, dtype=np.int32)
     na = np.zeros(x.B, dtype=np.int32)

@@ -22,7 +22,7 @@ TV_OK, TV_ERR_NULL, TV_ERR_SHAPE, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_L
 TV_F32, TV_BF16 = 0, 1
 TV_TREE_OK, TV_TREE_BAD_PARENT, TV_TREE_BAD_DEPTH, TV_TREE_BAD_CTX = range(4)
 MAX_NODES = 128      # mask, attention, walk, KV commit
-GDN_MAX_NODES = 64   # the Gated DeltaNet calls
+GDN_MAX_NODES = 128  # the Gated DeltaNet calls
 
 
 def anc_words(n: int) -> int:

@@ -17,21 +17,23 @@ namespace {
 // One workgroup per (sequence, head): thread t holds columns 4 (t % 32) .. +3
 // of rows 16 (t / 32) .. +15 of the 128 x 128 state, in registers, so that
 // the state moves in 16-byte pieces.  The accepted nodes' keys, values and
-// gates are staged in LDS first (one batch of loads); each step forms
+// gates are staged in LDS, 64 steps at a time (one batch of loads); each step forms
 // u = k^T S (eight partial sums per column, combined through LDS) and applies
 // S <- alpha S + k (beta (v - alpha u))^T, which is the recurrence written
 // out.  S0 and S_out may be the same buffer: each workgroup reads its whole
 // state before writing it.
 constexpr int kGD = 128;  // Dk = Dv
 
+constexpr int kChunk = 64;  // accepted steps staged in LDS at a time
+
 template <typename T>
 __global__ __launch_bounds__(256) void gdn_commit_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* S0, const int32_t* __restrict__ acc_nodes,
     const int32_t* __restrict__ num_acc, int N, int H, float* S_out) {
-  __shared__ __align__(16) float s_kv[TV_GDN_MAX_NODES][2 * kGD];  // [step][k | v]
-  __shared__ float2 s_ab[TV_GDN_MAX_NODES];                    // (alpha, beta) per step
-  __shared__ __align__(16) float s_u[8][kGD];                  // partial k^T S per row group
+  __shared__ __align__(16) float s_kv[kChunk][2 * kGD];  // [step][k | v]
+  __shared__ float2 s_ab[kChunk];                        // (alpha, beta) per step
+  __shared__ __align__(16) float s_u[8][kGD];            // partial k^T S per row group
   const int b = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x;
   const int cg = tid % 32, rg = tid / 32;  // columns 4 cg .. 4 cg + 3, rows 16 rg .. 16 rg + 15
@@ -42,70 +44,73 @@ __global__ __launch_bounds__(256) void gdn_commit_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     S[r] = *reinterpret_cast<const float4*>(S0 + sbase + static_cast<size_t>(16 * rg + r) * kGD + 4 * cg);
-  // keys and values of the accepted steps, 16 bytes per load
-  constexpr int kPer = 16 / static_cast<int>(sizeof(T));  // elements per piece
+  constexpr int kPer = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte piece
   constexpr int kPieces = kGD / kPer;                      // pieces per row
-  for (int e = tid; e < a * 2 * kPieces; e += 256) {
-    const int st = e / (2 * kPieces), c = e % (2 * kPieces);
-    const int node = min(max(acc_nodes[static_cast<size_t>(b) * N + st], 0), N - 1);
-    const size_t row = (static_cast<size_t>(b) * N + node) * H + h;
-    const bool isv = c >= kPieces;
-    const int piece = isv ? c - kPieces : c;
-    const uint4 raw = *reinterpret_cast<const uint4*>((isv ? v : k) + row * kGD + piece * kPer);
-    float* dst = &s_kv[st][(isv ? kGD : 0) + piece * kPer];
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int c0 = 0; c0 < a; c0 += kChunk) {
+    const int na = min(kChunk, a - c0);
+    // keys and values of the chunk's accepted steps, 16 bytes per load
+    for (int e = tid; e < na * 2 * kPieces; e += 256) {
+      const int st = e / (2 * kPieces), c = e % (2 * kPieces);
+      const int node = min(max(acc_nodes[static_cast<size_t>(b) * N + c0 + st], 0), N - 1);
+      const size_t row = (static_cast<size_t>(b) * N + node) * H + h;
+      const bool isv = c >= kPieces;
+      const int piece = isv ? c - kPieces : c;
+      const uint4 raw = *reinterpret_cast<const uint4*>((isv ? v : k) + row * kGD + piece * kPer);
+      float* dst = &s_kv[st][(isv ? kGD : 0) + piece * kPer];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dst[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
-        dst[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+        for (int i = 0; i < 4; ++i) {
+          dst[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
+          dst[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+        }
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y),
+                                                      __uint_as_float(raw.z), __uint_as_float(raw.w));
       }
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y),
-                                                    __uint_as_float(raw.z), __uint_as_float(raw.w));
     }
-  }
-  if (tid < a) {
-    const int node = min(max(acc_nodes[static_cast<size_t>(b) * N + tid], 0), N - 1);
-    const size_t g = (static_cast<size_t>(b) * N + node) * H + h;
-    s_ab[tid] = make_float2(alpha[g], beta[g]);
-  }
-  __syncthreads();
-
-  for (int st = 0; st < a; ++st) {
-    float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float kr = s_kv[st][16 * rg + r];
-      p.x += kr * S[r].x;
-      p.y += kr * S[r].y;
-      p.z += kr * S[r].z;
-      p.w += kr * S[r].w;
+    if (tid < na) {
+      const int node = min(max(acc_nodes[static_cast<size_t>(b) * N + c0 + tid], 0), N - 1);
+      const size_t g = (static_cast<size_t>(b) * N + node) * H + h;
+      s_ab[tid] = make_float2(alpha[g], beta[g]);
     }
-    *reinterpret_cast<float4*>(&s_u[rg][4 * cg]) = p;
     __syncthreads();
-    float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    for (int st = 0; st < na; ++st) {
+      float4 p = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 q = *reinterpret_cast<const float4*>(&s_u[i][4 * cg]);
-      u.x += q.x;
-      u.y += q.y;
-      u.z += q.z;
-      u.w += q.w;
-    }
-    const float al = s_ab[st].x, be = s_ab[st].y;
-    const float4 vv = *reinterpret_cast<const float4*>(&s_kv[st][kGD + 4 * cg]);
-    const float4 wv = make_float4(be * (vv.x - al * u.x), be * (vv.y - al * u.y),
-                                  be * (vv.z - al * u.z), be * (vv.w - al * u.w));
+      for (int r = 0; r < 16; ++r) {
+        const float kr = s_kv[st][16 * rg + r];
+        p.x += kr * S[r].x;
+        p.y += kr * S[r].y;
+        p.z += kr * S[r].z;
+        p.w += kr * S[r].w;
+      }
+      *reinterpret_cast<float4*>(&s_u[rg][4 * cg]) = p;
+      __syncthreads();
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float kr = s_kv[st][16 * rg + r];
-      S[r].x = al * S[r].x + kr * wv.x;
-      S[r].y = al * S[r].y + kr * wv.y;
-      S[r].z = al * S[r].z + kr * wv.z;
-      S[r].w = al * S[r].w + kr * wv.w;
+      for (int i = 0; i < 8; ++i) {
+        const float4 q = *reinterpret_cast<const float4*>(&s_u[i][4 * cg]);
+        u.x += q.x;
+        u.y += q.y;
+        u.z += q.z;
+        u.w += q.w;
+      }
+      const float al = s_ab[st].x, be = s_ab[st].y;
+      const float4 vv = *reinterpret_cast<const float4*>(&s_kv[st][kGD + 4 * cg]);
+      const float4 wv = make_float4(be * (vv.x - al * u.x), be * (vv.y - al * u.y),
+                                    be * (vv.z - al * u.z), be * (vv.w - al * u.w));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float kr = s_kv[st][16 * rg + r];
+        S[r].x = al * S[r].x + kr * wv.x;
+        S[r].y = al * S[r].y + kr * wv.y;
+        S[r].z = al * S[r].z + kr * wv.z;
+        S[r].w = al * S[r].w + kr * wv.w;
+      }
+      __syncthreads();  // s_u (and, after the last step, the staged chunk) is rewritten next
     }
-    __syncthreads();  // s_u is rewritten by the next step
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r)

@@ -13,14 +13,15 @@
 //   O = gamma (Q S0) + Y U                o_t = S_t^T q_t
 //
 // The section's (I + X) U = beta V carries the committed-state term in the
-// same system.  Node t depends only on rows of smaller depth, so the solve
-// runs level by level over depth.
+// same system.  The columns of U and O are independent, so a kernel may split
+// the state's columns over workgroups: S0 is still read once in total, while
+// the small node-by-node terms are formed again per column block.
 //
-// Two kernels.  bf16 inputs: one workgroup per (sequence, head), with the
-// dense products on MFMA (below).  fp32 inputs: workgroup = (sequence, head,
-// 32 output columns), every product as fp32 FMAs from LDS; the columns of U
-// and O are independent, so the state S0 is read once in total while the
-// (small) Gram terms are recomputed per column block.
+// Three kernels.  bf16 inputs up to 64 nodes: one 8-wave workgroup per
+// (sequence, head), the dense products on MFMA and the solve as a product of
+// matrix powers.  bf16 inputs past 64 nodes: workgroups of 64 state columns,
+// a blocked solve on MFMA.  fp32 inputs: every product as fp32 FMAs, the
+// solve level by level over depth.
 #include <atomic>
 
 #include "tv_internal.h"
@@ -29,240 +30,36 @@ namespace tv {
 
 namespace {
 
-constexpr int kDk = 128;
-constexpr int kCB = 32;  // output columns per workgroup
-constexpr int kThreads = 256;
+constexpr int kDk = 128;         // Dk = Dv
+constexpr int kGC = 32;          // state columns per workgroup of the fp32 kernel
+constexpr int kNCB = kDk / kGC;  // column blocks per (sequence, head)
+constexpr int kGThreads = 256;
 
-__device__ __forceinline__ float load_f(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ void store_f(float* p, size_t i, float v) { p[i] = v; }
-
-size_t gdn_lds_bytes(int N) {
-  // s_s0 [128][32]; s_k, s_q [N][128]; s_x, s_y [N][N]; s_u, s_ks, s_qs
-  // [N][32]; gamma, beta, alpha [N] (+1 pad); anc [N] (u64)
-  return sizeof(float) * (static_cast<size_t>(kDk) * kCB + static_cast<size_t>(N) * kDk * 2 +
-                          static_cast<size_t>(N) * N * 2 + static_cast<size_t>(N) * kCB * 3 +
-                          3 * N + 1) +
-         sizeof(uint64_t) * N + 16;
+// Workgroup -> (sequence-head bh, column block cb) for ncb column blocks per
+// (sequence, head).  Workgroups are dealt to the 8 XCDs round-robin by index,
+// so the column blocks of one (sequence, head) get indices equal mod 8: they
+// share an XCD and its L2, and their q and k rows come from HBM once.
+// Returns false for the padding workgroups of a grid rounded up to 8
+// (sequence, head) pairs.
+__device__ __forceinline__ bool gdn_block(int wgi, int BH, int ncb, int* bh, int* cb) {
+  const int xcd = wgi & 7, slot = wgi >> 3;
+  *cb = slot % ncb;
+  *bh = (slot / ncb) * 8 + xcd;
+  return *bh < BH;
 }
 
-// 8 consecutive elements of an input row, loaded with 16-byte accesses
-template <typename T>
-struct Chunk8 {
-  uint4 w[sizeof(T) / 2];
-};
+unsigned gdn_grid(int BH, int ncb) { return static_cast<unsigned>((BH + 7) / 8) * 8u * ncb; }
 
-template <typename T>
-__device__ __forceinline__ Chunk8<T> load8(const T* p) {
-  Chunk8<T> c;
-#pragma unroll
-  for (int i = 0; i < static_cast<int>(sizeof(T) / 2); ++i) c.w[i] = reinterpret_cast<const uint4*>(p)[i];
-  return c;
-}
-
-__device__ __forceinline__ void store8(float* dst, const Chunk8<float>& c) {
-  reinterpret_cast<uint4*>(dst)[0] = c.w[0];
-  reinterpret_cast<uint4*>(dst)[1] = c.w[1];
-}
-
-template <typename T, typename TO>
-__global__ __launch_bounds__(kThreads) void gdn_tree_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
-    const uint64_t* __restrict__ anc, int N, int H, int Dv, TO* __restrict__ out) {
-  extern __shared__ __align__(16) float lds[];
-  float* s_s0 = lds;                // [kDk][kCB]  this block's columns of S0
-  float* s_k = s_s0 + kDk * kCB;    // [N][kDk]
-  float* s_q = s_k + N * kDk;      // [N][kDk]
-  float* s_x = s_q + N * kDk;      // [N][N]
-  float* s_y = s_x + N * N;        // [N][N]
-  float* s_u = s_y + N * N;        // [N][kCB]  V, then the right-hand side, then U
-  float* s_ks = s_u + N * kCB;     // [N][kCB]  K S0
-  float* s_qs = s_ks + N * kCB;    // [N][kCB]  Q S0
-  float* s_gam = s_qs + N * kCB;   // [N]
-  float* s_beta = s_gam + N;       // [N]
-  float* s_alpha = s_beta + N;     // [N]
-  uint64_t* s_anc = reinterpret_cast<uint64_t*>(
-      (reinterpret_cast<uintptr_t>(s_alpha + N) + 7) & ~static_cast<uintptr_t>(7));  // [N]
-  __shared__ int s_maxdepth;
-
-  const int ncb = Dv / kCB;
-  const int cb = blockIdx.x % ncb;
-  const int bh = blockIdx.x / ncb;
-  const int h = bh % H;
-  const int b = bh / H;
-  const int tid = threadIdx.x;
-  const uint64_t live = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
-
-  // ---- phase 0: tree, gates, keys and queries into LDS
-  if (tid == 0) s_maxdepth = 1;
-  for (int t = tid; t < N; t += kThreads) {
-    const size_t nh = (static_cast<size_t>(b) * N + t) * H + h;
-    s_alpha[t] = alpha[nh];
-    s_beta[t] = beta[nh];
-    // keep only real, earlier nodes (ancestors precede their descendants);
-    // a node always sees itself
-    const uint64_t below = t >= 63 ? ~0ull >> 1 : ((1ull << t) - 1ull);
-    s_anc[t] = (anc[static_cast<size_t>(b) * N + t] & live & below) | (1ull << t);
-  }
-  {
-    // keys and queries, 8 elements per chunk: every thread issues all of its
-    // loads before converting any (N * 128 / 8 <= 1024 chunks, 4 per thread)
-    constexpr int kPer = 4;
-    const int nchunk = N * kDk / 8;
-    Chunk8<T> ck[kPer], cq[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < nchunk) {
-        const int t = e / (kDk / 8), d = (e % (kDk / 8)) * 8;
-        const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + d;
-        ck[u] = load8(k + off);
-        cq[u] = load8(q + off);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads;
-      if (e < nchunk) {
-        store8(s_k + e * 8, ck[u]);
-        store8(s_q + e * 8, cq[u]);
-      }
-    }
-  }
-  {
-    // the 128 x 32 column block of S0, as float4 (all loads in flight at once)
-    const float* s0 = S0 + (static_cast<size_t>(b) * H + h) * kDk * Dv + cb * kCB;
-    for (int e = tid; e < kDk * kCB / 4; e += kThreads) {
-      const int d = e / (kCB / 4), c4 = e % (kCB / 4);
-      reinterpret_cast<float4*>(s_s0)[e] =
-          *reinterpret_cast<const float4*>(s0 + static_cast<size_t>(d) * Dv + 4 * c4);
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 1: gamma, Gram terms, state products, V
-  for (int t = tid; t < N; t += kThreads) {
-    uint64_t m = s_anc[t];
-    float gm = 1.0f;
-    while (m) {
-      const int i = __ffsll(static_cast<unsigned long long>(m)) - 1;
-      gm *= s_alpha[i];
-      m &= m - 1;
-    }
-    s_gam[t] = gm;
-    atomicMax(&s_maxdepth, __popcll(s_anc[t]));
-  }
-
-  const int npairs = N * (N + 1) / 2;  // pairs (t, i) with i <= t
-  for (int pidx = tid; pidx < npairs; pidx += kThreads) {
-    int t = static_cast<int>((sqrtf(8.0f * pidx + 1.0f) - 1.0f) * 0.5f);
-    while (t * (t + 1) / 2 > pidx) --t;
-    while ((t + 1) * (t + 2) / 2 <= pidx) ++t;
-    const int i = pidx - t * (t + 1) / 2;
-    const uint64_t at = s_anc[t];
-    float xv = 0.0f, yv = 0.0f;
-    if ((at >> i) & 1ull) {
-      uint64_t seg = at & ~s_anc[i];  // t's path strictly below i
-      float r = 1.0f;
-      while (seg) {
-        const int s = __ffsll(static_cast<unsigned long long>(seg)) - 1;
-        r *= s_alpha[s];
-        seg &= seg - 1;
-      }
-      const float* kt = s_k + t * kDk;
-      const float* ki = s_k + i * kDk;
-      const float* qt = s_q + t * kDk;
-      float kk = 0.0f, qk = 0.0f;
-#pragma unroll 4
-      for (int d = 0; d < kDk; d += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(kt + d);
-        const float4 c = *reinterpret_cast<const float4*>(ki + d);
-        const float4 e = *reinterpret_cast<const float4*>(qt + d);
-        kk = fmaf(a.x, c.x, fmaf(a.y, c.y, fmaf(a.z, c.z, fmaf(a.w, c.w, kk))));
-        qk = fmaf(e.x, c.x, fmaf(e.y, c.y, fmaf(e.z, c.z, fmaf(e.w, c.w, qk))));
-      }
-      yv = r * qk;
-      if (i != t) xv = s_beta[t] * r * kk;
-    }
-    s_x[t * N + i] = xv;
-    s_y[t * N + i] = yv;
-  }
-
-  {
-    // K S0 and Q S0 for this column block: thread = (column c, node group),
-    // four nodes per pass, four head dimensions per LDS read
-    constexpr int kGroups = kThreads / kCB;
-    const int c = tid % kCB;
-    const int grp = tid / kCB;
-    for (int t0 = grp; t0 < N; t0 += 4 * kGroups) {
-      float ak[4] = {0.f, 0.f, 0.f, 0.f}, aq[4] = {0.f, 0.f, 0.f, 0.f};
-      int tt[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) tt[u] = min(t0 + u * kGroups, N - 1);
-#pragma unroll 4
-      for (int d = 0; d < kDk; d += 4) {
-        const float s0a = s_s0[(d + 0) * kCB + c], s0b = s_s0[(d + 1) * kCB + c];
-        const float s0c = s_s0[(d + 2) * kCB + c], s0d = s_s0[(d + 3) * kCB + c];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4 kv = *reinterpret_cast<const float4*>(s_k + tt[u] * kDk + d);
-          const float4 qv = *reinterpret_cast<const float4*>(s_q + tt[u] * kDk + d);
-          ak[u] = fmaf(kv.x, s0a, fmaf(kv.y, s0b, fmaf(kv.z, s0c, fmaf(kv.w, s0d, ak[u]))));
-          aq[u] = fmaf(qv.x, s0a, fmaf(qv.y, s0b, fmaf(qv.z, s0c, fmaf(qv.w, s0d, aq[u]))));
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = t0 + u * kGroups;
-        if (t < N) {
-          s_ks[t * kCB + c] = ak[u];
-          s_qs[t * kCB + c] = aq[u];
-          s_u[t * kCB + c] =
-              load_f(v, ((static_cast<size_t>(b) * N + t) * H + h) * Dv + cb * kCB + c);
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: right-hand side beta_t (v_t - gamma_t (K S0)_t)
-  for (int e = tid; e < N * kCB; e += kThreads) {
-    const int t = e / kCB;
-    s_u[e] = s_beta[t] * (s_u[e] - s_gam[t] * s_ks[e]);
-  }
-  __syncthreads();
-
-  // ---- phase 3: forward substitution, one depth level at a time
-  const int maxdepth = s_maxdepth;
-  for (int lvl = 2; lvl <= maxdepth; ++lvl) {
-    for (int e = tid; e < N * kCB; e += kThreads) {
-      const int t = e / kCB, c = e % kCB;
-      const uint64_t at = s_anc[t];
-      if (__popcll(at) != lvl) continue;
-      uint64_t m = at & ~(1ull << t);
-      float acc = s_u[e];
-      while (m) {
-        const int i = __ffsll(static_cast<unsigned long long>(m)) - 1;
-        acc = fmaf(-s_x[t * N + i], s_u[i * kCB + c], acc);
-        m &= m - 1;
-      }
-      s_u[e] = acc;
-    }
-    __syncthreads();
-  }
-
-  // ---- phase 4: outputs gamma_t (Q S0)_t + sum over ancestors-or-self of Y U
-  for (int e = tid; e < N * kCB; e += kThreads) {
-    const int t = e / kCB, c = e % kCB;
-    uint64_t m = s_anc[t];
-    float o = s_gam[t] * s_qs[e];
-    while (m) {
-      const int i = __ffsll(static_cast<unsigned long long>(m)) - 1;
-      o = fmaf(s_y[t * N + i], s_u[i * kCB + c], o);
-      m &= m - 1;
-    }
-    store_f(out, ((static_cast<size_t>(b) * N + t) * H + h) * Dv + cb * kCB + c, o);
-  }
+// Ancestor word `word` of node t, restricted to real, earlier nodes
+// (ancestors precede their descendants) plus t itself.
+__device__ __forceinline__ uint64_t anc_clean(uint64_t w, int t, int word) {
+  const int lo = 64 * word;
+  uint64_t below;
+  if (t >= lo + 64) below = ~0ull;
+  else if (t <= lo) below = 0ull;
+  else below = (1ull << (t - lo)) - 1ull;
+  const uint64_t self = (t >= lo && t < lo + 64) ? (1ull << (t - lo)) : 0ull;
+  return (w & below) | self;
 }
 
 // Product of the gates over an ancestor set, exact at zero gates and free of
@@ -278,18 +75,23 @@ struct GateProd {
   __device__ float value() const { return zeros ? 0.0f : ldexpf(mant, ex); }
 };
 
-__device__ __forceinline__ GateProd gate_product(const float* alpha, uint64_t set) {
+template <int W>
+__device__ __forceinline__ GateProd gate_product(const float* alpha, const uint64_t* set) {
   GateProd g{0, 0, 1.0f};
-  while (set) {
-    const float a = alpha[__ffsll(static_cast<unsigned long long>(set)) - 1];
-    set &= set - 1;
-    if (a == 0.0f) {
-      ++g.zeros;
-    } else {
-      int ea, em;
-      g.mant *= frexpf(a, &ea);
-      g.mant = frexpf(g.mant, &em);
-      g.ex += ea + em;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    uint64_t m = set[w];
+    while (m) {
+      const float a = alpha[64 * w + __ffsll(static_cast<unsigned long long>(m)) - 1];
+      m &= m - 1;
+      if (a == 0.0f) {
+        ++g.zeros;
+      } else {
+        int ea, em;
+        g.mant *= frexpf(a, &ea);
+        g.mant = frexpf(g.mant, &em);
+        g.ex += ea + em;
+      }
     }
   }
   return g;
@@ -304,8 +106,21 @@ __device__ __forceinline__ float gate_ratio(const int* zc, const float* mant, co
   return ldexpf(mant[t] * rmant[i], ex[t] - ex[i]);
 }
 
+typedef __bf16 gbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float gf32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowB = kDk * 2;  // bytes of one bf16 row of 128
+
+// 16-byte granules of a 256-byte bf16 row are XOR-swizzled by row, so reads
+// of one granule column from 16 rows spread over the LDS banks
+__device__ __forceinline__ int gswz(int row, int byte) {
+  const int key = ((row & 7) << 1) | ((row >> 3) & 1);
+  return row * kRowB + (((byte >> 4) ^ key) << 4) + (byte & 15);
+}
+
 // ---------------------------------------------------------------------------
-// bf16 inputs: the dense products on MFMA, one workgroup per (sequence, head).
+// bf16 inputs, N <= 64: the dense products on MFMA, one 8-wave workgroup per
+// (sequence, head).
 //
 // K S0 and Q S0 are one product [Q; K] S0, formed transposed (S0^T [Q; K]^T)
 // so that S0's rows come out of LDS through the transpose read, as the value
@@ -318,7 +133,6 @@ __device__ __forceinline__ float gate_ratio(const int* zc, const float* mant, co
 // and solve need neither S0 nor v, so they run first, while S0's loads are in
 // flight; the state products, the right-hand side and the outputs follow.
 constexpr int kMThreads = 512;
-constexpr int kRowB = kDk * 2;  // bytes of one bf16 row of 128
 
 typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 mbf16x4_t __attribute__((ext_vector_type(4)));
@@ -326,20 +140,12 @@ typedef short ms16x4_t __attribute__((ext_vector_type(4)));
 typedef short ms16x8_t __attribute__((ext_vector_type(8)));
 typedef float mf32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte granules of a 256-byte bf16 row are XOR-swizzled by row, so reads
-// of one granule column from 16 rows (and transpose reads of 4 rows) spread
-// over the LDS banks
-__device__ __forceinline__ int gswz(int row, int byte) {
-  const int key = ((row & 7) << 1) | ((row >> 3) & 1);
-  return row * kRowB + (((byte >> 4) ^ key) << 4) + (byte & 15);
-}
-
 __device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
   auto lp = (__attribute__((address_space(3))) mbf16x4_t*)(p);
   return __builtin_bit_cast(ms16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
-constexpr int kUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
+constexpr int kHUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
 
 // bytes of region 1: X, Y and two more NP x NP matrices for the solve, then one
 // bf16 half of S0 at a time, then [Q; K] S0 (fp32, 2NP rows of 128)
@@ -360,7 +166,7 @@ size_t gdn_mfma_lds_bytes(int N) {
   // beta, gamma, the gate-product mantissa and its reciprocal, depth, zero
   // count, exponent, ancestor words.  Up to 32 nodes this is 73 KB, so two
   // workgroups fit a CU.
-  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kUP * 4 +
+  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kHUP * 4 +
          static_cast<size_t>(np) * (np + 4) * 4 + 64 * 4 * 8 + 64 * 8;
 }
 
@@ -408,7 +214,7 @@ __device__ __forceinline__ void gdn_solve_step(const float* M, const float* P, f
 // Up to 32 nodes (kM <= 4) the kernel fits two workgroups per CU, registers
 // included.
 template <typename TO, int kM>
-__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <= 4 ? 4 : 2))) void gdn_mfma_kernel(
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <= 4 ? 4 : 2))) void gdn_head_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
@@ -418,7 +224,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   unsigned char* r1 = smem;                      // X, Y, third; then S0 hi, S0 lo; then [Q; K] S0 fp32
   unsigned char* r2 = smem + gdn_r1_bytes(NP);   // [Q; K] bf16 [2NP][128]
   float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V, then the right-hand side
-  float* s_m = s_u + NP * kUP;                   // M [NP][MP]
+  float* s_m = s_u + NP * kHUP;                   // M [NP][MP]
   float* s_alpha = s_m + NP * MP;
   float* s_beta = s_alpha + 64;
   float* s_gam = s_beta + 64;
@@ -489,8 +295,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
       lo.z = __uint_as_float(w.y << 16); lo.w = __uint_as_float(w.y & 0xffff0000u);
       hi.x = __uint_as_float(w.z << 16); hi.y = __uint_as_float(w.z & 0xffff0000u);
       hi.z = __uint_as_float(w.w << 16); hi.w = __uint_as_float(w.w & 0xffff0000u);
-      reinterpret_cast<float4*>(s_u + t * kUP + gr * 8)[0] = lo;
-      reinterpret_cast<float4*>(s_u + t * kUP + gr * 8)[1] = hi;
+      reinterpret_cast<float4*>(s_u + t * kHUP + gr * 8)[0] = lo;
+      reinterpret_cast<float4*>(s_u + t * kHUP + gr * 8)[1] = hi;
     }
   }
   if (tid < 64) {
@@ -519,7 +325,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     // gamma_t = product of alpha over t's root path, kept as a count of zero
     // gates and the product of the others as mantissa * 2^exponent
     const int t = tid;
-    const GateProd gp = gate_product(s_alpha, s_anc[t]);
+    const GateProd gp = gate_product<1>(s_alpha, s_anc + t);
     s_gam[t] = gp.value();
     s_mant[t] = gp.mant;
     s_rmant[t] = 1.0f / gp.mant;
@@ -696,14 +502,14 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   // ---- phase 4: right-hand side beta_t (v_t - gamma_t (K S0)_t), in place of V
   for (int e = tid; e < N * (kDk / 4); e += kMThreads) {
     const int t = e / (kDk / 4), c = (e % (kDk / 4)) * 4;
-    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kUP + c);
+    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kHUP + c);
     const float4 ks = *reinterpret_cast<const float4*>(s_qks + (NP + t) * kDk + c);
     const float bt = s_beta[t], gt = s_gam[t];
     uu.x = bt * (uu.x - gt * ks.x);
     uu.y = bt * (uu.y - gt * ks.y);
     uu.z = bt * (uu.z - gt * ks.z);
     uu.w = bt * (uu.w - gt * ks.w);
-    *reinterpret_cast<float4*>(s_u + t * kUP + c) = uu;
+    *reinterpret_cast<float4*>(s_u + t * kHUP + c) = uu;
   }
   __syncthreads();
 
@@ -722,7 +528,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
       mf32x4_t acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
 #pragma unroll
       for (int ks = 0; ks < NP / 4; ++ks) {
-        const float a = s_u[(4 * ks + lg) * kUP + 16 * ct + lr];
+        const float a = s_u[(4 * ks + lg) * kHUP + 16 * ct + lr];
         const float bv = s_m[t * MP + 4 * ks + lg];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
       }
@@ -740,6 +546,533 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs, 64 < N <= 128.  One 4-wave workgroup per (sequence, head, 64
+// state columns), wave w computing column tile w; the node count is padded to
+// NP = 16 NT.
+//
+//  1. q and k rows (bf16, exact) into LDS; this block's columns of S0 go
+//     straight into registers in the MFMA operand layout and stay in flight
+//     through steps 2-4, which do not need them.
+//  2. Gate products per node, then the Gram tiles [Q; K] K^T on bf16 MFMA,
+//     only the 16 x 16 tiles on or below the block diagonal (ancestors precede
+//     descendants), each masked and scaled by the gate ratios as it comes out:
+//     Y and X in LDS.
+//  3. Diagonal blocks D_b = (I + X_bb)^-1.  X_bb couples a node only to its
+//     strict ancestors inside the block, so X_bb^h = 0 for chains of at most h
+//     nodes and the inverse is the product of (I + (-X_bb)^(2^j)),
+//     j < ceil(log2 h): at most four steps, each two 16 x 16 fp32 MFMA
+//     products in one wave.
+//  4. M = Y (I + X)^-1 by block back-substitution over block columns a from
+//     the last: M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a.  M overwrites
+//     Y tile by tile (a tile is read only by its own update); one barrier per
+//     block column.
+//  5. [Q; K] S0 for this column block on bf16 MFMA, S0 split into
+//     hi = bf16(S0) and lo = bf16(S0 - hi) (two products: ~16 mantissa bits).
+//  6. Right-hand side beta (V - gamma K S0) from the K S0 accumulators, into
+//     the LDS of [Q; K], which is free by then; then O = gamma Q S0 + M RHS on
+//     fp32 MFMA, starting from the Q S0 accumulators, and the store.
+// ---------------------------------------------------------------------------
+
+constexpr int kWC = 64;            // state columns per workgroup
+constexpr int kWCB = kDk / kWC;    // column blocks per (sequence, head)
+constexpr int kWUP = kWC + 4;      // row pitch of the right-hand side (floats)
+
+// element (r, c) of a 16 x 16 fp32 tile: row-major, column XOR-swizzled by row
+__device__ __forceinline__ int tix(int r, int c) { return r * 16 + (c ^ r); }
+
+// lower-block-triangular tile (rt, kt), kt <= rt
+__device__ __forceinline__ int ltri(int rt, int kt) { return rt * (rt + 1) / 2 + kt; }
+
+template <int NT>
+struct GdnLds {
+  static constexpr int NP = 16 * NT;
+  static constexpr int NTRI = NT * (NT + 1) / 2;
+  static constexpr int W = (NP + 63) / 64;
+  static constexpr int kQK = 2 * NP * kRowB;      // [Q; K] bf16, later the RHS
+  static constexpr int kTiles = NTRI * 256 * 4;   // X or Y tiles
+  static constexpr int kScr = 4 * 2 * 256 * 4;    // per wave: two 16 x 16 fp32 tiles
+  static constexpr int kSmall = NP * 4 * 6 + NP * W * 8;  // gate product (4), alpha, beta, gamma; anc
+  static constexpr int kBytes = kQK + 2 * kTiles + kScr + kSmall;
+  static_assert(NP * kWUP * 4 <= kQK, "the RHS fits the rows' region");
+};
+
+// 16 x 16 x 16 fp32 product on v_mfma_f32_16x16x4f32: acc += (sa A) B
+__device__ __forceinline__ gf32x4_t mm16(const float* A, const float* B, gf32x4_t acc, int lr, int lg,
+                                         float sa = 1.0f) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const float a = sa * A[tix(lr, 4 * ks + lg)];
+    const float b = B[tix(4 * ks + lg, lr)];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// a tile in the accumulator layout: lane (lr, lg) holds rows 4 lg .. 4 lg + 3 of column lr
+__device__ __forceinline__ gf32x4_t tload(const float* T, int lr, int lg) {
+  return gf32x4_t{T[tix(4 * lg, lr)], T[tix(4 * lg + 1, lr)], T[tix(4 * lg + 2, lr)], T[tix(4 * lg + 3, lr)]};
+}
+
+__device__ __forceinline__ void tstore(float* T, gf32x4_t v, int lr, int lg) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) T[tix(4 * lg + r, lr)] = v[r];
+}
+
+// LDS written by this wave is read back by other lanes of the same wave: wait
+// for the wave's LDS operations only (global loads stay in flight)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier over LDS only: unlike __syncthreads it does not wait for
+// the wave's outstanding global loads, so S0's loads stay in flight across it
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+template <typename TO, int NT>
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+                     const float* __restrict__ beta, const float* __restrict__ S0,
+                     const uint64_t* __restrict__ anc, int N, int H, int BH, TO* __restrict__ out) {
+  using L = GdnLds<NT>;
+  constexpr int NP = L::NP, NTRI = L::NTRI, W = L::W;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* r_qk = smem;
+  float* r_u = reinterpret_cast<float*>(smem);  // the RHS, once [Q; K] is no longer read
+  float* r_x = reinterpret_cast<float*>(smem + L::kQK);
+  float* r_y = r_x + NTRI * 256;
+  float* r_s = r_y + NTRI * 256;                    // scratch tiles
+  float4* s_gp = reinterpret_cast<float4*>(r_s + 4 * 512);  // [NP] (mant, 1/mant, zeros, exponent)
+  float* s_alpha = reinterpret_cast<float*>(s_gp + NP);
+  float* s_beta = s_alpha + NP;
+  float* s_gam = s_beta + NP;
+  uint64_t* s_anc = reinterpret_cast<uint64_t*>(s_gam + NP);  // [NP][W]
+  __shared__ int s_maxdepth;
+
+  int bh, cb;
+  if (!gdn_block(blockIdx.x, BH, kWCB, &bh, &cb)) return;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int ct = wave;                    // this wave's column tile
+  const int col = cb * kWC + 16 * ct + lr;  // this lane's state column in the outputs
+
+  // ---- 1. loads
+  if (tid == 0) s_maxdepth = 1;
+  {
+    constexpr int kGr = 2 * NP * (kRowB / 16);  // 16-byte granules of [Q; K]
+    constexpr int kPer = kGr / kGThreads;
+    constexpr int kBatch = kPer % 8 == 0 ? 8 : (kPer % 4 == 0 ? 4 : 2);
+    static_assert(kGr % kGThreads == 0 && kPer % kBatch == 0, "granules per thread");
+#pragma unroll
+    for (int u0 = 0; u0 < kPer; u0 += kBatch) {
+      uint4 g[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = tid + (u0 + u) * kGThreads;
+        const int row = e >> 4, gr = e & 15;
+        const bool isk = row >= NP;
+        const int t = isk ? row - NP : row;
+        g[u] = make_uint4(0, 0, 0, 0);
+        if (t < N)
+          g[u] = *reinterpret_cast<const uint4*>((isk ? k : q) +
+                                                 ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = tid + (u0 + u) * kGThreads;
+        *reinterpret_cast<uint4*>(r_qk + gswz(e >> 4, (e & 15) * 16)) = g[u];
+      }
+    }
+  }
+  // issue order matters: the waits for the rows above and the loads below must
+  // not include S0's loads, which stay in flight until step 5
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < NP) {
+    const int t = tid;
+    float a = 1.0f, be = 0.0f;
+    if (t < N) {
+      const size_t nh = (static_cast<size_t>(b) * N + t) * H + h;
+      a = alpha[nh];
+      be = beta[nh];
+    }
+    s_alpha[t] = a;
+    s_beta[t] = be;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      s_anc[t * W + w] = t < N ? anc_clean(anc[(static_cast<size_t>(b) * N + t) * W + w], t, w) : 0ull;
+  }
+  // v at this wave's output positions (row 16 rt + 4 lg + r, column `col`)
+  uint16_t vv[NT][4];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * rt + 4 * lg + r;
+      vv[rt][r] = t < N ? v[((static_cast<size_t>(b) * N + t) * H + h) * kDk + col] : static_cast<uint16_t>(0);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  // S0 fragments of column tile ct: lane (lr, lg) holds rows 32 ks + 8 lg .. +7
+  // of column `col` (the B operand of v_mfma_f32_16x16x32_bf16)
+  float s0f[4][8];
+  {
+    const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s0f[ks][j] = s0[static_cast<size_t>(32 * ks + 8 * lg + j) * kDk];
+  }
+  lds_barrier();
+
+  // ---- 2. gate products per node, then the masked Gram tiles
+  if (tid < NP) {
+    const int t = tid;
+    const GateProd gp = gate_product<W>(s_alpha, s_anc + t * W);
+    s_gam[t] = gp.value();
+    s_gp[t] = make_float4(gp.mant, 1.0f / gp.mant, __int_as_float(gp.zeros), __int_as_float(gp.ex));
+    int dpt = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) dpt += __popcll(s_anc[t * W + w]);
+    if (t < N) atomicMax(&s_maxdepth, dpt);
+  }
+  lds_barrier();
+  for (int u = wave; u < 2 * NTRI; u += 4) {
+    const int part = u >= NTRI, lt = part ? u - NTRI : u;  // Y tiles, then X tiles
+    int rt = 0;
+    while ((rt + 1) * (rt + 2) / 2 <= lt) ++rt;
+    const int kt = lt - rt * (rt + 1) / 2;
+    const int arow = (part ? NP : 0) + 16 * rt + lr, brow = NP + 16 * kt + lr;
+    gf32x4_t g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDk / 32; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(r_qk + gswz(arow, 2 * (32 * ks + 8 * lg)));
+      const uint4 bk = *reinterpret_cast<const uint4*>(r_qk + gswz(brow, 2 * (32 * ks + 8 * lg)));
+      g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8_t, a),
+                                                   __builtin_bit_cast(gbf16x8_t, bk), g, 0, 0, 0);
+    }
+    // masks and gate ratios: Y over ancestors-or-self, X over strict ancestors
+    const int i = 16 * kt + lr;
+    const float4 gi = s_gp[i];
+    float* dst = (part ? r_x : r_y) + lt * 256;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * rt + 4 * lg + r;
+      const bool on = ((s_anc[t * W + (i >> 6)] >> (i & 63)) & 1ull) && !(part && i == t);
+      float val = 0.0f;
+      if (on) {
+        const float4 gt = s_gp[t];
+        float ratio = 1.0f;
+        if (i != t)
+          ratio = __float_as_int(gt.z) != __float_as_int(gi.z)
+                      ? 0.0f
+                      : ldexpf(gt.x * gi.y, __float_as_int(gt.w) - __float_as_int(gi.w));
+        val = part ? s_beta[t] * ratio * g[r] : ratio * g[r];
+      }
+      dst[tix(4 * lg + r, lr)] = val;
+    }
+  }
+  lds_barrier();
+
+  // ---- 3. inverse diagonal blocks, written over X's diagonal tiles
+  {
+    const int hmax = min(16, s_maxdepth);
+    int J = 1;
+    while ((1 << J) < hmax) ++J;
+    float* mb = r_s + wave * 512;  // this wave's two scratch tiles
+    float* pb = mb + 256;
+    for (int bb = wave; bb < NT; bb += 4) {
+      float* xb = r_x + ltri(bb, bb) * 256;
+      // M = I - X (the first factor), P = X X (the next power)
+      const gf32x4_t p = mm16(xb, xb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
+      gf32x4_t mm = tload(xb, lr, lg);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mm[r] = (4 * lg + r == lr ? 1.0f : 0.0f) - mm[r];
+      tstore(mb, mm, lr, lg);
+      tstore(pb, p, lr, lg);
+      wave_lds_sync();
+      for (int j = 1; j < J; ++j) {
+        // M <- M + M P, and P <- P P for the next step
+        const gf32x4_t m2 = mm16(mb, pb, tload(mb, lr, lg), lr, lg);
+        gf32x4_t p2 = p;
+        if (j + 1 < J) p2 = mm16(pb, pb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
+        wave_lds_sync();
+        tstore(mb, m2, lr, lg);
+        if (j + 1 < J) tstore(pb, p2, lr, lg);
+        wave_lds_sync();
+      }
+      tstore(xb, tload(mb, lr, lg), lr, lg);
+      wave_lds_sync();
+    }
+  }
+  lds_barrier();
+
+  // ---- 4. M = Y (I + X)^-1, block column a from the last, over Y
+  {
+    float* tb = r_s + wave * 512;
+    for (int a = NT - 1; a >= 0; --a) {
+      for (int t = a + wave; t < NT; t += 4) {
+        float* yt = r_y + ltri(t, a) * 256;
+        gf32x4_t acc = tload(yt, lr, lg);
+        for (int c = a + 1; c <= t; ++c)
+          acc = mm16(r_y + ltri(t, c) * 256, r_x + ltri(c, a) * 256, acc, lr, lg, -1.0f);
+        tstore(tb, acc, lr, lg);
+        wave_lds_sync();
+        const gf32x4_t mt = mm16(tb, r_x + ltri(a, a) * 256, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
+        wave_lds_sync();
+        tstore(yt, mt, lr, lg);
+      }
+      lds_barrier();
+    }
+  }
+
+  // ---- 5. [Q; K] S0 for this wave's column tile
+  gf32x4_t qs[NT], ksa[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    qs[rt] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+    ksa[rt] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    gbf16x8_t hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      hi[j] = static_cast<__bf16>(s0f[ks][j]);
+      lo[j] = static_cast<__bf16>(s0f[ks][j] - static_cast<float>(hi[j]));
+    }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const uint4 aq = *reinterpret_cast<const uint4*>(r_qk + gswz(16 * rt + lr, 2 * (32 * ks + 8 * lg)));
+      const uint4 ak = *reinterpret_cast<const uint4*>(r_qk + gswz(NP + 16 * rt + lr, 2 * (32 * ks + 8 * lg)));
+      const gbf16x8_t q8 = __builtin_bit_cast(gbf16x8_t, aq), k8 = __builtin_bit_cast(gbf16x8_t, ak);
+      qs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q8, hi, qs[rt], 0, 0, 0);
+      qs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q8, lo, qs[rt], 0, 0, 0);
+      ksa[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, hi, ksa[rt], 0, 0, 0);
+      ksa[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, lo, ksa[rt], 0, 0, 0);
+    }
+  }
+  lds_barrier();  // every read of [Q; K] is done: its LDS takes the RHS
+
+  // ---- 6. right-hand side beta (v - gamma K S0), then O = gamma Q S0 + M RHS
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * rt + 4 * lg + r;
+      r_u[t * kWUP + 16 * ct + lr] = s_beta[t] * (bf16_to_f32(vv[rt][r]) - s_gam[t] * ksa[rt][r]);
+    }
+  lds_barrier();
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    gf32x4_t acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = s_gam[16 * rt + 4 * lg + r] * qs[rt][r];
+    for (int a = 0; a <= rt; ++a) {
+      const float* mt = r_y + ltri(rt, a) * 256;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float am = mt[tix(lr, 4 * ks + lg)];
+        const float bu = r_u[(16 * a + 4 * ks + lg) * kWUP + 16 * ct + lr];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am, bu, acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * rt + 4 * lg + r;
+      if (t < N) {
+        const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + col;
+        if constexpr (sizeof(TO) == 2)
+          out[off] = f32_to_bf16(acc[r]);
+        else
+          out[off] = acc[r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs.  One 256-thread workgroup per (sequence, head, 32 state
+// columns), every product as fp32 FMAs: the gate products, X and Y over the
+// ancestor pairs (packed lower triangle, diagonal included), K S0 and Q S0
+// for the column block, then forward substitution one depth level at a time
+// and the outputs.  q and k rows are read through the caches, not staged.
+// ---------------------------------------------------------------------------
+
+size_t gdn_f32_lds_bytes(int N, int W) {
+  const size_t P = static_cast<size_t>(N) * (N + 1) / 2;
+  // S0 block; X, Y; U, K S0, Q S0; gamma, beta; depth; anc
+  return sizeof(float) * (static_cast<size_t>(kDk) * kGC + 2 * P + 3 * static_cast<size_t>(N) * kGC + 2 * N) +
+         sizeof(int) * N + sizeof(uint64_t) * N * W + 16;
+}
+
+__device__ __forceinline__ float dot128(const float* a, const float* b) {
+  float s = 0.0f;
+#pragma unroll 8
+  for (int d = 0; d < kDk; d += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(a + d);
+    const float4 y = *reinterpret_cast<const float4*>(b + d);
+    s = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, s))));
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(kGThreads) void gdn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ S0,
+    const uint64_t* __restrict__ anc, int N, int W, int H, int BH, float* __restrict__ out) {
+  extern __shared__ __align__(16) float lds[];
+  const int P = N * (N + 1) / 2;
+  float* s_s0 = lds;              // [kDk][kGC]
+  float* s_x = s_s0 + kDk * kGC;  // packed: (t, i) at t (t + 1) / 2 + i
+  float* s_y = s_x + P;
+  float* s_u = s_y + P;           // [N][kGC]  V, then the right-hand side, then U
+  float* s_ks = s_u + N * kGC;    // [N][kGC]  K S0
+  float* s_qs = s_ks + N * kGC;   // [N][kGC]  Q S0
+  float* s_gam = s_qs + N * kGC;  // [N]
+  float* s_beta = s_gam + N;      // [N]
+  int* s_depth = reinterpret_cast<int*>(s_beta + N);
+  uint64_t* s_anc = reinterpret_cast<uint64_t*>(
+      (reinterpret_cast<uintptr_t>(s_depth + N) + 7) & ~static_cast<uintptr_t>(7));  // [N][W]
+  __shared__ int s_maxdepth;
+  __shared__ float s_alpha[TV_MAX_NODES];
+
+  int bh, cb;
+  if (!gdn_block(blockIdx.x, BH, kNCB, &bh, &cb)) return;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x;
+  const int col0 = cb * kGC;
+  const size_t row0 = static_cast<size_t>(b) * N;  // node rows of this sequence
+
+  if (tid == 0) s_maxdepth = 1;
+  for (int t = tid; t < N; t += kGThreads) {
+    const size_t nh = (row0 + t) * H + h;
+    s_alpha[t] = alpha[nh];
+    s_beta[t] = beta[nh];
+    for (int w = 0; w < W; ++w) s_anc[t * W + w] = anc_clean(anc[(row0 + t) * W + w], t, w);
+  }
+  {
+    const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + col0;
+    for (int e = tid; e < kDk * kGC / 4; e += kGThreads) {
+      const int d = e / (kGC / 4), c4 = e % (kGC / 4);
+      reinterpret_cast<float4*>(s_s0)[e] =
+          *reinterpret_cast<const float4*>(s0 + static_cast<size_t>(d) * kDk + 4 * c4);
+    }
+  }
+  __syncthreads();
+
+  // gamma (a direct product: exactly 0 past a zero gate) and depth per node
+  for (int t = tid; t < N; t += kGThreads) {
+    float gm = 1.0f;
+    int dpt = 0;
+    for (int w = 0; w < W; ++w) {
+      uint64_t m = s_anc[t * W + w];
+      dpt += __popcll(m);
+      while (m) {
+        gm *= s_alpha[64 * w + __ffsll(static_cast<unsigned long long>(m)) - 1];
+        m &= m - 1;
+      }
+    }
+    s_gam[t] = gm;
+    s_depth[t] = dpt;
+    atomicMax(&s_maxdepth, dpt);
+  }
+  // X and Y over the pairs (t, i <= t)
+  for (int p = tid; p < P; p += kGThreads) {
+    int t = static_cast<int>((sqrtf(8.0f * p + 1.0f) - 1.0f) * 0.5f);
+    while (t * (t + 1) / 2 > p) --t;
+    while ((t + 1) * (t + 2) / 2 <= p) ++t;
+    const int i = p - t * (t + 1) / 2;
+    float xv = 0.0f, yv = 0.0f;
+    if ((s_anc[t * W + (i >> 6)] >> (i & 63)) & 1ull) {
+      // product of the gates on t's path strictly below i
+      float r = 1.0f;
+      for (int w = 0; w < W; ++w) {
+        uint64_t seg = s_anc[t * W + w] & ~s_anc[i * W + w];
+        while (seg) {
+          r *= s_alpha[64 * w + __ffsll(static_cast<unsigned long long>(seg)) - 1];
+          seg &= seg - 1;
+        }
+      }
+      const float* ki = k + ((row0 + i) * H + h) * kDk;
+      yv = r * dot128(q + ((row0 + t) * H + h) * kDk, ki);
+      if (i != t) xv = s_beta[t] * r * dot128(k + ((row0 + t) * H + h) * kDk, ki);
+    }
+    s_x[p] = xv;
+    s_y[p] = yv;
+  }
+  // K S0 and Q S0 for the column block, and V: thread = (column c, node group)
+  {
+    constexpr int kGroups = kGThreads / kGC;
+    const int c = tid % kGC, grp = tid / kGC;
+    for (int t = grp; t < N; t += kGroups) {
+      const float* kt = k + ((row0 + t) * H + h) * kDk;
+      const float* qt = q + ((row0 + t) * H + h) * kDk;
+      float ak = 0.0f, aq = 0.0f;
+#pragma unroll 4
+      for (int d = 0; d < kDk; d += 4) {
+        const float4 kv4 = *reinterpret_cast<const float4*>(kt + d);
+        const float4 qv4 = *reinterpret_cast<const float4*>(qt + d);
+        const float s0a = s_s0[(d + 0) * kGC + c], s0b = s_s0[(d + 1) * kGC + c];
+        const float s0c = s_s0[(d + 2) * kGC + c], s0d = s_s0[(d + 3) * kGC + c];
+        ak = fmaf(kv4.x, s0a, fmaf(kv4.y, s0b, fmaf(kv4.z, s0c, fmaf(kv4.w, s0d, ak))));
+        aq = fmaf(qv4.x, s0a, fmaf(qv4.y, s0b, fmaf(qv4.z, s0c, fmaf(qv4.w, s0d, aq))));
+      }
+      s_ks[t * kGC + c] = ak;
+      s_qs[t * kGC + c] = aq;
+      s_u[t * kGC + c] = v[((row0 + t) * H + h) * kDk + col0 + c];
+    }
+  }
+  __syncthreads();
+
+  // right-hand side beta_t (v_t - gamma_t (K S0)_t)
+  for (int e = tid; e < N * kGC; e += kGThreads) {
+    const int t = e / kGC;
+    s_u[e] = s_beta[t] * (s_u[e] - s_gam[t] * s_ks[e]);
+  }
+  __syncthreads();
+
+  // forward substitution, one depth level at a time
+  const int maxdepth = s_maxdepth;
+  for (int lvl = 2; lvl <= maxdepth; ++lvl) {
+    for (int e = tid; e < N * kGC; e += kGThreads) {
+      const int t = e / kGC, c = e % kGC;
+      if (s_depth[t] != lvl) continue;
+      const float* xr = s_x + t * (t + 1) / 2;
+      float acc = s_u[e];
+      for (int w = 0; w < W; ++w) {
+        uint64_t m = s_anc[t * W + w];
+        if (t >= 64 * w && t < 64 * w + 64) m &= ~(1ull << (t - 64 * w));
+        while (m) {
+          const int i = 64 * w + __ffsll(static_cast<unsigned long long>(m)) - 1;
+          acc = fmaf(-xr[i], s_u[i * kGC + c], acc);
+          m &= m - 1;
+        }
+      }
+      s_u[e] = acc;
+    }
+    __syncthreads();
+  }
+
+  // outputs gamma_t (Q S0)_t + sum over ancestors-or-self of Y U
+  for (int e = tid; e < N * kGC; e += kGThreads) {
+    const int t = e / kGC, c = e % kGC;
+    const float* yr = s_y + t * (t + 1) / 2;
+    float o = s_gam[t] * s_qs[e];
+    for (int w = 0; w < W; ++w) {
+      uint64_t m = s_anc[t * W + w];
+      while (m) {
+        const int i = 64 * w + __ffsll(static_cast<unsigned long long>(m)) - 1;
+        o = fmaf(yr[i], s_u[i * kGC + c], o);
+        m &= m - 1;
+      }
+    }
+    out[((row0 + t) * H + h) * kDk + col0 + c] = o;
+  }
+}
+
 // Raises a kernel's dynamic LDS limit once per device (the attribute is held
 // per device); `done` holds one flag per device id.
 constexpr int kMaxDevices = 64;
@@ -754,22 +1087,38 @@ hipError_t max_lds_once(std::atomic<int>* done, const void* fn, int bytes) {
   return e;
 }
 
+template <typename TO, int NT>
+hipError_t launch_gdn_cols_nt(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                              int H, void* out, hipStream_t stream) {
+  constexpr int lds = GdnLds<NT>::kBytes;
+  static_assert(lds + 16 <= 160 * 1024, "LDS budget");
+  static std::atomic<int> lds_set[kMaxDevices];
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_cols_kernel<TO, NT>), lds);
+  if (attr != hipSuccess) return attr;
+  const int BH = B * H;
+  hipLaunchKernelGGL((gdn_cols_kernel<TO, NT>), dim3(gdn_grid(BH, kWCB)), dim3(kGThreads), lds, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), alpha, beta, S0, anc, N, H, BH, static_cast<TO*>(out));
+  return hipGetLastError();
+}
+
 // A grid that fits the CUs one workgroup each asks for more LDS than half a
 // CU's, so that no two of its workgroups share a CU.
 constexpr size_t kGdnSpreadLds = 81 * 1024;
 
 template <typename TO, int kM>
-hipError_t launch_gdn_mfma_m(const void* q, const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_head_m(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                              int H, void* out, hipStream_t stream) {
   const size_t most = gdn_mfma_lds_bytes(8 * kM);
   static std::atomic<int> lds_set[kMaxDevices];
-  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_mfma_kernel<TO, kM>),
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_head_kernel<TO, kM>),
                                        static_cast<int>(most > kGdnSpreadLds ? most : kGdnSpreadLds));
   if (attr != hipSuccess) return attr;
   size_t lds = gdn_mfma_lds_bytes(N);
   if (static_cast<long long>(B) * H <= device_cus() && lds < kGdnSpreadLds) lds = kGdnSpreadLds;
-  hipLaunchKernelGGL((gdn_mfma_kernel<TO, kM>), dim3(static_cast<unsigned>(B) * H), dim3(kMThreads),
+  hipLaunchKernelGGL((gdn_head_kernel<TO, kM>), dim3(static_cast<unsigned>(B) * H), dim3(kMThreads),
                      lds, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), alpha, beta, S0,
                      anc, N, H, static_cast<TO*>(out));
@@ -777,31 +1126,47 @@ hipError_t launch_gdn_mfma_m(const void* q, const void* k, const void* v, const 
 }
 
 template <typename TO>
-hipError_t launch_gdn_mfma(const void* q, const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_head(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                            int H, void* out, hipStream_t stream) {
   switch ((N + 15) / 16) {
-    case 1: return launch_gdn_mfma_m<TO, 2>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
-    case 2: return launch_gdn_mfma_m<TO, 4>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
-    case 3: return launch_gdn_mfma_m<TO, 6>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
-    case 4: return launch_gdn_mfma_m<TO, 8>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 1: return launch_gdn_head_m<TO, 2>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 2: return launch_gdn_head_m<TO, 4>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 3: return launch_gdn_head_m<TO, 6>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    case 4: return launch_gdn_head_m<TO, 8>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, typename TO>
-hipError_t launch_gdn_typed(const void* q, const void* k, const void* v, const float* alpha,
-                            const float* beta, const float* S0, const uint64_t* anc, int B, int N,
-                            int H, int Dv, void* out, hipStream_t stream) {
-  const size_t lds = gdn_lds_bytes(N);
+template <typename TO>
+hipError_t launch_gdn_cols(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                           int H, void* out, hipStream_t stream) {
+#define TV_GDN_NT(X) \
+  case X: return launch_gdn_cols_nt<TO, X>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+  switch ((N + 15) / 16) {
+    TV_GDN_NT(5);
+    TV_GDN_NT(6);
+    TV_GDN_NT(7);
+    TV_GDN_NT(8);
+    default: return hipErrorInvalidValue;
+  }
+#undef TV_GDN_NT
+}
+
+hipError_t launch_gdn_f32(const void* q, const void* k, const void* v, const float* alpha,
+                          const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                          int H, void* out, hipStream_t stream) {
+  const int W = (N + 63) / 64;
+  const size_t lds = gdn_f32_lds_bytes(N, W);
   static std::atomic<int> lds_set[kMaxDevices];
-  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_tree_kernel<T, TO>),
-                                       static_cast<int>(gdn_lds_bytes(64)));
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_f32_kernel),
+                                       static_cast<int>(gdn_f32_lds_bytes(TV_MAX_NODES, (TV_MAX_NODES + 63) / 64)));
   if (attr != hipSuccess) return attr;
-  const unsigned grid = static_cast<unsigned>(B) * H * (Dv / kCB);
-  hipLaunchKernelGGL((gdn_tree_kernel<T, TO>), dim3(grid), dim3(kThreads), lds, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                     alpha, beta, S0, anc, N, H, Dv, static_cast<TO*>(out));
+  const int BH = B * H;
+  hipLaunchKernelGGL(gdn_f32_kernel, dim3(gdn_grid(BH, kNCB)), dim3(kGThreads), lds, stream,
+                     static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                     alpha, beta, S0, anc, N, W, H, BH, static_cast<float*>(out));
   return hipGetLastError();
 }
 
@@ -812,12 +1177,15 @@ hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* 
                       int Dk, int Dv, tv_dtype dtype, tv_dtype out_dtype, void* out,
                       hipStream_t stream) {
   (void)Dk;
+  (void)Dv;
   if (dtype == TV_BF16 && out_dtype == TV_BF16)
-    return launch_gdn_mfma<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    return N <= 64 ? launch_gdn_head<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+                   : launch_gdn_cols<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_BF16 && out_dtype == TV_F32)
-    return launch_gdn_mfma<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    return N <= 64 ? launch_gdn_head<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+                   : launch_gdn_cols<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_F32 && out_dtype == TV_F32)
-    return launch_gdn_typed<float, float>(q, k, v, alpha, beta, S0, anc, B, N, H, Dv, out, stream);
+    return launch_gdn_f32(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   return hipErrorInvalidValue;
 }
 
