@@ -1,7 +1,8 @@
 """Draft-tree construction on the GPU against the oracle: candidate tokens
-bit-exact and log-probabilities within 1e-5 + 1e-6 |lp| (fp32 log-sum-exp
-over up to 262144 entries), tree structure and float32 scores bit-exact on
-given candidates (both sides add in float32, one rounding per node)."""
+bit-exact, log-probabilities equal to the oracle's float64 log-softmax
+rounded to float32 (the library rounds its float64 log-sum-exp once), tree
+structure and float32 scores bit-exact on given candidates (both sides add in
+float32, one rounding per node) and end to end from the draft logits."""
 import numpy as np
 import pytest
 import torch
@@ -20,9 +21,10 @@ def _check_topk(lib, x, K):
     torch.cuda.synchronize()
     tok, lp = OT.draft_topk(x.double().cpu().numpy(), K)
     assert np.array_equal(got["cand_tokens"].cpu().numpy(), tok)
-    g = got["cand_logprob"].cpu().numpy().astype(np.float64)
-    err = np.abs(g - lp) - (1e-5 + 1e-6 * np.abs(lp))
-    assert err.max() <= 0, float(err.max())
+    g = got["cand_logprob"].cpu().numpy()
+    want = lp.astype(np.float32)
+    bad = np.flatnonzero(g.ravel() != want.ravel())
+    assert bad.size == 0, (bad[:8], g.ravel()[bad[:8]], lp.ravel()[bad[:8]])
     return got
 
 
@@ -71,54 +73,26 @@ def test_build(lib, L, K, N, w, ties):
 
 def test_end_to_end_ddtree_batch(lib):
     """The DDTree workload's construction at full size: 64 sequences, 8 depths
-    of 262144-entry bf16 draft logits, top 8, budget 64.  Candidates are
-    compared exactly (tokens) and within tolerance (log-probabilities).  bf16
-    logits lie on a coarse grid, so different paths can have equal cumulative
-    values; which of them fills the last places is decided by the last bit of
-    each side's own float32 log-probabilities.  What is unique is compared:
-    the sorted cumulative values of the tree (recomputed along each GPU path
-    from the oracle's float64 log-probabilities) against the oracle tree's,
-    within 1e-4; and the GPU tree is checked to be valid: parents first,
-    depths consistent, every node the candidate of its depth, better
-    siblings and parents in the tree."""
+    of 262144-entry bf16 draft logits, top 8, budget 64, one candidate per
+    round and 8 per round.  bf16 logits lie on a coarse grid, so different
+    paths often tie on their float32 cumulative values; with candidates and
+    log-probabilities bit-exact, every tie is decided the same way on both
+    sides and the trees must be identical node for node."""
     B, L, V, K, N = 64, 8, 262144, 8, 64
     x = W.draft_logits(4, B, L, V, torch.bfloat16, device=DEV, on_device=True)
     say("tree construction, DDTree batch")
     cand = lib.tree_draft_topk(x, K)
-    tree = lib.tree_build(cand["cand_tokens"], cand["cand_logprob"], N, 1)
     torch.cuda.synchronize()
     tok, lp = OT.draft_topk(x.double().cpu().numpy(), K)
     assert np.array_equal(cand["cand_tokens"].cpu().numpy(), tok)
-    ref = OT.tree_build(tok, lp.astype(np.float32), N, 1)
-    g = {k: tree[k].cpu().numpy() for k in ("tokens", "parent", "depth", "num_nodes")}
-    assert np.array_equal(g["num_nodes"], ref["num_nodes"])
-    same = 0
-    for b in range(B):
-        rank_of = [{int(t): r for r, t in enumerate(tok[b, d])} for d in range(L)]
-
-        def path_value(par, dep, toks, t):
-            v, ranks = 0.0, []
-            while t >= 0:
-                r = rank_of[dep[t] - 1][int(toks[t])]
-                v += lp[b, dep[t] - 1, r]
-                ranks.append(r)
-                t = par[t]
-            return v, tuple(ranks[::-1])
-
-        par, dep, toks = g["parent"][b], g["depth"][b], g["tokens"][b]
-        vals, paths = [], set()
-        for t in range(N):
-            assert par[t] < t and dep[t] == (1 if par[t] < 0 else dep[par[t]] + 1)
-            assert int(toks[t]) in rank_of[dep[t] - 1]
-            v, pth = path_value(par, dep, toks, t)
-            vals.append(v)
-            paths.add(pth)
-        for pth in paths:  # closed under parents and better siblings
-            assert pth[:-1] in paths or len(pth) == 1
-            assert pth[-1] == 0 or pth[:-1] + (pth[-1] - 1,) in paths
-        rvals = [path_value(ref["parent"][b], ref["depth"][b], ref["tokens"][b], t)[0] for t in range(N)]
-        assert np.abs(np.sort(vals) - np.sort(rvals)).max() <= 1e-4
-        same += int(np.array_equal(toks, ref["tokens"][b]) and np.array_equal(par, ref["parent"][b]))
-    say(f"   trees identical to the oracle's in {same} of {B} sequences")
+    assert np.array_equal(cand["cand_logprob"].cpu().numpy(), lp.astype(np.float32))
+    for w in (1, 8):
+        tree = lib.tree_build(cand["cand_tokens"], cand["cand_logprob"], N, w)
+        torch.cuda.synchronize()
+        ref = OT.tree_build(tok, lp.astype(np.float32), N, w)
+        g = {k: tree[k].cpu().numpy() for k in ("tokens", "parent", "depth", "num_nodes", "score")}
+        for k in ("tokens", "parent", "depth", "num_nodes"):
+            assert np.array_equal(g[k], ref[k]), (w, k)
+        assert np.array_equal(g["score"], ref["score"]), w
     m = OM.tree_mask(g["parent"], np.full(B, 100), g["depth"])
     assert np.all(m["status"] == 0)

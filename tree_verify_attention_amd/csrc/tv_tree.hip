@@ -10,8 +10,8 @@
 // depth: one list of K candidates per depth, the same under every parent.
 //
 // Two kernels.  draft_topk_kernel: per (sequence, depth) row of draft logits,
-// the log-sum-exp over the vocabulary and the K largest logits (ties to the
-// lower token id), in one pass (an HBM stream).  tree_build_kernel: one wave
+// the log-sum-exp over the vocabulary (fp64) and the K largest logits (ties
+// to the lower token id), in one pass (an HBM stream).  tree_build_kernel: one wave
 // per sequence runs the queue in LDS; a candidate's push counter is its slot
 // in the pool, so "equal scores in push order" is "equal scores, lower slot".
 #include "tv_internal.h"
@@ -52,22 +52,46 @@ __device__ __forceinline__ float elem(const T* p, size_t i) {
 }
 
 // Row r = (sequence, depth) of V logits: K candidates and their log-softmax
-// values.  Each thread scans 16-byte chunks c = tid, tid + 512, ... keeping a
-// running (max, sum of exp2).  Each wave keeps one sorted list of its K best
-// (lane k < K holds entry k): an element is a candidate only if it beats the
-// list's last entry, which the whole wave knows, so after the first few
-// chunks a chunk costs a compare and a ballot per element; the rare
-// candidates enter one at a time by a lane-parallel insertion.  The four
-// waves' lists merge at the end.
+// values, the latter correctly rounded to fp32 (the fp64 log-sum-exp, rounded
+// once).  Each thread scans 16-byte chunks c = tid, tid + 512, ... keeping a
+// running max m.  An element more than kBig below the workgroup's running max
+// (shared through LDS after every pass) adds its exp in fp32 to a running sum
+// s: all of them together weigh at most V e^-kBig of the row's sum (the row
+// maximum alone weighs 1), so the fp32 rounding there stays far below fp32's
+// resolution of the result.  The larger elements are queued in LDS, one value
+// per entry, and the wave sums their exp in fp64, 64 at a time (one per lane),
+// against a wave-uniform reference.  Each wave keeps one sorted list of its K
+// best (lane k < K holds entry k): an element is a candidate only if it beats
+// the list's last entry, which the whole wave knows, so after the first few
+// chunks a chunk costs a compare and a ballot per element; the rare candidates
+// enter one at a time by a lane-parallel insertion.  The waves' lists and sums
+// merge at the end.
+constexpr float kBig = 22.0f;  // natural-log distance below the running max summed in fp32
+constexpr int kQ = 1024;       // queued values per wave: a power of two >= 63 + 64 * 16
+
+// order-preserving map of a float onto a signed int (for an LDS atomicMax)
+__device__ __forceinline__ int f2ord(float f) {
+  const int i = __float_as_int(f);
+  return i >= 0 ? i : i ^ 0x7fffffff;
+}
+__device__ __forceinline__ float ord2f(int i) { return __int_as_float(i >= 0 ? i : i ^ 0x7fffffff); }
+
 template <typename T>
-__global__ __launch_bounds__(kTopkThreads) void draft_topk_kernel(const T* __restrict__ logits,
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4))) void draft_topk_kernel(const T* __restrict__ logits,
                                                                   int V, int K,
                                                                   int32_t* __restrict__ cand_tok,
                                                                   float* __restrict__ cand_lp) {
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int nw = kTopkThreads / 64;
+  constexpr int E = 16 / static_cast<int>(sizeof(T));  // elements per chunk
+  static_assert(kQ >= 63 + 64 * E && (kQ & (kQ - 1)) == 0, "queue capacity");
+  __shared__ float s_q[nw][kQ];  // queued large elements
+  __shared__ int s_rowmax;       // the workgroup's running max (order-preserving int)
   const size_t row = blockIdx.x;
   const T* p = logits + row * static_cast<size_t>(V);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_rowmax = f2ord(-INFINITY);
+  __syncthreads();
 
   float wv = -INFINITY;  // this lane's entry of the wave list (lanes < K)
   int wi = 0x7fffffff;
@@ -94,57 +118,142 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_kernel(const T* __res
       thr_i = __shfl(wi, K - 1, 64);
     }
   };
-  float m = -INFINITY, s = 0.0f;  // running max and sum of exp2((x - m) log2 e)
+  float m = -INFINITY, s = 0.0f;  // running max and fp32 sum of the small elements' exp(x - m)
+  float base = -INFINITY;         // the workgroup's max as last seen (wave-uniform)
+  double S = 0.0;                 // fp64 sum of the queued elements' exp(x - R)
+  float R = -INFINITY;            // its reference (wave-uniform)
+  int qhead = 0, qtail = 0;       // the wave's queue (wave-uniform)
 
-  constexpr int E = 16 / static_cast<int>(sizeof(T));  // elements per chunk
+  // queue the values of the lanes with `big` set (one ballot)
+  auto push = [&](float x, bool big) __attribute__((always_inline)) {
+    const uint64_t b = __ballot(big);
+    if (b != 0ull) {
+      const int slot = qtail + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                   static_cast<uint32_t>(b >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+      if (big) s_q[wave][slot & (kQ - 1)] = x;
+      qtail += __popcll(b);
+    }
+  };
+  // every full batch of 64 queued values: their exp in fp64, the reference
+  // moved up to the batch's maximum first
+  auto drain = [&](bool all) __attribute__((always_inline)) {
+    if (qtail - qhead < (all ? 1 : 64)) return;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's queue writes are in
+    while (qtail - qhead >= (all ? 1 : 64)) {
+      const int n = min(64, qtail - qhead);
+      const float x = lane < n ? s_q[wave][(qhead + lane) & (kQ - 1)] : -INFINITY;
+      float bm = x;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off, 64));
+      if (bm > R) {
+        if (R != -INFINITY) S *= exp(static_cast<double>(R) - static_cast<double>(bm));
+        R = bm;
+      }
+      if (lane < n) S += exp(static_cast<double>(x) - static_cast<double>(R));
+      qhead += n;
+    }
+  };
+
   const bool vec = ((static_cast<size_t>(V) * sizeof(T)) % 16 == 0) &&
                    ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
   const int nchunk = vec ? V / E : 0;
-  // one chunk: the running max and sum absorb it, and its elements are offered
-  // to the wave list.  Called by the whole wave (the list lives in its first K
-  // lanes); a lane without a chunk offers nothing.
+  // one chunk: the running max and sums absorb it, and its elements are
+  // offered to the wave list.  Called by the whole wave (the list lives in its
+  // first K lanes); a lane without a chunk offers nothing.
   auto absorb = [&](const u32x4_t raw, int c, bool valid) __attribute__((always_inline)) {
     float x[E];
     if constexpr (sizeof(T) == 2) {
-      const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        x[2 * k] = __uint_as_float(raw[k] << 16);
+        x[2 * k + 1] = __uint_as_float(raw[k] & 0xffff0000u);
       }
     } else {
-      x[0] = __uint_as_float(raw[0]);
-      x[1] = __uint_as_float(raw[1]);
-      x[2] = __uint_as_float(raw[2]);
-      x[3] = __uint_as_float(raw[3]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(raw[k]);
     }
     float cm = x[0];
 #pragma unroll
     for (int k = 1; k < E; ++k) cm = fmaxf(cm, x[k]);
+    bool big[E];
     if (valid) {
       const float nm = fmaxf(m, cm);
+      const float cut = fmaxf(nm, base) - kBig;
       float add = 0.0f;
 #pragma unroll
-      for (int k = 0; k < E; ++k) add += __builtin_amdgcn_exp2f((x[k] - nm) * kLog2e);
+      for (int k = 0; k < E; ++k) {
+        big[k] = !(x[k] < cut);
+        if (!big[k]) add += __builtin_amdgcn_exp2f((x[k] - nm) * kLog2e);
+      }
       s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f((m - nm) * kLog2e)) + add;
       m = nm;
+    } else {
+#pragma unroll
+      for (int k = 0; k < E; ++k) big[k] = false;
     }
+#pragma unroll
+    for (int k = 0; k < E; ++k) push(x[k], big[k]);
+    drain(false);
     if (__ballot(valid && cm >= thr) != 0ull) {
 #pragma unroll
       for (int k = 0; k < E; ++k) consider(valid ? x[k] : -INFINITY, valid ? c * E + k : 0x7fffffff);
     }
+  };
+  // share the running max: publish the wave's, read the workgroup's
+  auto share_max = [&]() __attribute__((always_inline)) {
+    float wm = m;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
+    if (lane == 0) atomicMax(&s_rowmax, f2ord(wm));
+    base = fmaxf(base, ord2f(__shfl(s_rowmax, 0, 64)));
   };
   // kU loads in flight per thread, then their chunks; the loop bounds are
   // wave-uniform (cw = the wave's first chunk of a pass)
   constexpr int kU = 8;
   const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(p);
   int cw = wave * 64;
+  {
+    // the first pass: the maximum of its chunks is shared before any of them
+    // is classified (the running max knows nothing yet); the barrier is
+    // reached by every wave, with or without a first pass
+    const bool have = cw + 63 + (kU - 1) * kTopkThreads < nchunk;
+    u32x4_t r[kU];
+    float lm = -INFINITY;
+    if (have) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) r[u] = __builtin_nontemporal_load(pc + cw + lane + u * kTopkThreads);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            lm = fmaxf(lm, fmaxf(__uint_as_float(r[u][k] << 16), __uint_as_float(r[u][k] & 0xffff0000u)));
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) lm = fmaxf(lm, __uint_as_float(r[u][k]));
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off, 64));
+    if (lane == 0) atomicMax(&s_rowmax, f2ord(lm));
+    __syncthreads();
+    base = ord2f(s_rowmax);
+    if (have) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) absorb(r[u], cw + lane + u * kTopkThreads, true);
+      share_max();
+      cw += kU * kTopkThreads;
+    }
+  }
   for (; cw + 63 + (kU - 1) * kTopkThreads < nchunk; cw += kU * kTopkThreads) {
     u32x4_t r[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) r[u] = __builtin_nontemporal_load(pc + cw + lane + u * kTopkThreads);
 #pragma unroll
     for (int u = 0; u < kU; ++u) absorb(r[u], cw + lane + u * kTopkThreads, true);
+    share_max();
   }
   for (; cw < nchunk; cw += kTopkThreads) {
     const int c = cw + lane;
@@ -153,29 +262,34 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_kernel(const T* __res
     absorb(r, c, ok);
   }
   // elements past the last whole chunk (or every element without 16-byte
-  // rows); the loop runs while any lane of the wave has one
+  // rows): all go to the queue; the loop runs while any lane of the wave has one
   for (int v0 = nchunk * E + (tid & ~63); v0 < V; v0 += kTopkThreads) {
     const int v = v0 + lane;
     const float x = v < V ? elem(p, v) : -INFINITY;
-    if (v < V) {
-      const float nm = fmaxf(m, x);
-      s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f((m - nm) * kLog2e)) +
-          __builtin_amdgcn_exp2f((x - nm) * kLog2e);
-      m = nm;
-    }
+    m = fmaxf(m, x);
+    push(x, v < V);
+    drain(false);
     consider(x, v < V ? v : 0x7fffffff);
   }
+  drain(true);
 
-  // log-sum-exp over the workgroup
-  __shared__ float s_m[kTopkThreads / 64], s_s[kTopkThreads / 64];
-  __shared__ float s_lv[kTopkThreads / 64][kKMax];
-  __shared__ int s_li[kTopkThreads / 64][kKMax];
+  // log-sum-exp over the workgroup, in fp64: the fp32 sums of the small
+  // elements (each relative to its lane's max) and the fp64 sums (relative to
+  // their wave's reference)
+  __shared__ float s_m[nw], s_r[nw];
+  __shared__ double s_s[nw], s_big[nw];
+  __shared__ float s_lv[nw][kKMax];
+  __shared__ int s_li[nw][kKMax];
   float wm = m;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
-  float ws = m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f((m - wm) * kLog2e);
+  double ws = m == -INFINITY ? 0.0 : static_cast<double>(s) * exp(static_cast<double>(m) - static_cast<double>(wm));
+  double wb = S;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off, 64);
+  for (int off = 32; off >= 1; off >>= 1) {
+    ws += __shfl_xor(ws, off, 64);
+    wb += __shfl_xor(wb, off, 64);
+  }
   if (lane < K) {
     s_lv[wave][lane] = wv;
     s_li[wave][lane] = wi;
@@ -183,21 +297,24 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_kernel(const T* __res
   if (lane == 0) {
     s_m[wave] = wm;
     s_s[wave] = ws;
+    s_r[wave] = R;
+    s_big[wave] = wb;
   }
   __syncthreads();
   if (wave != 0) return;
   float gm = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) gm = fmaxf(gm, s_m[w]);
-  float gs = 0.0f;
+  for (int w = 0; w < nw; ++w) gm = fmaxf(gm, fmaxf(s_m[w], s_r[w]));
+  double gs = 0.0;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w)
-    gs += s_m[w] == -INFINITY ? 0.0f : s_s[w] * __builtin_amdgcn_exp2f((s_m[w] - gm) * kLog2e);
-  const float lse = gm + __builtin_amdgcn_logf(gs) * 0.6931471805599453f;
+  for (int w = 0; w < nw; ++w) {
+    if (s_m[w] != -INFINITY) gs += s_s[w] * exp(static_cast<double>(s_m[w]) - static_cast<double>(gm));
+    if (s_r[w] != -INFINITY) gs += s_big[w] * exp(static_cast<double>(s_r[w]) - static_cast<double>(gm));
+  }
+  const double lse = static_cast<double>(gm) + log(gs);
   // merge the waves' lists: lane j holds entries j and j + 64 of the
   // concatenated lists (entry e = entry e % K of wave e / K), offering the
   // better of the two it still has
-  constexpr int nw = kTopkThreads / 64;
   static_assert(nw * kKMax <= 128, "two merge entries per lane");
   float ev[2];
   int ei[2];
@@ -224,7 +341,7 @@ __global__ __launch_bounds__(kTopkThreads) void draft_topk_kernel(const T* __res
     }
     if (lane == 0) {
       cand_tok[row * K + k] = i;
-      cand_lp[row * K + k] = v - lse;
+      cand_lp[row * K + k] = static_cast<float>(static_cast<double>(v) - lse);
     }
   }
 }
@@ -239,11 +356,18 @@ __device__ __forceinline__ int meta_depth(int m) { return (m >> 5) & 31; }
 __device__ __forceinline__ int meta_rank(int m) { return m & 31; }
 __device__ __forceinline__ int meta_parent(int m) { return (m >> 10) - 1; }
 
-// One wave per sequence.  Rounds pop min(w, budget left, queued) candidates
-// (best score first, equal scores by lower slot), then push, for each popped
-// node in pop order, its next sibling (depth >= 2) and its first child (below
-// the maximum depth).  The popped nodes are then flattened by depth (stable)
-// and their parents renumbered.
+// One wave per sequence.  The queue is kept sorted in LDS (best score first,
+// equal scores by lower slot; a slot is the push counter), so a round is a few
+// lane-parallel steps whatever w is:
+//  1. the round's min(w, budget left, queued) candidates are the queue's
+//     first entries, in pop order;
+//  2. each popped node's successors, its next sibling (depth >= 2) and its
+//     first child (below the maximum depth), get slots in pop order;
+//  3. the rest of the queue and the new candidates merge: an entry's place is
+//     its place in its own group plus the number of entries of the other group
+//     that sort before it.
+// The popped nodes are then flattened by depth (stable) and their parents
+// renumbered.
 __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restrict__ cand_tok,
                                                         const float* __restrict__ cand_lp, int L,
                                                         int K, int N, int w,
@@ -252,8 +376,11 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ depth,
                                                         float* __restrict__ score,
                                                         int32_t* __restrict__ num_nodes) {
-  __shared__ float p_score[kPoolMax];
-  __shared__ int p_meta[kPoolMax];
+  __shared__ float q_score[2][kPoolMax];  // sorted queue (two buffers): score
+  __shared__ int q_slot[2][kPoolMax];     // and slot
+  __shared__ int p_meta[kPoolMax];        // per slot: depth, rank, parent
+  __shared__ float c_score[2 * TV_MAX_NODES];  // a round's new candidates, in push order
+  __shared__ int c_slot[2 * TV_MAX_NODES];
   __shared__ float n_score[TV_MAX_NODES];
   __shared__ int n_meta[TV_MAX_NODES];
   __shared__ float s_lp[TV_TREE_MAX_DEPTH * TV_TREE_MAX_TOPK];
@@ -261,76 +388,121 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restric
   const int b = blockIdx.x, lane = threadIdx.x;
   const float* lp_b = cand_lp + static_cast<size_t>(b) * L * K;
   for (int e = lane; e < L * K; e += 64) s_lp[e] = lp_b[e];
-  for (int e = lane; e < kPoolMax; e += 64) p_score[e] = -INFINITY;
   __syncthreads();
-  // the roots: the K depth-1 candidates in rank order (slots 0 .. K - 1)
+  // the roots: the K depth-1 candidates in rank order (slots 0 .. K - 1), whose
+  // log-probabilities decrease: they are the sorted queue (ties keep rank order)
   for (int r = lane; r < K; r += 64) {
-    p_score[r] = s_lp[r];
+    q_score[0][r] = s_lp[r];
+    q_slot[0][r] = r;
     p_meta[r] = meta_pack(1, r, -1);
   }
-  int pushed = K;  // slots used (= pushes so far)
-  int queued = K;  // live candidates
-  int n = 0;       // popped nodes
+  int cur = 0;      // buffer holding the queue
+  int queued = K;   // its length
+  int pushed = K;   // slots used
+  int n = 0;        // popped nodes
   __syncthreads();
   while (n < N && queued > 0) {
     const int take = min(min(w, N - n), queued);
-    for (int t = 0; t < take; ++t) {
-      // best live slot: larger score, then lower slot (empty slots are -inf
-      // and marked by a meta of -1)
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int e = lane; e < pushed; e += 64) {
-        const float v = p_score[e];
-        if (p_meta[e] >= 0 && cand_before(v, e, bv, bi)) {
-          bv = v;
-          bi = e;
-        }
+    // 1. pop the first `take` entries
+    for (int t = lane; t < take; t += 64) {
+      const int sl = q_slot[cur][t];
+      n_score[n + t] = q_score[cur][t];
+      n_meta[n + t] = p_meta[sl];
+    }
+    __syncthreads();
+    // 2. successors in pop order: a prefix count over the popped nodes
+    int base = 0;
+    for (int t0 = 0; t0 < take; t0 += 64) {
+      const int t = t0 + lane;
+      int d = 0, r = 0, par = -1;
+      bool sib = false, child = false;
+      if (t < take) {
+        const int m = n_meta[n + t];
+        d = meta_depth(m);
+        r = meta_rank(m);
+        par = meta_parent(m);
+        sib = d >= 2 && r + 1 < K;
+        child = d < L;
       }
-      int owner;
-      wave_best(bv, bi, owner);
+      const int cnt = static_cast<int>(sib) + static_cast<int>(child);
+      // exclusive prefix sum of cnt over the lanes (two ballots)
+      const uint64_t b1 = __ballot(cnt >= 1), b2 = __ballot(cnt >= 2);
+      const uint32_t lo1 = static_cast<uint32_t>(b1), hi1 = static_cast<uint32_t>(b1 >> 32);
+      const uint32_t lo2 = static_cast<uint32_t>(b2), hi2 = static_cast<uint32_t>(b2 >> 32);
+      const int before = static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi1, __builtin_amdgcn_mbcnt_lo(lo1, 0u)) +
+                                          __builtin_amdgcn_mbcnt_hi(hi2, __builtin_amdgcn_mbcnt_lo(lo2, 0u)));
+      int c = base + before;
+      if (sib) {
+        c_score[c] = n_score[par] + s_lp[(d - 1) * K + r + 1];
+        c_slot[c] = pushed + c;
+        p_meta[pushed + c] = meta_pack(d, r + 1, par);
+        ++c;
+      }
+      if (child) {
+        c_score[c] = n_score[n + t] + s_lp[d * K];
+        c_slot[c] = pushed + c;
+        p_meta[pushed + c] = meta_pack(d + 1, 0, n + t);
+      }
+      base += __popcll(b1) + __popcll(b2);
+    }
+    __syncthreads();
+    // 3. merge the rest of the queue (entries take .. queued - 1) with the new
+    // candidates into the other buffer
+    const int rest = queued - take, nc = base;
+    const int nxt = cur ^ 1;
+    for (int e = lane; e < rest; e += 64) {
+      const float v = q_score[cur][take + e];
+      const int sl = q_slot[cur][take + e];
+      int pos = e;
+      for (int j = 0; j < nc; ++j) pos += cand_before(c_score[j], c_slot[j], v, sl);
+      q_score[nxt][pos] = v;
+      q_slot[nxt][pos] = sl;
+    }
+    // a new candidate's place: the entries of either group before it, counted
+    // across the lanes (one ballot per 64 entries)
+    for (int j = 0; j < nc; ++j) {
+      const float v = c_score[j];
+      const int sl = c_slot[j];
+      int pos = 0;
+      for (int e0 = 0; e0 < rest; e0 += 64) {
+        const int e = e0 + lane;
+        pos += __popcll(__ballot(e < rest && cand_before(q_score[cur][take + e], q_slot[cur][take + e], v, sl)));
+      }
+      for (int i0 = 0; i0 < nc; i0 += 64) {
+        const int i2 = i0 + lane;
+        pos += __popcll(__ballot(i2 < nc && cand_before(c_score[i2], c_slot[i2], v, sl)));
+      }
       if (lane == 0) {
-        n_score[n + t] = p_score[bi];
-        n_meta[n + t] = p_meta[bi];
-        p_meta[bi] = -1;
-      }
-      __syncthreads();
-    }
-    if (lane == 0) {
-      for (int t = 0; t < take; ++t) {
-        const int me = n + t;
-        const int m = n_meta[me];
-        const int d = meta_depth(m), r = meta_rank(m), par = meta_parent(m);
-        if (d >= 2 && r + 1 < K) {
-          p_score[pushed] = n_score[par] + s_lp[(d - 1) * K + r + 1];
-          p_meta[pushed] = meta_pack(d, r + 1, par);
-          ++pushed;
-          ++queued;
-        }
-        if (d < L) {
-          p_score[pushed] = n_score[me] + s_lp[d * K];
-          p_meta[pushed] = meta_pack(d + 1, 0, me);
-          ++pushed;
-          ++queued;
-        }
+        q_score[nxt][pos] = v;
+        q_slot[nxt][pos] = sl;
       }
     }
+    cur = nxt;
+    queued = rest + nc;
+    pushed += nc;
     n += take;
-    queued -= take;
-    pushed = __shfl(pushed, 0, 64);
-    queued = __shfl(queued, 0, 64);
     __syncthreads();
   }
 
   // flatten by depth, stable: new index = nodes of smaller depth + nodes of
-  // the same depth popped earlier
-  for (int i = lane; i < n; i += 64) {
-    const int di = meta_depth(n_meta[i]);
-    int pos = 0;
-    for (int j = 0; j < n; ++j) {
-      const int dj = meta_depth(n_meta[j]);
-      pos += (dj < di) || (dj == di && j < i);
+  // the same depth popped earlier.  Lane l holds nodes l and l + 64; one
+  // ballot per (depth, half) counts them.
+  {
+    const int d0 = lane < n ? meta_depth(n_meta[lane]) : 0;
+    const int d1 = lane + 64 < n ? meta_depth(n_meta[lane + 64]) : 0;
+    int before = 0, p0 = 0, p1 = 0;
+    for (int d = 1; d <= L; ++d) {
+      const uint64_t b0 = __ballot(d0 == d), b1 = __ballot(d1 == d);
+      const uint32_t below0 = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b0 >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b0), 0u));
+      const uint32_t below1 = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b1 >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b1), 0u));
+      if (d0 == d) p0 = before + static_cast<int>(below0);
+      if (d1 == d) p1 = before + __popcll(b0) + static_cast<int>(below1);
+      before += __popcll(b0) + __popcll(b1);
     }
-    s_new[i] = pos;
+    if (lane < n) s_new[lane] = p0;
+    if (lane + 64 < n) s_new[lane + 64] = p1;
   }
   __syncthreads();
   const size_t ob = static_cast<size_t>(b) * N;
