@@ -24,10 +24,11 @@ BLOCK = 16
 def context_kv(k_cache, v_cache, block_table_b, g, ctx):
     """Gather the ctx context keys/values of one sequence and kv head: position
     j lives in page block_table_b[j // 16], slot j % 16."""
+    D = k_cache.shape[-1]
     j = np.arange(ctx)
     pages = np.asarray(block_table_b)[j // BLOCK].astype(np.int64)
-    K = np.asarray(k_cache[pages, g, j % BLOCK], dtype=np.float64).reshape(ctx, -1)
-    V = np.asarray(v_cache[pages, g, j % BLOCK], dtype=np.float64).reshape(ctx, -1)
+    K = np.asarray(k_cache[pages, g, j % BLOCK], dtype=np.float64).reshape(ctx, D)
+    V = np.asarray(v_cache[pages, g, j % BLOCK], dtype=np.float64).reshape(ctx, D)
     return K, V
 
 

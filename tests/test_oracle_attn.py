@@ -66,6 +66,26 @@ def test_chain_equals_causal_attention(N):
             np.testing.assert_allclose(out[b, :, h], ref.numpy(), rtol=0, atol=1e-12)
 
 
+def test_empty_and_ragged_contexts_equal_causal_attention():
+    """Contexts of 0, 1, 15, 16 and 17 tokens (no page, a partial page, page
+    boundaries) with a chain of nodes: still plain causal attention over
+    context ++ chain; with no context, over the chain alone."""
+    trees = W.make_trees(12, "chain", 5, 6, 100)
+    x = _case(tree="chain", B=5, N=6, trees=trees, ctx_len=np.array([0, 1, 15, 16, 17], dtype=np.int32))
+    out, _ = _run_oracle(x)
+    G = x.Hq // x.Hkv
+    for b in range(x.B):
+        ctx = int(x.ctx_len[b])
+        for h in range(x.Hq):
+            g = h // G
+            Kc, Vc = _contiguous_ctx(x, b, g)
+            K = torch.cat([Kc, x.k_node[b, :, g].double()])
+            V = torch.cat([Vc, x.v_node[b, :, g].double()])
+            allowed = torch.ones(x.N, ctx + x.N, dtype=torch.bool).tril(diagonal=ctx)
+            ref = _sdpa(x.q[b, :, h].double(), K, V, allowed, x.scale)
+            np.testing.assert_allclose(out[b, :, h], ref.numpy(), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("tree", ["random_parent", "spine_first", "leaf_sibling"])
 def test_each_node_is_attention_over_its_root_path(tree):
     """Every node's output equals ordinary attention of its query over the
