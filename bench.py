@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="MiB written before each repetition in `configs` (0: no flush)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload timing")
+    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5],
+                    help="time only this workload's step (as in `configs`) and print its JSON line "
+                         "(for per-workload kernel traces)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per global-layer attention call (rocprofv3 --pmc)")
     ap.add_argument("--attn-only", type=int, default=0, choices=[0, 2, 4],
@@ -474,8 +477,10 @@ def _summary(name, workload, B, N, calls, timing):
             "nodes_per_s": round(B * N / (step * 1e-3), 1)}
 
 
-def per_config(step: Step, dev, args, ceiling) -> dict:
-    """Each workload as its own step, timed call by call (see time_calls)."""
+def per_config(step, dev, args, ceiling, only: int = 0) -> dict:
+    """Each workload as its own step, timed call by call (see time_calls);
+    `only` > 0 times that workload alone (`step` may then be None unless it
+    is workload 3, whose inputs are the headline step's)."""
     import tree_verify_attention_amd as tv
     from synth import configs as CF
     from synth import workloads as W
@@ -491,85 +496,91 @@ def per_config(step: Step, dev, args, ceiling) -> dict:
         return x, wins, vocab
 
     # c1: tiny fp32 step (launch-bound)
-    x, wins, vocab = attn_cfg(1, False)
-    par = torch.from_numpy(x.trees.parent).to(dev)
-    mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
-    logits = W.walk_inputs(1, x.trees, vocab, torch.float32, device=dev).logits
-    calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev)), ("walk", _walk_call(tv, x.trees, logits, dev))]
-    t = time_calls(calls, reps, warm, flush)
-    r = _summary("c1", "B=1, N=16 random-parent tree, Hq=8, Hkv=2, D=64, ctx 512, fp32; logits [1,17,1000] fp32",
-                 x.B, x.N, calls, t)
-    kv = _kv_bytes(x, 0)
-    r["roofline"] = {"bound": "launch", "note": f"{kv} B of context K+V and a 68 KB logits row set: the "
-                     "calls are launch-latency bound", "attn_achieved_GBps": round(_gbps(kv, t["attn"]["median_ms"]), 1)}
-    res["c1"] = r
-    del x, logits, calls
+    if only in (0, 1):
+        x, wins, vocab = attn_cfg(1, False)
+        par = torch.from_numpy(x.trees.parent).to(dev)
+        mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
+        logits = W.walk_inputs(1, x.trees, vocab, torch.float32, device=dev).logits
+        calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev)), ("walk", _walk_call(tv, x.trees, logits, dev))]
+        t = time_calls(calls, reps, warm, flush)
+        r = _summary("c1", "B=1, N=16 random-parent tree, Hq=8, Hkv=2, D=64, ctx 512, fp32; logits [1,17,1000] fp32",
+                     x.B, x.N, calls, t)
+        kv = _kv_bytes(x, 0)
+        r["roofline"] = {"bound": "launch", "note": f"{kv} B of context K+V and a 68 KB logits row set: the "
+                         "calls are launch-latency bound", "attn_achieved_GBps": round(_gbps(kv, t["attn"]["median_ms"]), 1)}
+        res["c1"] = r
+        del x, logits, calls
 
     # c2: leaf-sibling batch, HBM-bound
-    x, wins, vocab = attn_cfg(2, True)
-    par = torch.from_numpy(x.trees.parent).to(dev)
-    mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
-    calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev))]
-    t = time_calls(calls, reps, warm, flush)
-    r = _summary("c2", "B=8, N=32 leaf-sibling trees, Hq=16, Hkv=8, D=256, ctx 4096, bf16", x.B, x.N, calls, t)
-    r["roofline"] = _hbm_roof("tree_verify_attn", _kv_bytes(x, 0), t["attn"]["median_ms"], ceiling)
-    res["c2"] = r
-    del x, calls
-    torch.cuda.empty_cache()
+    if only in (0, 2):
+        x, wins, vocab = attn_cfg(2, True)
+        par = torch.from_numpy(x.trees.parent).to(dev)
+        mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
+        calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev))]
+        t = time_calls(calls, reps, warm, flush)
+        r = _summary("c2", "B=8, N=32 leaf-sibling trees, Hq=16, Hkv=8, D=256, ctx 4096, bf16", x.B, x.N, calls, t)
+        r["roofline"] = _hbm_roof("tree_verify_attn", _kv_bytes(x, 0), t["attn"]["median_ms"], ceiling)
+        res["c2"] = r
+        del x, calls
+        torch.cuda.empty_cache()
 
     # c3: the headline step's layers, mask + window layer + global layer
-    xw, xg = step.layers
-    mo, mask = _mask_call(tv, step.parent, step.ctx_len, step.B, step.N, dev)
-    calls = [("mask", mask), ("attn_window", _attn_call(tv, xw, mo, xw.window, dev)),
-             ("attn_global", _attn_call(tv, xg, mo, xg.window, dev))]
-    t = time_calls(calls, reps, warm, flush)
-    r = _summary("c3", "B=32, N=32 spine-first trees, ctx U[1024,32768], Hq=16, Hkv=8, D=256, bf16; "
-                 "W=512 layer + global layer", step.B, step.N, calls, t)
-    bw, bg = _kv_bytes(xw, xw.window), _kv_bytes(xg, 0)
-    tw, tg = t["attn_window"]["median_ms"], t["attn_global"]["median_ms"]
-    r["roofline"] = {"pair": _hbm_roof("tree_verify_attn, window + global layer", bw + bg, tw + tg, ceiling),
-                     "window": _hbm_roof("tree_verify_attn, W=512", bw, tw, ceiling),
-                     "global": _hbm_roof("tree_verify_attn, global", bg, tg, ceiling)}
-    res["c3"] = r
-    del calls
+    if only in (0, 3):
+        xw, xg = step.layers
+        mo, mask = _mask_call(tv, step.parent, step.ctx_len, step.B, step.N, dev)
+        calls = [("mask", mask), ("attn_window", _attn_call(tv, xw, mo, xw.window, dev)),
+                 ("attn_global", _attn_call(tv, xg, mo, xg.window, dev))]
+        t = time_calls(calls, reps, warm, flush)
+        r = _summary("c3", "B=32, N=32 spine-first trees, ctx U[1024,32768], Hq=16, Hkv=8, D=256, bf16; "
+                     "W=512 layer + global layer", step.B, step.N, calls, t)
+        bw, bg = _kv_bytes(xw, xw.window), _kv_bytes(xg, 0)
+        tw, tg = t["attn_window"]["median_ms"], t["attn_global"]["median_ms"]
+        r["roofline"] = {"pair": _hbm_roof("tree_verify_attn, window + global layer", bw + bg, tw + tg, ceiling),
+                         "window": _hbm_roof("tree_verify_attn, W=512", bw, tw, ceiling),
+                         "global": _hbm_roof("tree_verify_attn, global", bg, tg, ceiling)}
+        res["c3"] = r
+        del calls
 
     # c4: DDTree batch, MFMA-bound attention and a 2.18 GB walk
-    x, wins, vocab = attn_cfg(4, True)
-    par = torch.from_numpy(x.trees.parent).to(dev)
-    mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
-    logits = W.walk_inputs(4, x.trees, vocab, torch.bfloat16, device=dev, on_device=True).logits
-    calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev)), ("walk", _walk_call(tv, x.trees, logits, dev))]
-    t = time_calls(calls, reps, warm, flush)
-    r = _summary("c4", "B=64, N=64 DDTree trees, Hq=64, Hkv=8, D=128, ctx 32768, bf16; logits [64,65,262144] bf16",
-                 x.B, x.N, calls, t)
-    fl = _attn_flops(x)
-    ta = t["attn"]["median_ms"]
-    tfl = fl / (ta * 1e-3) / 1e12
-    r["roofline"] = {"attn": {"kernel": "tree_verify_attn (wide-tile)", "bound": "mfma", "algorithmic_flops": fl,
-                              "achieved": round(tfl, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": round(tfl / BF16_MFMA_PEAK_TFLOPS, 4),
-                              "kv_GBps": round(_gbps(_kv_bytes(x, 0), ta), 1)},
-                     "walk": _hbm_roof("tree_walk_accept", logits.numel() * logits.element_size(),
-                                       t["walk"]["median_ms"], ceiling)}
-    res["c4"] = r
-    del x, logits, calls
-    torch.cuda.empty_cache()
+    if only in (0, 4):
+        x, wins, vocab = attn_cfg(4, True)
+        par = torch.from_numpy(x.trees.parent).to(dev)
+        mo, mask = _mask_call(tv, par, x.ctx_len, x.B, x.N, dev)
+        logits = W.walk_inputs(4, x.trees, vocab, torch.bfloat16, device=dev, on_device=True).logits
+        calls = [("mask", mask), ("attn", _attn_call(tv, x, mo, 0, dev)), ("walk", _walk_call(tv, x.trees, logits, dev))]
+        t = time_calls(calls, reps, warm, flush)
+        r = _summary("c4", "B=64, N=64 DDTree trees, Hq=64, Hkv=8, D=128, ctx 32768, bf16; logits [64,65,262144] bf16",
+                     x.B, x.N, calls, t)
+        fl = _attn_flops(x)
+        ta = t["attn"]["median_ms"]
+        tfl = fl / (ta * 1e-3) / 1e12
+        r["roofline"] = {"attn": {"kernel": "tree_verify_attn (wide-tile)", "bound": "mfma", "algorithmic_flops": fl,
+                                  "achieved": round(tfl, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tfl / BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "kv_GBps": round(_gbps(_kv_bytes(x, 0), ta), 1)},
+                         "walk": _hbm_roof("tree_walk_accept", logits.numel() * logits.element_size(),
+                                           t["walk"]["median_ms"], ceiling)}
+        res["c4"] = r
+        del x, logits, calls
+        torch.cuda.empty_cache()
 
     # c5: GDN tree verify
-    g = dict(CF.GDN[5])
-    gx = W.gdn_inputs(5, device=dev, **g)
-    par = torch.from_numpy(gx.trees.parent).to(dev)
-    ctx = torch.full((gx.B,), 1, dtype=torch.int32, device=dev)
-    mo, mask = _mask_call(tv, par, ctx, gx.B, gx.N, dev)
-    gout = torch.empty_like(gx.v)
-    calls = [("mask", mask),
-             ("gdn", lambda: tv.tree_gdn_verify(gx.q, gx.k, gx.v, gx.alpha, gx.beta, gx.S0, mo["anc"], out=gout))]
-    t = time_calls(calls, reps, warm, flush)
-    r = _summary("c5", "B=16, H=16, Dk=Dv=128, N=32 spine-first trees, bf16 q/k/v, fp32 gates and state",
-                 gx.B, gx.N, calls, t)
-    gbytes = sum(z.numel() * z.element_size() for z in (gx.q, gx.k, gx.v, gx.alpha, gx.beta, gx.S0, gout, mo["anc"]))
-    r["roofline"] = _hbm_roof("tree_gdn_verify", gbytes, t["gdn"]["median_ms"], ceiling)
-    res["c5"] = r
+    if only in (0, 5):
+        g = dict(CF.GDN[5])
+        gx = W.gdn_inputs(5, device=dev, **g)
+        par = torch.from_numpy(gx.trees.parent).to(dev)
+        ctx = torch.full((gx.B,), 1, dtype=torch.int32, device=dev)
+        mo, mask = _mask_call(tv, par, ctx, gx.B, gx.N, dev)
+        gout = torch.empty_like(gx.v)
+        calls = [("mask", mask),
+                 ("gdn", lambda: tv.tree_gdn_verify(gx.q, gx.k, gx.v, gx.alpha, gx.beta, gx.S0, mo["anc"], out=gout))]
+        t = time_calls(calls, reps, warm, flush)
+        r = _summary("c5", "B=16, H=16, Dk=Dv=128, N=32 spine-first trees, bf16 q/k/v, fp32 gates and state",
+                     gx.B, gx.N, calls, t)
+        gbytes = sum(z.numel() * z.element_size() for z in (gx.q, gx.k, gx.v, gx.alpha, gx.beta, gx.S0, gout, mo["anc"]))
+        r["roofline"] = _hbm_roof("tree_gdn_verify", gbytes, t["gdn"]["median_ms"], ceiling)
+        res["c5"] = r
+
     res["protocol"] = (f"per call: {warm} untimed then {reps} timed repetitions, each after writing "
                        f"{args.flush_mib} MiB and reading {args.flush_mib // 2} MiB on the same stream "
                        f"(outside the events); median, p10, p90 of the event-timed durations; "
@@ -721,6 +732,11 @@ def main():
     dev = torch.device("cuda:0")
     if args.attn_only:
         print(json.dumps(attn_only(args, dev)), flush=True)
+        return
+    if args.config:
+        step = Step(dev) if args.config == 3 else None
+        res = per_config(step, dev, args, None, only=args.config)
+        print(json.dumps({"config_only": args.config, **res}), flush=True)
         return
     log("building the headline step's inputs")
     step = Step(dev)

@@ -9,8 +9,15 @@
  *
  * Conventions shared by every entry point
  *  - Array arguments are DEVICE pointers owned by the caller; the library
- *    never allocates, frees or synchronises, and keeps no mutable global
- *    state.  Arrays are dense, row-major, in the layout stated per argument.
+ *    never allocates, frees or synchronises.  Arrays are dense, row-major, in
+ *    the layout stated per argument.
+ *  - State: the library keeps only per-device caches, filled on its first
+ *    call on a device and written with atomics (safe across host threads):
+ *    the device's compute-unit and XCD counts (which size some grids), flags
+ *    recording that the dynamic-LDS limit of a kernel was raised with
+ *    hipFuncSetAttribute on that device, and the device address of the static
+ *    scratch of tree_walk_accept_noalloc.  No call depends on an earlier
+ *    call's data.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call enqueues its kernels on that stream and returns at once.
  *  - Argument errors (null pointers, shapes, unsupported sizes or dtypes,

@@ -1705,7 +1705,7 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
 static_assert(TV_ATTN_PAIR_PM >= 500 && TV_ATTN_PAIR_PM < 1000, "pair weight");
 static_assert(TV_ATTN_XCD_PM >= 500 && TV_ATTN_XCD_PM <= 1500, "XCD weight");
 #ifndef TV_ATTN_STREAM_MIN_TILES
-#define TV_ATTN_STREAM_MIN_TILES 16  // key tiles per stream workgroup at least
+#define TV_ATTN_STREAM_MIN_TILES 16  // key tiles per stream workgroup while the grid fills the chip
 #endif
 
 int device_cus() {
@@ -1716,6 +1716,18 @@ int device_cus() {
   if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+int device_xcds() {
+  static std::atomic<int> cached[64];  // zero-initialised (static storage)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) n = -1;
     cached[dev].store(n, std::memory_order_relaxed);
   }
   return n;
@@ -1735,12 +1747,21 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int wi
       units * ((static_cast<long long>(max_ctx_len) + kTile - 1) / kTile + (N + kTile - 1) / kTile);
   if (TV_ATTN_STREAM_WG_PER_CU > 0 && window <= 0 && p.row_groups == 1 && B >= 1 && B <= kMaxSeqs && tiles < (1ll << 30)) {
     long long wg = static_cast<long long>(TV_ATTN_STREAM_WG_PER_CU) * device_cus();
-    const long long by_work = (tiles + TV_ATTN_STREAM_MIN_TILES - 1) / TV_ATTN_STREAM_MIN_TILES;
+    // tiles per workgroup: at least TV_ATTN_STREAM_MIN_TILES while the grid
+    // fills the chip (the partials stay small next to the keys streamed);
+    // fewer, down to 2, for small batches, whose time is latency
+    long long per = (tiles + wg - 1) / wg;
+    if (per > TV_ATTN_STREAM_MIN_TILES) per = TV_ATTN_STREAM_MIN_TILES;
+    if (per < 2) per = 2;
+    const long long by_work = (tiles + per - 1) / per;
     if (wg > by_work) wg = by_work;
     if (wg < 1) wg = 1;
     p.stream_wg = static_cast<int>(wg);
-    // a full grid of two workgroups per CU pairs workgroup w with w + CUs
-    const bool full = TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus();
+    // a full grid of two workgroups per CU pairs workgroup w with w + CUs; the
+    // pair and XCD weights were measured on 256 CUs in 8 XCDs and apply only
+    // there (equal shares elsewhere)
+    const bool full = TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus() && device_cus() == 256 &&
+                      device_xcds() == 8;
     p.stream_pm = full ? TV_ATTN_PAIR_PM : 500;
     p.stream_xm = full ? TV_ATTN_XCD_PM : 1000;
     p.nsplit = 1;

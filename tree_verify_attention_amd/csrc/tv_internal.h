@@ -32,6 +32,10 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // when no device can be queried, e.g. for a size query on a host without one)
 int device_cus();
 
+// XCDs (accelerator complex dies) of the current device, -1 when the runtime
+// does not say, 0 without a device
+int device_xcds();
+
 // ---- launchers (one per kernel family); return the launch error
 hipError_t launch_mask(const int32_t* parent, const int32_t* depth_in, const int32_t* ctx_len,
                        int B, int N, uint64_t* anc, int32_t* depth_out, int32_t* pos,
