@@ -84,14 +84,17 @@ struct Cfg {
   static_assert(kInstPerWave * (2 * kSlots - 1) <= 63, "vmcnt range");
 };
 
-// XOR key of a row's 16-byte granules.  Rows 0..7 of every 16 get the even
-// keys 0, 2, .., 14 and rows 8..15 the odd ones: the K operand reads (16 rows,
-// one granule each) and the V transpose reads (4 rows, two adjacent granules
-// each, per 16 lanes) then fall on distinct LDS banks.
+// XOR key of a row's 16-byte granules: key(r) = 4 r0 ^ 8 r1 ^ 15 r2 ^ 6 r3 over
+// the bits of r mod 16 (a bijection).  Chosen by timing every invertible
+// linear key on gfx950: with it the K operand reads (16 rows, one granule each,
+// ds_read_b128), the V transpose reads (4 rows, two adjacent granules each, per
+// 16 lanes) and the fp32 V reads all run without bank conflicts, where the
+// key r0..r3 -> r1 r2 r3 r0 made every K read a two-way conflict.
 template <typename T, int D>
 __device__ __forceinline__ int swz_key(int row) {
   using C = Cfg<T, D>;
-  return ((((row & 7) << 1) | ((row >> 3) & 1))) & C::kSwz;
+  const int k = ((row & 3) << 2) ^ ((row & 4) ? 15 : 0) ^ ((row & 8) ? 6 : 0);
+  return k & C::kSwz;
 }
 
 // Byte offset of (row, byte) in a tile slot under that swizzle.
