@@ -37,8 +37,14 @@ def flags() -> list:
     ]
 
 
+# per-source additions.  The attention kernels take row maxima of matrix-core
+# results, which no NaN reaches unless the inputs hold one: without NaN
+# semantics the compiler drops the quieting of each operand before a max.
+EXTRA_FLAGS = {"tv_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, obj: str, verbose: bool):
-    cmd = [hipcc(), *flags(), "-c", "-o", obj, src]
+    cmd = [hipcc(), *flags(), *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", "-o", obj, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     return subprocess.run(cmd, capture_output=True, text=True)

@@ -57,6 +57,7 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // kTeams teams of kWaves waves share a workgroup: a ring stage holds kTeams
 // consecutive 32-key tiles, team i computes the i-th, and the teams' softmax
@@ -123,6 +124,19 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds) {
 // element (i & 3) of the 8-byte rows addressed by lanes 4j + (i >> 2), j = 0..3.
 __device__ __forceinline__ s16x4_t lds_read_tr16(const unsigned char* p) {
   auto lp = (__attribute__((address_space(3))) bf16x4_t*)(p);
+  return __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+// 32-bit LDS address of a shared array, and reads at such an address
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const unsigned char*)(p)));
+}
+__device__ __forceinline__ u32x4_t lds_u4(uint32_t a) {
+  return *(__attribute__((address_space(3))) const u32x4_t*)(static_cast<uintptr_t>(a));
+}
+__device__ __forceinline__ s16x4_t lds_tr16(uint32_t a) {
+  auto lp = (__attribute__((address_space(3))) bf16x4_t*)(static_cast<uintptr_t>(a));
   return __builtin_bit_cast(s16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
 
@@ -206,6 +220,13 @@ __device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// an empty asm that takes v in and out of a register: v is computed before
+// this point and not moved past it
+template <typename V>
+__device__ __forceinline__ void pin(V& v) {
+  asm volatile("" : "+v"(v));
+}
 
 // The values of lanes l and l ^ S (S = 16 or 32), through the gfx950 lane-swap
 // instructions (VALU, no LDS round trip): the two results hold exactly that
@@ -807,16 +828,34 @@ __device__ __forceinline__ void wide_row_store(bool final_out, const f32x4_t* ac
 // the softmax runs once per stage.  Same work units (unit, row group, split),
 // masking and partials as the per-unit layout; bf16 inputs.
 //
-// Eight waves, two per SIMD, in two groups: waves 0-3 and 4-7 (one of each
-// per SIMD) take the three steps of a stage -- scores (MFMA), softmax (VALU),
-// P.V (MFMA) -- in opposite orders.  In iteration i, group 0 runs P.V of
-// stage i - 1, then the scores and the softmax of stage i; group 1 runs the
-// softmax of stage i - 1, then P.V of stage i - 1 and the scores of stage i.
-// So on every SIMD one wave's softmax runs while the other wave's products
-// keep the matrix unit busy.  One barrier per stage: behind it the keys of
-// stage i and the values of stage i - 1 have landed, and every wave is done
-// with the keys of stage i - 1 and the values of stage i - 2, whose slots are
-// refilled at once.
+// This layout is bound by the matrix and vector units, which on gfx950 issue
+// to one SIMD nearly one after the other: every vector instruction adds to
+// the stage time.  P therefore enters P.V as one bf16 product (the per-unit
+// layout, bound by HBM, also carries P's rounding residual), and the softmax
+// sums come from the matrix unit: P times a tile of ones, accumulated and
+// rescaled like the output, so each row is normalised by the sum of exactly
+// the bf16 weights its output was formed with.  The softmax reference
+// follows each row's running maximum exactly, so a row's largest weight is
+// 1 and rounds without error: rows dominated by a few keys, whose outputs
+// stand far above the batch's RMS, keep their error small.  Against exact
+// arithmetic the output then differs by the relative rounding of the other
+// weights (2^-9), which averages out over the keys: under 1% of the output's
+// RMS on N(0, 1) inputs.
+//
+// All eight waves (two per SIMD) run one software pipeline.  Iteration i
+// forms the scores of stage i, then runs the P.V products of stage i - 1
+// with the softmax of stage i spread between them, a few work items per
+// product step: a wave issues vector instructions only every few cycles, so
+// the softmax is hidden in the gaps of its own matrix stream rather than in
+// another wave's (the two waves of a SIMD keep the matrix unit fed between
+// them).  P.V walks the key tiles in order, so the bf16 probabilities of
+// stage i's first key tile overwrite stage i - 1's once its products are
+// done and the last key tile's follow the products: one probability buffer.
+// A move of a row's softmax reference rescales the accumulators after that
+// stage's products.  One barrier per stage: behind it the keys of stage i
+// and the values of stage i - 1 have landed, and every wave is done with
+// the keys of stage i - 1 and the values of stage i - 2, whose slots each
+// wave refills with its share of the loads.
 template <int D>
 constexpr int wide_tiles() {
   return D == 256 ? 1 : 2;
@@ -843,18 +882,17 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
   constexpr int kSB = kKT * C::kTileBytes;               // bytes of a stage (keys or values)
   constexpr int kFitW = 131072 / (2 * kSB);
   constexpr int kSlots = kFitW > 6 ? 6 : kFitW;
-  // the waves of group 0 issue every load (group 1 carries the longer chain
-  // of an iteration): kIPW 1 KB loads per loading wave and stage
-  constexpr int kLW = kW / 2;
-  constexpr int kIPW = kSB / 1024 / kLW;
+  // every wave issues kIPW 1 KB loads per stage (keys or values)
+  constexpr int kIPW = kSB / 1024 / kW;
   static_assert(kSlots >= 3, "the ring holds the keys of stage i + 1 while stage i is in use");
-  static_assert(kIPW >= 1 && kIPW * 1024 * kLW == kSB, "stage must split over the loading waves");
+  static_assert(kIPW >= 1 && kIPW * 1024 * kW == kSB, "stage must split over the waves");
   static_assert(kIPW * (2 * kSlots - 1) <= 63, "vmcnt range");
   constexpr int kQ = D / 32;  // k steps of the score products
   __shared__ __align__(1024) unsigned char kring[kSlots * kSB];
   __shared__ __align__(1024) unsigned char vring[kSlots * kSB];
   __shared__ int s_pages[kSplitPages];
   __shared__ int s_pos[TV_MAX_NODES];
+  __shared__ uint64_t s_anc[TV_MAX_NODES][kAncW];
   __shared__ int2 s_rng;
 
   // work units as in the per-unit layout: split-major, XCD-interleaved, the
@@ -871,38 +909,36 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
 
-  // rows R = (rg kW + wave) 16 kRT + 16 rt + lr; their queries, positions and
-  // ancestor words go out with the context length
+  // rows R = (rg kW + wave) 16 kRT + 16 rt + lr (node R / G); their queries
+  // go out with the context length, the tree's positions and ancestor words
+  // to LDS (read only by masked stages)
   const int ctx_raw = ctx_len[b];
-  int Rr[kRT];
+  int Rr[kRT], tn[kRT];
   bool ok[kRT];
   bf16x8_t qf[kRT][kQ];
-  int rpos[kRT];
-  uint64_t ranc[kRT][kAncW];
   const int nw = (N + 63) / 64;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     Rr[rt] = (rg * kW + wave) * 16 * kRT + 16 * rt + lr;
     ok[rt] = Rr[rt] < rows;
-    const int t = ok[rt] ? Rr[rt] / G : 0;
+    tn[rt] = ok[rt] ? Rr[rt] / G : 0;
     const int hl = ok[rt] ? Rr[rt] % G : 0;
-    const size_t qoff = ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D;
+    const size_t qoff = ((static_cast<size_t>(b) * N + tn[rt]) * Hq + g * G + hl) * D;
 #pragma unroll
     for (int ks = 0; ks < kQ; ++ks) {
       const uint4 v = ok[rt] ? *reinterpret_cast<const uint4*>(q + qoff + ks * 32 + lg * 8)
                              : make_uint4(0, 0, 0, 0);
       qf[rt][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
-    rpos[rt] = pos_b[t];
-#pragma unroll
-    for (int w = 0; w < kAncW; ++w)
-      ranc[rt][w] = w < nw ? anc[(static_cast<size_t>(b) * N + t) * nw + w] : 0ull;
   }
   if (tid < TV_MAX_NODES) s_pos[tid] = tid < N ? pos_b[tid] : 0;
+  for (int i = tid; i < TV_MAX_NODES * kAncW; i += kNT) {
+    const int t = i / kAncW, w = i % kAncW;
+    s_anc[t][w] = (t < N && w < nw) ? anc[(static_cast<size_t>(b) * N + t) * nw + w] : 0ull;
+  }
   const int2 prng = tree_pos_range(pos_b, N, &s_rng);
   const SeqPlan sp = seq_plan(ctx_raw, max_ctx, window, prng.x, nsplit_max, split_tokens);
   if (s >= sp.nsplit) return;  // uniform over the workgroup
@@ -921,18 +957,17 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
   for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
     for (int ks = 0; ks < kQ; ++ks) asm volatile("" ::"v"(qf[rt][ks]));
-    asm volatile("" ::"v"(rpos[rt]));
-#pragma unroll
-    for (int w = 0; w < kAncW; ++w) asm volatile("" ::"v"(ranc[rt][w]));
   }
-  f32x4_t acc[kRT][C::kDT];
-  float m_run[kRT], l_run[kRT];
+  // acc: O^T column tiles; acc_l: the product of P with a tile of ones, whose
+  // every element is the row's softmax sum over the same bf16 probabilities
+  f32x4_t acc[kRT][C::kDT], acc_l[kRT];
+  float m_run[kRT];
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc_l[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run[rt] = -INFINITY;
-    l_run[rt] = 0.0f;
   }
   // stages: context keys [k0, k1) in stages of kSK, then the node keys
   const int nctx = k1 > k0 ? (k1 - k0 + kSK - 1) / kSK : 0;
@@ -946,106 +981,136 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
   __syncthreads();  // page cache ready
 
   // Loads of stage keys (or values) into their slot: stage row r is row r % 32
-  // of tile r / 32, swizzled as in the per-unit layout.  Lane data of load j
-  // (group 0): its stage row and granule, fixed for the whole stream.
-  const int lwave = wave % kLW;
-  int ld_row[kIPW], ld_part[kIPW];
+  // of tile r / 32, swizzled as in the per-unit layout.  Load j of a wave
+  // fills the 1 KB block wave kIPW + j of the slot: its lane takes granule
+  // (gl % kGran) ^ key of stage row gl / kGran, gl = (wave kIPW + j) 64 + lane.
+  // Lane coordinates are formed where they are used, from a copy of the lane
+  // index the compiler cannot see through, so that no part of the address
+  // arithmetic is hoisted into registers held across the stream.
+  auto opaque_lane = [&]() __attribute__((always_inline)) {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  auto ld_row = [&](int j, int l) __attribute__((always_inline)) {
+    return ((wave * kIPW + j) * 64 + l) / C::kGran;
+  };
+  auto ld_gran = [&](int j, int l) __attribute__((always_inline)) {
+    const int r = ld_row(j, l);
+    return ((((wave * kIPW + j) * 64 + l) % C::kGran) ^ swz_key<T, D>(r));
+  };
+  // the loads of one half (values or keys) of stage st, issued at once, each
+  // lane's page read from the cache (any stage: partial, windowed or nodes)
+  auto issue_stage = [&](int st, bool values) __attribute__((always_inline)) {
+    if (st >= ntiles) return;
+    const bool is_node = st >= nctx;
+    const int base = is_node ? (st - nctx) * kSK : k0 + st * kSK;
+    const int lim = is_node ? N : k1;
+    const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
+    unsigned char* dst = (values ? vring : kring) + (st % kSlots) * kSB;
+    const int l = opaque_lane();
+    int key[kIPW], page[kIPW];
 #pragma unroll
-  for (int j = 0; j < kIPW; ++j) {
-    const int gl = (lwave * kIPW + j) * 64 + lane;
-    ld_row[j] = gl / C::kGran;
-    ld_part[j] = (gl % C::kGran) ^ swz_key<T, D>(ld_row[j]);
-  }
-  // the values of stage sv and the keys of stage sk (either may lie past the
-  // stream, then it is skipped): every page index is read from LDS first, so
-  // that one wait covers all of them (splits are capped so that every page of
-  // a split is in the cache)
+    for (int j = 0; j < kIPW; ++j) {
+      key[j] = min(base + ld_row(j, l), lim - 1);
+      page[j] = s_pages[min(max((key[j] >> 4) - p0, 0), kSplitPages - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kIPW; ++j) {
+      const size_t off =
+          is_node ? ((static_cast<size_t>(b) * N + key[j]) * Hkv + g) * C::kRowBytes
+                  : ((static_cast<size_t>(page[j]) * Hkv + g) * 16 + (key[j] & 15)) * C::kRowBytes;
+      lds_dma16(src + off + ld_gran(j, l) * 16, dst + (wave * kIPW + j) * 1024);
+    }
+  };
   auto refill = [&](int sv, int sk) __attribute__((always_inline)) {
-    if (grp != 0) return;
-    const int st[2] = {sv, sk};
-    int key[2][kIPW], page[2][kIPW];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const bool is_node = st[q] >= nctx;
-      const int base = is_node ? (st[q] - nctx) * kSK : k0 + st[q] * kSK;
-      const int lim = is_node ? N : k1;
-#pragma unroll
-      for (int j = 0; j < kIPW; ++j) {
-        key[q][j] = min(base + ld_row[j], lim - 1);
-        page[q][j] = s_pages[min(max((key[q][j] >> 4) - p0, 0), kSplitPages - 1)];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (st[q] >= ntiles) continue;
-      const bool values = q == 0;
-      unsigned char* dst = (values ? vring : kring) + (st[q] % kSlots) * kSB;
-      const bool is_node = st[q] >= nctx;
-      const unsigned char* src = is_node ? (values ? vnb : knb) : (values ? vcb : kcb);
-#pragma unroll
-      for (int j = 0; j < kIPW; ++j) {
-        const size_t off =
-            is_node ? ((static_cast<size_t>(b) * N + key[q][j]) * Hkv + g) * C::kRowBytes
-                    : ((static_cast<size_t>(page[q][j]) * Hkv + g) * 16 + (key[q][j] & 15)) * C::kRowBytes;
-        lds_dma16(src + off + ld_part[j] * 16, dst + (lwave * kIPW + j) * 1024);
-      }
-    }
+    issue_stage(sv, true);
+    issue_stage(sk, false);
     asm volatile("" ::: "memory");
   };
 
-  // The same loads, prepared (page lookups and addresses) right after the
-  // barrier and issued one by one between the products of P.V, so that no
-  // issue stalls on a full memory pipeline: load q of the prepared set is
-  // value load q (q < kIPW), then key load q - kIPW.
-  const unsigned char* pre_src[2 * kIPW];
-  bool pre_on[2];  // per half: the stage lies inside the stream
-  int pre_dst[2];  // LDS byte offset of the half's slot (+ the wave's blocks)
+  // The steady-state refills (values of stage sv, keys of stage sk), set up
+  // right after the scores.  A context stage that lies wholly inside the
+  // split and starts on a page boundary gives each wave rows of a single
+  // page: its page base is one wave-uniform value and each load adds its
+  // lane's offset inside the page.  When both halves are such stages their
+  // loads are issued one by one between the products of P.V (load q is
+  // value load q for q < kIPW, then key load q - kIPW), so that no issue
+  // stalls on a full memory pipeline; otherwise they all go out at once.
+  constexpr int kRowsW = kIPW * 64 / C::kGran;  // stage rows one wave fills
+  static_assert(kRowsW <= 16 && 16 % kRowsW == 0, "a wave's rows share a page");
+  const unsigned char* pre_base[2];  // per half: the page base (wave-uniform)
+  int pre_dst[2];                    // LDS byte offset of the half's slot
+  int page_off[kIPW];  // load j's byte offset inside a page (row and granule)
+#pragma unroll
+  for (int j = 0; j < kIPW; ++j) page_off[j] = (ld_row(j, lane) & 15) * C::kRowBytes + ld_gran(j, lane) * 16;
+  auto issue_prepared = [&](int q) __attribute__((always_inline)) {
+    const int half = q / kIPW, j = q % kIPW;
+    const int off = page_off[j];
+    unsigned char* dst = (half == 0 ? vring : kring) + pre_dst[half] + (wave * kIPW + j) * 1024;
+    lds_dma16(pre_base[half] + off, dst);
+  };
+  // returns whether the loads are left to P.V
   auto prepare = [&](int sv, int sk) __attribute__((always_inline)) {
     const int st[2] = {sv, sk};
+    bool fast[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
+      pre_dst[q] = (st[q] % kSlots) * kSB;
       const bool is_node = st[q] >= nctx;
       const int base = is_node ? (st[q] - nctx) * kSK : k0 + st[q] * kSK;
       const int lim = is_node ? N : k1;
-      const unsigned char* src = is_node ? (q == 0 ? vnb : knb) : (q == 0 ? vcb : kcb);
-      pre_on[q] = st[q] < ntiles;
-      pre_dst[q] = (st[q] % kSlots) * kSB;
-#pragma unroll
-      for (int j = 0; j < kIPW; ++j) {
-        const int key = min(base + ld_row[j], lim - 1);
-        const int page = s_pages[min(max((key >> 4) - p0, 0), kSplitPages - 1)];
-        const size_t off = is_node ? ((static_cast<size_t>(b) * N + key) * Hkv + g) * C::kRowBytes
-                                   : ((static_cast<size_t>(page) * Hkv + g) * 16 + (key & 15)) * C::kRowBytes;
-        pre_src[q * kIPW + j] = src + off + ld_part[j] * 16;
+      fast[q] = st[q] < ntiles && !is_node && (base & 15) == 0 && base + kSK <= lim;
+      pre_base[q] = kcb;
+      if (fast[q]) {
+        const int page = __builtin_amdgcn_readfirstlane(
+            s_pages[((base + wave * kRowsW) >> 4) - p0]);
+        pre_base[q] = (q == 0 ? vcb : kcb) +
+                      (static_cast<size_t>(page) * Hkv + g) * (16 * C::kRowBytes);
       }
     }
-  };
-  auto issue_prepared = [&](int q) __attribute__((always_inline)) {
-    const int half = q / kIPW, j = q % kIPW;
-    if (!pre_on[half]) return;
-    unsigned char* dst = (half == 0 ? vring : kring) + pre_dst[half] + (lwave * kIPW + j) * 1024;
-    lds_dma16(pre_src[q], dst);
+    if (fast[0] && fast[1]) return true;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (fast[q]) {
+#pragma unroll
+        for (int j = 0; j < kIPW; ++j) issue_prepared(q * kIPW + j);
+      } else {
+        issue_stage(st[q], q == 0);
+      }
+    }
+    asm volatile("" ::: "memory");
+    return false;
   };
 
-  f32x4_t S[kRT][2 * kKT];               // scores of a stage, from its products to its softmax
-  bf16x8_t ph[kRT][kKT], pl[kRT][kKT];  // its probabilities, from the softmax to P.V
+  // Operand reads address the ring by 32-bit LDS offsets.  The swizzle XORs
+  // only the granule bits of a row, and the slots are 1 KB aligned, so the
+  // granule steps of a lane's reads are XORs on one lane base: k step ks adds
+  // 4 ks to the granule (XOR ks << 6), column tile dt adds 2 dt (XOR dt << 5);
+  // the second 16 rows and the second key tile are plain offsets.
+  static_assert(4 * (kQ - 1) < C::kGran && 2 * (C::kDT - 1) < C::kGran, "steps stay in the row");
+  const uint32_t kring_a = lds_addr(kring), vring_a = lds_addr(vring);
+  const uint32_t k_lane = swz<T, D>(lr, lg * 16);
+  const uint32_t v_lane = swz<T, D>(4 * lg + (lr >> 2), 8 * (lr & 3));
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  f32x4_t S[kRT][2 * kKT];  // scores of a stage, from its products to its softmax
+  bf16x8_t ph[kRT][kKT];  // its probabilities in bf16
 
   // S^T of every row tile for the 16-key quarters of stage `it`: the key
   // fragments of a k step are read once (two k steps ahead) and feed all kRT
   // row tiles
   auto scores = [&](int it) __attribute__((always_inline)) {
-    const unsigned char* Ks = kring + (it % kSlots) * kSB;
+    const uint32_t kb = kring_a + (it % kSlots) * kSB + k_lane;
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
       for (int h = 0; h < 2 * kKT; ++h) S[rt][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
-      const unsigned char* Kt = Ks + kt * C::kTileBytes;
       constexpr int kAh = kQ < 2 ? kQ : 2;
-      uint4 ka[kAh + 1][2];
+      u32x4_t ka[kAh + 1][2];
       auto kread = [&](int ks, int j) __attribute__((always_inline)) {
-        return *reinterpret_cast<const uint4*>(Kt + swz<T, D>(16 * j + lr, ks * 64 + lg * 16));
+        return lds_u4((kb ^ (ks << 6)) + j * 16 * C::kRowBytes + kt * C::kTileBytes);
       };
 #pragma unroll
       for (int ks = 0; ks < kAh; ++ks) {
@@ -1071,121 +1136,152 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     }
   };
 
-  // mask and online softmax of stage `it` in the log2 domain.  Masks run only
-  // on partial stages, as one straight block per kind of stage.  The scale is
-  // positive, so row maxima are taken on the raw scores and the scale folds
-  // into one fma per score.  The reference point m moves only when a stage
-  // maximum passes it by more than kLazy (always from -inf): probabilities
-  // stay below 2^kLazy and most stages skip the rescale of the accumulators.
-  // P goes to bf16 high and low parts, pairs at a time (keys 16 h + 4 lg + i).
-  auto softmax = [&](int it) __attribute__((always_inline)) {
+  // Softmax of stage `it` in the log2 domain, as work items that P.V spreads
+  // over its steps.  Masks run only on partial stages, as one straight block
+  // per kind of stage, before the products.  The scale is positive, so row
+  // maxima are taken on the raw scores and the scale folds into one fma per
+  // score.  The reference point m is the row's running maximum: weights are
+  // at most 1, and a wave rescales its accumulators only on stages where
+  // some row's maximum grew (a few percent of a long stream).  P goes to
+  // bf16 pairs at a time (keys 16 h + 4 lg + i).
+  float sv[kRT][2 * kKT][4];  // the stage's (masked) raw scores, then its probabilities
+  float alpha[kRT], neg_m[kRT];
+  bool need[kRT];
+  auto mask_scores = [&](int it) __attribute__((always_inline)) {
     const bool is_node = it >= nctx;
     const int base = is_node ? (it - nctx) * kSK : k0 + it * kSK;
     const int lim = is_node ? N : k1;
     const bool full = !is_node && base + kSK <= lim &&
                       (window <= 0 || (base >= win_all && base + kSK - 1 <= prng.x));
-    float sv[kRT][2 * kKT][4];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
       for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[rt][h][i] = S[rt][h][i];
-    if (!full) {
-      if (is_node) {
+    if (full) return;
+    if (is_node) {
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-          const uint64_t aw = anc_word(ranc[rt], base);  // a stage lies within one word
+      for (int rt = 0; rt < kRT; ++rt) {
+        const int rpos = s_pos[tn[rt]];
+        const uint64_t aw = s_anc[tn[rt]][(base >> 6) & (kAncW - 1)];  // a stage lies within one word
 #pragma unroll
-          for (int h = 0; h < 2 * kKT; ++h)
+        for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = base + 16 * h + 4 * lg + i;
-              const int dpos = rpos[rt] - s_pos[key & (TV_MAX_NODES - 1)];
-              bool vis = ok[rt] & (key < lim) & (((aw >> (key & 63)) & 1ull) != 0ull);
-              vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-              sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
-            }
-        }
-      } else {
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + 16 * h + 4 * lg + i;
+            const int dpos = rpos - s_pos[key & (TV_MAX_NODES - 1)];
+            bool vis = ok[rt] & (key < lim) & (((aw >> (key & 63)) & 1ull) != 0ull);
+            vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+            sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+          }
+      }
+    } else {
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
+      for (int rt = 0; rt < kRT; ++rt) {
+        const int rpos = s_pos[tn[rt]];
 #pragma unroll
-          for (int h = 0; h < 2 * kKT; ++h)
+        for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = base + 16 * h + 4 * lg + i;
-              const int dpos = rpos[rt] - key;
-              bool vis = ok[rt] & (key < lim);
-              vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-              sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
-            }
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + 16 * h + 4 * lg + i;
+            const int dpos = rpos - key;
+            bool vis = ok[rt] & (key < lim);
+            vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
+            sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+          }
       }
     }
+  };
+  // Work items.  Phase 1: the kRT row maxima, then per key tile and row tile
+  // the two exponential quarters of that tile.  Phase 2: the bf16 conversion
+  // of key tile 0 (into the buffer P.V has finished with), and phase 3, after
+  // the products, that of the last key tile.
+  constexpr int kN1 = kRT + 2 * kKT * kRT;
+  auto item_max = [&](int rt) __attribute__((always_inline)) {
+    float mt = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2 * kKT; ++h)
+      mt = fmaxf(mt, fmaxf(fmaxf(sv[rt][h][0], sv[rt][h][1]), fmaxf(sv[rt][h][2], sv[rt][h][3])));
+    mt = pair_max<32>(pair_max<16>(mt));
+    const float mc = mt * scale_log2;
+    need[rt] = mc > m_run[rt];
+    // rows that keep their reference scale by exactly 1 (also rows still
+    // at -inf, where the difference of references would be NaN)
+    alpha[rt] = need[rt] ? fast_exp2(m_run[rt] - mc) : 1.0f;  // 0 from -inf
+    m_run[rt] = need[rt] ? mc : m_run[rt];
+    neg_m[rt] = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
+    pin(alpha[rt]);
+    pin(neg_m[rt]);
+  };
+  auto item_exp = [&](int rt, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[rt][h][i] = fast_exp2(fmaf(sv[rt][h][i], scale_log2, neg_m[rt]));
+      pin(sv[rt][h][i]);
+    }
+  };
+  auto item_split = [&](int rt, int kt) __attribute__((always_inline)) {
+    uint32_t hw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // fragment elements 2e, 2e + 1: quarter 2 kt + e / 2, keys 4 lg + 2 (e % 2) + 0, 1
+      const f32x2_t f = {sv[rt][2 * kt + e / 2][2 * (e % 2)], sv[rt][2 * kt + e / 2][2 * (e % 2) + 1]};
+      hw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+    }
+    ph[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    pin(ph[rt][kt]);
+  };
+  // phase-1 item w (an item's results are pinned where it runs, so that the
+  // compiler keeps the items between the product steps they were placed in)
+  auto item1 = [&](int w) __attribute__((always_inline)) {
+    if (w < kRT) {
+      item_max(w);
+    } else {
+      const int kt = (w - kRT) / (2 * kRT), r = (w - kRT) % (2 * kRT);
+      item_exp(r / 2, 2 * kt + r % 2);
+    }
+  };
+  auto soft_all = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < kN1; ++w) item1(w);
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) item_split(rt, kt);
+  };
+  // a row's reference moved: its accumulators and sum follow (after the
+  // products of the previous stage)
+  auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-      float mt = -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(need[rt]) != 0ull) {
 #pragma unroll
-      for (int h = 0; h < 2 * kKT; ++h)
-        mt = fmaxf(mt, fmaxf(fmaxf(sv[rt][h][0], sv[rt][h][1]), fmaxf(sv[rt][h][2], sv[rt][h][3])));
-      mt = pair_max<32>(pair_max<16>(mt));
-      const float mc = mt * scale_log2;
-      const bool need = mc > m_run[rt] + kLazy;
-      if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-        // rows that keep their reference scale by exactly 1 (also rows still
-        // at -inf, where the difference of references would be NaN)
-        const float alpha = need ? fast_exp2(m_run[rt] - mc) : 1.0f;  // 0 from -inf
-        l_run[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha;
-        m_run[rt] = need ? mc : m_run[rt];
-      }
-      const float neg_m = m_run[rt] == -INFINITY ? 0.0f : -m_run[rt];
-      float ps = 0.0f;
-      float pv[2 * kKT][4];
-#pragma unroll
-      for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[h][i] = fast_exp2(fmaf(sv[rt][h][i], scale_log2, neg_m));
-          ps += pv[h][i];
-        }
-      l_run[rt] += ps;
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        uint32_t hw[4], lw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // fragment elements 2e, 2e + 1: quarter 2 kt + e / 2, keys 4 lg + 2 (e % 2) + 0, 1
-          const float a0 = pv[2 * kt + e / 2][2 * (e % 2)];
-          const float a1 = pv[2 * kt + e / 2][2 * (e % 2) + 1];
-          const f32x2_t f = {a0, a1};
-          hw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-          const f32x2_t r = {a0 - __uint_as_float(hw[e] << 16), a1 - __uint_as_float(hw[e] & 0xffff0000u)};
-          lw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
-        }
-        ph[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-        pl[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        for (int dt = 0; dt < C::kDT; ++dt) acc[rt][dt] *= alpha[rt];
+        acc_l[rt] *= alpha[rt];
       }
     }
   };
 
-  // O^T += V^T P^T for stage `it`, one 32-key tile at a time: the value
-  // fragments of a column tile feed all row tiles; reads run two steps ahead
-  auto pv_product = [&](int it, bool with_loads) __attribute__((always_inline)) {
-    const unsigned char* Vs = vring + (it % kSlots) * kSB;
-    const int vrow = 4 * lg + (lr >> 2);
-    const int vcol = 8 * (lr & 3);
-    constexpr int kSteps = C::kDT * kKT;  // (column tile, key tile) pairs
+  // O^T += V^T P^T for stage `it`, key tile by key tile: the value fragments
+  // of a column tile feed all row tiles; reads run two steps ahead.  With
+  // `soft`, the softmax of the next stage runs in the gaps: phase 1 over the
+  // first kS1 steps, phase 2 (key tile 0's conversion, once key tile 0 is done)
+  // over the rest, phase 3 after the last step.
+  constexpr int kSteps = C::kDT * kKT;  // (key tile, column tile) pairs
+  constexpr int kS1 = kKT == 2 ? kSteps - C::kDT / 2 : kSteps;
+  static_assert(kKT == 1 || kS1 >= C::kDT, "key tile 0 is done before its split");
+  auto pv_product = [&](int it, bool with_loads, bool soft) __attribute__((always_inline)) {
+    const uint32_t vb = vring_a + (it % kSlots) * kSB + v_lane;
     constexpr int kVA = 2;
     constexpr int kEvery = kSteps / (2 * kIPW);  // steps per prepared load
     static_assert(kEvery >= 1 && kEvery * 2 * kIPW == kSteps, "prepared loads spread over the steps");
     s16x4_t vlo[kVA + 1], vhi[kVA + 1];
     auto vread = [&](int st, s16x4_t& lo, s16x4_t& hi) __attribute__((always_inline)) {
-      const int dt = st / kKT, kt = st % kKT;
-      const unsigned char* Vt = Vs + kt * C::kTileBytes;
-      lo = lds_read_tr16(Vt + swz<T, D>(vrow, dt * 32 + vcol));
-      hi = lds_read_tr16(Vt + swz<T, D>(16 + vrow, dt * 32 + vcol));
+      const int kt = st / C::kDT, dt = st % C::kDT;
+      const uint32_t a = (vb ^ (dt << 5)) + kt * C::kTileBytes;
+      lo = lds_tr16(a);
+      hi = lds_tr16(a + 16 * C::kRowBytes);
     };
 #pragma unroll
     for (int st = 0; st < kVA; ++st) vread(st, vlo[st], vhi[st]);
@@ -1193,7 +1289,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     for (int st = 0; st < kSteps; ++st) {
       if (st + kVA < kSteps) vread(st + kVA, vlo[(st + kVA) % (kVA + 1)], vhi[(st + kVA) % (kVA + 1)]);
       __builtin_amdgcn_sched_barrier(0);
-      const int dt = st / kKT, kt = st % kKT;
+      const int kt = st / C::kDT, dt = st % C::kDT;
       const s16x4_t lo = vlo[st % (kVA + 1)];
       const s16x4_t hi = vhi[st % (kVA + 1)];
       const s16x8_t av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -1201,12 +1297,28 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt][kt], acc[rt][dt], 0, 0, 0);
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt][kt], acc[rt][dt], 0, 0, 0);
+        // the row sums, once per key tile
+        if (dt == C::kDT - 1)
+          acc_l[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph[rt][kt], acc_l[rt], 0, 0, 0);
       }
       if (with_loads && st % kEvery == kEvery - 1) issue_prepared(st / kEvery);
+      if (soft) {
+        if (st < kS1) {
+#pragma unroll
+          for (int w = st * kN1 / kS1; w < (st + 1) * kN1 / kS1; ++w) item1(w);
+        } else if (kKT == 2) {
+          constexpr int kS2 = kSteps - kS1;
+#pragma unroll
+          for (int rt = (st - kS1) * kRT / kS2; rt < (st - kS1 + 1) * kRT / kS2; ++rt) item_split(rt, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (with_loads) asm volatile("" ::: "memory");
+    if (soft) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) item_split(rt, kKT - 1);
+    }
   };
 
   if (ntiles > 0) {
@@ -1218,9 +1330,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     // the start of iteration it: K(it) and V(it - 1) have landed (later loads
     // may stay in flight), then the freed slots are refilled
     auto sync = [&](int it) __attribute__((always_inline)) {
-      if (grp != 0) {
-        // no loads of its own: the barrier covers group 0's
-      } else if (it < ntiles) {
+      if (it < ntiles) {
         if (it >= 2 && it - 2 + kSlots < ntiles) {
           wait_vmem<kIPW * 2 * (kSlots - 2)>();
         } else {
@@ -1233,36 +1343,29 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
       }
       lds_barrier();
     };
-    // one loop per group, so that only the probabilities (group 0) or only the
-    // scores (group 1) stay live from one iteration to the next
-    if (grp == 0) {
-      for (int it = 0; it <= ntiles; ++it) {
-        sync(it);
-        // the refills of this iteration (the slots of K(it - 1) and V(it - 2)
-        // are free past the barrier) go out during P.V
-        const bool loads = it >= 1 && it - 2 + kSlots < ntiles;
-        if (loads) prepare(it - 2 + kSlots, it - 1 + kSlots);
-        if (it >= 1) pv_product(it - 1, loads);
-        if (it < ntiles) {
-          scores(it);
-          softmax(it);
-        }
-      }
-    } else {
-      for (int it = 0; it <= ntiles; ++it) {
-        sync(it);
-        if (it >= 1) {
-          softmax(it - 1);
-          pv_product(it - 1, false);
-        }
-        if (it < ntiles) scores(it);
-      }
+    // stage 0: scores and softmax alone
+    sync(0);
+    scores(0);
+    mask_scores(0);
+    soft_all();
+    rescale();
+    // iteration it: scores of stage it, then P.V of stage it - 1 with the
+    // softmax of stage it
+    for (int it = 1; it < ntiles; ++it) {
+      sync(it);
+      scores(it);
+      const bool spread = it - 2 + kSlots < ntiles && prepare(it - 2 + kSlots, it - 1 + kSlots);
+      mask_scores(it);
+      pv_product(it - 1, spread, true);
+      rescale();
     }
+    sync(ntiles);
+    pv_product(ntiles - 1, false, false);
   }
 
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    const float l_tot = pair_sum<32>(pair_sum<16>(l_run[rt]));
+    const float l_tot = acc_l[rt][0];
     if (!ok[rt]) continue;
     const int t = Rr[rt] / G, hl = Rr[rt] % G;
     const size_t qoff = ((static_cast<size_t>(b) * N + t) * Hq + g * G + hl) * D;
