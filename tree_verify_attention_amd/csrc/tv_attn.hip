@@ -1814,7 +1814,7 @@ hipError_t launch_typed(const AttnPlan& pl, const void* q, const void* k_node, c
 #define TV_ATTN_PAIR_PM 535  // thousandths of a CU's tiles for the first of its two workgroups
 #endif
 #ifndef TV_ATTN_XCD_PM
-#define TV_ATTN_XCD_PM 1020  // thousandths of the average share for workgroups on even XCDs
+#define TV_ATTN_XCD_PM 1050  // thousandths of the average share for workgroups on even XCDs
 #endif
 static_assert(TV_ATTN_PAIR_PM >= 500 && TV_ATTN_PAIR_PM < 1000, "pair weight");
 static_assert(TV_ATTN_XCD_PM >= 500 && TV_ATTN_XCD_PM <= 1500, "XCD weight");
