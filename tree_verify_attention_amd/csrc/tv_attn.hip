@@ -47,7 +47,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kMaxPages = 1024;     // page indices of one stream segment cached in LDS
 constexpr int kSplitPages = 4096;   // of one split (splits are capped to fit)
 constexpr int kAncW = (TV_MAX_NODES + 63) / 64;  // ancestor words per node at most
-constexpr float kLazy = 8.0f;  // log2 headroom of the lazily moved softmax reference
 static_assert(kThreads >= TV_MAX_NODES, "one thread per node position");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
