@@ -97,15 +97,6 @@ __device__ __forceinline__ GateProd gate_product(const float* alpha, const uint6
   return g;
 }
 
-// gamma_t / gamma_i for i an ancestor of t (or t): the product of the gates
-// strictly below i down to t; 0 when one of them is 0
-__device__ __forceinline__ float gate_ratio(const int* zc, const float* mant, const float* rmant,
-                                            const int* ex, int t, int i) {
-  if (t == i) return 1.0f;
-  if (zc[t] != zc[i]) return 0.0f;
-  return ldexpf(mant[t] * rmant[i], ex[t] - ex[i]);
-}
-
 typedef __bf16 gbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float gf32x4_t __attribute__((ext_vector_type(4)));
 
@@ -122,73 +113,90 @@ __device__ __forceinline__ int gswz(int row, int byte) {
 // bf16 inputs, N <= 64: the dense products on MFMA, one 8-wave workgroup per
 // (sequence, head).
 //
-// K S0 and Q S0 are one product [Q; K] S0, formed transposed (S0^T [Q; K]^T)
-// so that S0's rows come out of LDS through the transpose read, as the value
-// tile does in the attention kernel.  S0 is fp32; it is split into two bf16
-// parts S0 = hi + lo (hi its round-to-nearest bf16, lo that of the remainder),
-// so two bf16 products with fp32 accumulation carry S0 to ~16 mantissa bits
-// while q and k are used exactly.  The Gram products [Q; K] K^T are exact bf16
-// products; their masks and gate ratios are applied in registers.  The solve
-// (I + X)^-1 is a short product of matrix powers on fp32 MFMA.  Gram products
-// and solve need neither S0 nor v, so they run first, while S0's loads are in
-// flight; the state products, the right-hand side and the outputs follow.
+// K S0 and Q S0 are one product [Q; K] S0 whose S0 operand never passes
+// through LDS: each wave owns 16 state columns, and every lane loads straight
+// from HBM the eight rows of one column that the matrix-core operand layout
+// gives it.  S0 is fp32; it is split into two bf16 parts S0 = hi + lo (hi its
+// round-to-nearest bf16, lo that of the remainder), so two bf16 products with
+// fp32 accumulation carry S0 to ~16 mantissa bits while q and k are used
+// exactly.  The Q rows are formed transposed (S0^T Q^T), which leaves each lane
+// one node's outputs for four consecutive columns, the layout the output
+// product accumulates in; the K rows are formed as K S0 with the node rows
+// permuted so that each lane holds, for one column, the nodes the output
+// product takes as its contraction operand.  The right-hand side is then made
+// in registers and no barrier follows the state products.  The Gram products
+// [Q; K] K^T are exact bf16 products; their masks and gate ratios are applied
+// in registers.  The solve (I + X)^-1 is a short product of matrix powers on
+// fp32 MFMA.  Gram products and solve need neither S0 nor v, so they run
+// first, while S0's loads are in flight.
 constexpr int kMThreads = 512;
 
 typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 mbf16x4_t __attribute__((ext_vector_type(4)));
-typedef short ms16x4_t __attribute__((ext_vector_type(4)));
-typedef short ms16x8_t __attribute__((ext_vector_type(8)));
 typedef float mf32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ ms16x4_t tr_read(const unsigned char* p) {
-  auto lp = (__attribute__((address_space(3))) mbf16x4_t*)(p);
-  return __builtin_bit_cast(ms16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+// one quad_perm lane exchange (DPP): lane i of each quad of lanes takes the
+// value of lane perm[i]
+template <int kCtrl>
+__device__ __forceinline__ float quad_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+}
+
+// 4 x 4 transpose inside each quad of lanes: lane b of a quad holds row b of
+// a block and returns column b, in two exchanges, first with lane b ^ 1 (the
+// odd or even columns), then with lane b ^ 2 (the column pairs)
+__device__ __forceinline__ float4 quad_transpose(float4 x, int b) {
+  const bool odd = b & 1, hi = b & 2;
+  const float a0 = quad_dpp<0xb1>(odd ? x.x : x.y), a1 = quad_dpp<0xb1>(odd ? x.z : x.w);
+  const float y0 = odd ? a0 : x.x, y1 = odd ? x.y : a0, y2 = odd ? a1 : x.z, y3 = odd ? x.w : a1;
+  const float c0 = quad_dpp<0x4e>(hi ? y0 : y2), c1 = quad_dpp<0x4e>(hi ? y1 : y3);
+  return hi ? make_float4(c0, c1, y2, y3) : make_float4(y0, y1, c0, c1);
 }
 
 constexpr int kHUP = kDk + 16;  // row pitch of the right-hand side (floats): conflict-free column reads
 
-// bytes of region 1: X, Y and two more NP x NP matrices for the solve, then one
-// bf16 half of S0 at a time, then [Q; K] S0 (fp32, 2NP rows of 128)
-__host__ __device__ inline size_t gdn_r1_bytes(int np) {
-  const size_t half = static_cast<size_t>(kDk) * kRowB;
-  const size_t qks = 2 * static_cast<size_t>(np) * kDk * 4;
-  const size_t solve = 4 * static_cast<size_t>(np) * (np + 4) * 4;
-  const size_t m = half > qks ? half : qks;
-  return m > solve ? m : solve;
-}
+// bytes of region 1: X, Y and two more NP x NP matrices for the solve; M is
+// left in one of them
+__host__ __device__ inline size_t gdn_r1_bytes(int np) { return 4 * static_cast<size_t>(np) * (np + 4) * 4; }
 
 // bytes of the [Q; K] rows (bf16)
 __host__ __device__ inline size_t gdn_r2_bytes(int np) { return 2 * static_cast<size_t>(np) * kRowB; }
 
 size_t gdn_mfma_lds_bytes(int N) {
   const int np = (N + 15) / 16 * 16;
-  // region 1; [Q; K]; V, later the right-hand side (fp32); M (fp32); alpha,
-  // beta, gamma, the gate-product mantissa and its reciprocal, depth, zero
-  // count, exponent, ancestor words.  Up to 32 nodes this is 73 KB, so two
-  // workgroups fit a CU.
-  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kHUP * 4 +
-         static_cast<size_t>(np) * (np + 4) * 4 + 64 * 4 * 8 + 64 * 8;
+  // region 1; [Q; K]; V (fp32); beta, gamma, the gate-product mantissa and its
+  // reciprocal, zero count, exponent, ancestor words.  Up to 32 nodes this is
+  // 54 KB, so two workgroups fit a CU.
+  return gdn_r1_bytes(np) + gdn_r2_bytes(np) + static_cast<size_t>(np) * kHUP * 4 + 64 * 4 * 6 + 64 * 8;
 }
 
 // One 16 x 16 tile (row tile rt, column tile ct) of C = A B (+ D), NP x NP
 // fp32 matrices of row pitch mp in LDS, on v_mfma_f32_16x16x4f32; B's
 // entries are scaled by `sb`.  A lane holds column lr of rows 4 lg .. 4 lg + 3.
+// A and B are lower triangular (a node couples only to itself and its
+// ancestors, which precede it): only k-tiles ct .. rt contribute, and a tile
+// above the diagonal is zero.  Two accumulators halve the dependent chain.
 template <bool kAdd, int kNT>
 __device__ __forceinline__ void gdn_mm_tile(const float* A, const float* B, const float* Dm, float* C, int mp,
                                             int rt, int ct, int lr, int lg, float sb) {
-  mf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  mf32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kAdd) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = Dm[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr];
   }
 #pragma unroll
-  for (int ks = 0; ks < 4 * kNT; ++ks) {
-    const float a = A[(16 * rt + lr) * mp + 4 * ks + lg];
-    const float bv = sb * B[(4 * ks + lg) * mp + 16 * ct + lr];
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+  for (int ks = 0; ks < 4 * kNT; ks += 2) {
+    if (ks >= 4 * ct && ks < 4 * rt + 4) {
+      const float a = A[(16 * rt + lr) * mp + 4 * ks + lg];
+      const float bv = sb * B[(4 * ks + lg) * mp + 16 * ct + lr];
+      const float a2 = A[(16 * rt + lr) * mp + 4 * ks + 4 + lg];
+      const float bv2 = sb * B[(4 * ks + 4 + lg) * mp + 16 * ct + lr];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, bv2, acc2, 0, 0, 0);
+    }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) C[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr] = acc[r];
+  for (int r = 0; r < 4; ++r) C[(16 * rt + 4 * lg + r) * mp + 16 * ct + lr] = acc[r] + acc2[r];
 }
 
 // One step of the solve as a single phase: Mo = M + M (sb P) and, when Po is
@@ -221,20 +229,17 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NP = 8 * kM;  // N rounded up to 16 (the launch picks kM)
   constexpr int MP = NP + 4;                     // row pitch of the NP x NP matrices (floats)
-  unsigned char* r1 = smem;                      // X, Y, third; then S0 hi, S0 lo; then [Q; K] S0 fp32
+  unsigned char* r1 = smem;                      // X, Y and two more NP x NP matrices for the solve
   unsigned char* r2 = smem + gdn_r1_bytes(NP);   // [Q; K] bf16 [2NP][128]
-  float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V, then the right-hand side
-  float* s_m = s_u + NP * kHUP;                   // M [NP][MP]
-  float* s_alpha = s_m + NP * MP;
-  float* s_beta = s_alpha + 64;
+  float* s_u = reinterpret_cast<float*>(r2 + gdn_r2_bytes(NP));  // V [NP][kHUP]
+  float* s_beta = s_u + NP * kHUP;
   float* s_gam = s_beta + 64;
   float* s_mant = s_gam + 64;   // gate product over nonzero gates: mantissa,
   float* s_rmant = s_mant + 64; // its reciprocal,
-  int* s_depth = reinterpret_cast<int*>(s_rmant + 64);
-  int* s_zc = s_depth + 64;     // zero gates on the root path,
+  int* s_zc = reinterpret_cast<int*>(s_rmant + 64);  // zero gates on the root path,
   int* s_ex = s_zc + 64;        // and the binary exponent of the product
   uint64_t* s_anc = reinterpret_cast<uint64_t*>(s_ex + 64);
-  __shared__ int s_maxdepth;
+  __shared__ int s_steps;       // ceil(log2(depth of the deepest node))
 
   const int bh = blockIdx.x;
   const int h = bh % H;
@@ -246,7 +251,6 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 
   // ---- phase 0: q and k rows, v and the gates, then S0.  S0's loads stay in
   // flight through the Gram products and the solve, which do not need it.
-  if (tid == 0) s_maxdepth = 1;
   constexpr int kQKPer = 2 * 64 * (kRowB / 16) / kMThreads;  // q / k granules per thread (at most)
   constexpr int kVPer = 64 * (kDk / 8) / kMThreads;           // v granules per thread (at most)
   uint4 gq[kQKPer], gv[kVPer];
@@ -300,44 +304,67 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     }
   }
   if (tid < 64) {
+    // Wave 0, lane t = node t: gamma_t, the product of alpha over t's root
+    // path, kept as a count of zero gates and the product of the others as
+    // mant * 2^ex (|mant| in [0.5, 1)), by pointer jumping: (mant, ex, zeros)
+    // covers the path segment (jmp, t], and a round appends the segment that
+    // ends at jmp, doubling the reach.  Rounds run until every node has
+    // reached its root: ceil(log2(depth)) of them, the step count of the solve.
     const int t = tid;
-    s_alpha[t] = ga;
     s_beta[t] = gb;
     // keep only real, earlier nodes (ancestors precede their descendants);
     // a node always sees itself
     const uint64_t below = t >= 63 ? ~0ull >> 1 : ((1ull << t) - 1ull);
-    s_anc[t] = t < N ? ((gw & live & below) | (1ull << t)) : 0ull;
+    const uint64_t strict = t < N ? (gw & live & below) : 0ull;
+    s_anc[t] = t < N ? (strict | (1ull << t)) : 0ull;
+    int jmp = strict ? 63 - __clzll(static_cast<long long>(strict)) : -1;
+    int zeros = (t < N && ga == 0.0f) ? 1 : 0;
+    int ex = 1;
+    float mant = 0.5f;
+    if (!zeros) mant = frexpf(ga, &ex);
+    int rounds = 0;
+    while (__ballot(jmp >= 0)) {
+      const int src = jmp >= 0 ? jmp : t;
+      const float mj = __shfl(mant, src, 64);
+      const int ej = __shfl(ex, src, 64), zj = __shfl(zeros, src, 64), pj = __shfl(jmp, src, 64);
+      if (jmp >= 0) {
+        int e2;
+        mant = frexpf(mant * mj, &e2);
+        ex += ej + e2;
+        zeros += zj;
+        jmp = pj;
+      }
+      ++rounds;
+    }
+    s_gam[t] = zeros ? 0.0f : ldexpf(mant, ex);
+    s_mant[t] = mant;
+    s_rmant[t] = 1.0f / mant;
+    s_zc[t] = zeros;
+    s_ex[t] = ex;
+    if (t == 0) s_steps = rounds;
   }
   __syncthreads();
   // S0 goes out once the small loads are in (issued with them, it would
   // delay them: every workgroup's S0 competes for HBM at the same moment),
   // in three batches between the phases that do not need it, so that no
-  // wave stalls long on a full memory pipeline
-  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk;
-  float4 f[8];
+  // wave stalls long on a full memory pipeline.  Wave w owns state columns
+  // 16w .. 16w + 15.  Load u = 2 ks + hf gives lane (lr, lg) = (4 q + b, lg)
+  // the four columns 16 w + 4 q .. + 3 of row 32 ks + 8 lg + 4 hf + b (16
+  // rows of 64 bytes per instruction; 16-byte loads keep the instruction count
+  // low, which matters while misses are slow); a 4 x 4 transpose inside each
+  // quad of lanes then leaves lane (lr, lg) rows 32 ks + 8 lg + j, j < 8, of
+  // column 16 w + lr: the bf16 operand layout of the state products.
+  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
+  float4 f[kDk / 16];
   auto s0_issue = [&](int u0, int u1) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (u >= u0 && u < u1) f[u] = reinterpret_cast<const float4*>(s0)[tid + u * kMThreads];
+    for (int u = 0; u < kDk / 16; ++u)
+      if (u >= u0 && u < u1)
+        f[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
   };
   s0_issue(0, 3);
-  if (tid < 64) {
-    // gamma_t = product of alpha over t's root path, kept as a count of zero
-    // gates and the product of the others as mantissa * 2^exponent
-    const int t = tid;
-    const GateProd gp = gate_product<1>(s_alpha, s_anc + t);
-    s_gam[t] = gp.value();
-    s_mant[t] = gp.mant;
-    s_rmant[t] = 1.0f / gp.mant;
-    s_zc[t] = gp.zeros;
-    s_ex[t] = gp.ex;
-    const int dpt = __popcll(s_anc[t]);
-    s_depth[t] = dpt;
-    if (t < N) atomicMax(&s_maxdepth, dpt);
-  }
 
   // ---- phase 1: the Gram products [Q; K] K^T on MFMA (exact bf16 products)
-  constexpr int nqks = NP;              // 8 column tiles x 2NP / 16 node tiles
   constexpr int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
   mf32x4_t qks[kM], gram[kM / 2];
 #pragma unroll
@@ -357,37 +384,44 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     }
   }
   s0_issue(3, 6);
-  __syncthreads();  // gamma and the depths are in
 
   // X and Y with their masks and gate ratios, into region 1
   float* s_x = reinterpret_cast<float*>(r1);  // [NP][MP]
   float* s_y = s_x + NP * MP;                 // [NP][MP]
   float* s_t = s_y + NP * MP;                 // [NP][MP], two more matrices for the solve
   float* s_t2 = s_t + NP * MP;                // [NP][MP]
+  // Query rows give Y over ancestors-or-self, key rows X over strict
+  // ancestors (times beta_t).  Every operand is read before any is used, and
+  // the masks are selects, so one LDS round trip serves the tile.
 #pragma unroll
   for (int m = 0; m < kM / 2; ++m) {
     const int u = wave + 8 * m;
     if (u < ngram) {
       const int kt = u % (NP / 16), rt = u / (NP / 16);
+      const bool query = rt < NP / 16;
       const int i = 16 * kt + lr;
+      const int t0 = 16 * rt + 4 * lg - (query ? 0 : NP);
+      const int zi = s_zc[i], ei = s_ex[i];
+      const float rmi = s_rmant[i];
+      uint64_t at[4];
+      int zt[4], et[4];
+      float mt[4], bt[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * rt + 4 * lg + r;
-        if (row < NP) {
-          // a query row: Y over ancestors-or-self
-          const int t = row;
-          float y = 0.0f;
-          if (t < N && i < N && ((s_anc[t] >> i) & 1ull))
-            y = gate_ratio(s_zc, s_mant, s_rmant, s_ex, t, i) * gram[m][r];
-          s_y[t * MP + i] = y;
-        } else {
-          // a key row: X over strict ancestors
-          const int t = row - NP;
-          float x = 0.0f;
-          if (t < N && i < N && i != t && ((s_anc[t] >> i) & 1ull))
-            x = s_beta[t] * gate_ratio(s_zc, s_mant, s_rmant, s_ex, t, i) * gram[m][r];
-          s_x[t * MP + i] = x;
-        }
+        at[r] = s_anc[t0 + r];
+        zt[r] = s_zc[t0 + r];
+        et[r] = s_ex[t0 + r];
+        mt[r] = s_mant[t0 + r];
+        bt[r] = query ? 1.0f : s_beta[t0 + r];
+      }
+      float* dst = query ? s_y : s_x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + r;
+        // gamma_t / gamma_i: the gates strictly below i down to t, 0 past a zero gate
+        const float ratio = t == i ? 1.0f : (zt[r] != zi ? 0.0f : ldexpf(mt[r] * rmi, et[r] - ei));
+        const bool keep = t < N && i < N && ((at[r] >> i) & 1ull) && (query || i != t);
+        dst[t * MP + i] = keep ? bt[r] * ratio * gram[m][r] : 0.0f;
       }
     }
   }
@@ -401,10 +435,9 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
   // one factor per step, while the power is squared for the next step (both
   // products in one phase, one barrier per step).  Four NP x NP buffers
   // rotate; fp32 MFMA throughout.
+  const float* s_m;  // M [NP][MP], left in region 1 by the last step
   {
-    const int maxdepth = s_maxdepth;
-    int steps = 0;
-    while ((1 << steps) < maxdepth) ++steps;
+    const int steps = s_steps;
     float* bm = s_y;   // M
     float* bp = s_x;   // the power of X, stored as X^(2^j) ((-X)^(2^j) for j > 0 is the same)
     float* fm = s_t;   // free, for the next M
@@ -424,114 +457,81 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
         fp = tmp;
       }
     }
-    // M out of region 1, which S0 takes next
-    for (int e = tid; e < NP * MP / 4; e += kMThreads)
-      reinterpret_cast<float4*>(s_m)[e] = reinterpret_cast<const float4*>(bm)[e];
+    s_m = bm;  // behind a barrier: the last step's, else the one after X and Y
   }
-  __syncthreads();
 
-  // ---- phase 3: [Q; K] S0 on MFMA, formed transposed (S0^T [Q; K]^T).  S0
-  // is split into bf16 hi = bf16(S0) (round to nearest even, the hardware
-  // conversion) and lo = bf16(S0 - hi); the halves pass one after the other
-  // through region 1, lo waiting packed in registers.
-  uint2 s0lo[8];
+  // ---- phase 3: [Q; K] S0 on MFMA from registers.  S0 = hi + lo, hi =
+  // bf16(S0) (round to nearest even, the hardware conversion) and lo =
+  // bf16(S0 - hi).  Node tile m < kM / 2 is Q: the product S0^T Q^T leaves lane
+  // (lr, lg) node 16 m + lr, columns 16 w + 4 lg + r.  The others are K: K S0
+  // with A-row i reading node 4 (i & 3) + (i >> 2) of the tile, which leaves
+  // lane (lr, lg) column 16 w + lr of nodes 16 m' + 4 r + lg.
+  mbf16x8_t shi[kDk / 32], slo[kDk / 32];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + u * kMThreads;
-    const int d = e >> 5, c = (e & 31) * 4;
-    const mbf16x4_t hv = {static_cast<__bf16>(f[u].x), static_cast<__bf16>(f[u].y),
-                          static_cast<__bf16>(f[u].z), static_cast<__bf16>(f[u].w)};
-    const mbf16x4_t lv = {static_cast<__bf16>(f[u].x - static_cast<float>(hv[0])),
-                          static_cast<__bf16>(f[u].y - static_cast<float>(hv[1])),
-                          static_cast<__bf16>(f[u].z - static_cast<float>(hv[2])),
-                          static_cast<__bf16>(f[u].w - static_cast<float>(hv[3]))};
-    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = __builtin_bit_cast(uint2, hv);
-    s0lo[u] = __builtin_bit_cast(uint2, lv);
-  }
-  __syncthreads();
-  // Tile u = wave + 8 m is column tile `wave` of node tile m: a wave keeps one
-  // column tile, so each k-step reads its S0 fragment once for all node tiles.
-  auto s0_product = [&]() {
-    const int vcol = wave * 32 + 8 * (lr & 3);
+  for (int u = 0; u < kDk / 16; ++u) f[u] = quad_transpose(f[u], lr & 3);
 #pragma unroll
-    for (int ks = 0; ks < kDk / 32; ++ks) {
-      const int vrow = 32 * ks + 4 * lg + (lr >> 2);
-      const ms16x4_t h0 = tr_read(r1 + gswz(vrow, vcol));
-      const ms16x4_t h1 = tr_read(r1 + gswz(vrow + 16, vcol));
-      const ms16x8_t ah = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  for (int ks = 0; ks < kDk / 32; ++ks) {
 #pragma unroll
-      for (int m = 0; m < kM; ++m) {
-        if (wave + 8 * m < nqks) {
-          const int row = 16 * m + lr;
-          const uint2 b0 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 4 * lg)));
-          const uint2 b1 = *reinterpret_cast<const uint2*>(r2 + gswz(row, 2 * (32 * ks + 16 + 4 * lg)));
-          const mbf16x8_t bb = __builtin_bit_cast(mbf16x8_t, make_uint4(b0.x, b0.y, b1.x, b1.y));
-          qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mbf16x8_t, ah), bb,
-                                                            qks[m], 0, 0, 0);
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      const float4& fq = f[2 * ks + (j >> 2)];
+      const float x = (j & 3) == 0 ? fq.x : (j & 3) == 1 ? fq.y : (j & 3) == 2 ? fq.z : fq.w;
+      const __bf16 hv = static_cast<__bf16>(x);
+      shi[ks][j] = hv;
+      slo[ks][j] = static_cast<__bf16>(x - static_cast<float>(hv));
     }
-  };
-#pragma unroll
-  for (int m = 0; m < kM; ++m) qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
-  s0_product();  // high half
-  __syncthreads();  // every read of S0's high half is done
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + u * kMThreads;
-    const int d = e >> 5, c = (e & 31) * 4;
-    *reinterpret_cast<uint2*>(r1 + gswz(d, 2 * c)) = s0lo[u];
   }
-  __syncthreads();
-  s0_product();  // low half
-  __syncthreads();  // every read of S0 is done
-
-  // [Q; K] S0 rows into region 1
-  float* s_qks = reinterpret_cast<float*>(r1);  // [2NP][128]
+  const int kperm = 4 * (lr & 3) + (lr >> 2);
 #pragma unroll
   for (int m = 0; m < kM; ++m) {
-    const int u = wave + 8 * m;
-    if (u < nqks) {
-      const int ct = u & 7, nt = u >> 3;
-      *reinterpret_cast<float4*>(s_qks + (16 * nt + lr) * kDk + 16 * ct + 4 * lg) =
-          make_float4(qks[m][0], qks[m][1], qks[m][2], qks[m][3]);
+    qks[m] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int row = 16 * m + (m < kM / 2 ? lr : kperm);
+#pragma unroll
+    for (int ks = 0; ks < kDk / 32; ++ks) {
+      const mbf16x8_t nb = __builtin_bit_cast(mbf16x8_t, *reinterpret_cast<const uint4*>(
+                                                             r2 + gswz(row, 2 * (32 * ks + 8 * lg))));
+      if (m < kM / 2) {
+        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(slo[ks], nb, qks[m], 0, 0, 0);
+        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(shi[ks], nb, qks[m], 0, 0, 0);
+      } else {
+        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nb, slo[ks], qks[m], 0, 0, 0);
+        qks[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nb, shi[ks], qks[m], 0, 0, 0);
+      }
     }
   }
-  __syncthreads();
 
-  // ---- phase 4: right-hand side beta_t (v_t - gamma_t (K S0)_t), in place of V
-  for (int e = tid; e < N * (kDk / 4); e += kMThreads) {
-    const int t = e / (kDk / 4), c = (e % (kDk / 4)) * 4;
-    float4 uu = *reinterpret_cast<const float4*>(s_u + t * kHUP + c);
-    const float4 ks = *reinterpret_cast<const float4*>(s_qks + (NP + t) * kDk + c);
-    const float bt = s_beta[t], gt = s_gam[t];
-    uu.x = bt * (uu.x - gt * ks.x);
-    uu.y = bt * (uu.y - gt * ks.y);
-    uu.z = bt * (uu.z - gt * ks.z);
-    uu.w = bt * (uu.w - gt * ks.w);
-    *reinterpret_cast<float4*>(s_u + t * kHUP + c) = uu;
+  // ---- phase 4: right-hand side beta_t (v_t - gamma_t (K S0)_t) in
+  // registers, lane (lr, lg) holding column 16 w + lr of node 4 ks + lg for
+  // k-step ks of the output product.  Rows past N have zero V, K and beta.
+  constexpr int nt = NP / 16;
+  float rhs[NP / 4];
+#pragma unroll
+  for (int mt = 0; mt < nt; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = 16 * mt + 4 * r + lg;
+      rhs[4 * mt + r] = s_beta[n] * (s_u[n * kHUP + 16 * wave + lr] - s_gam[n] * qks[nt + mt][r]);
+    }
   }
-  __syncthreads();
 
   // ---- phase 5: O^T = (right-hand side)^T M^T + gamma (Q S0)^T, tiles of
   // 16 state columns x 16 nodes; a lane ends with 4 consecutive columns of
   // one node's output
-  constexpr int nt = NP / 16;
 #pragma unroll
-  for (int mm = 0; mm < 4; ++mm) {
-    const int u = wave + 8 * mm;
-    if (u < 8 * nt) {
-      const int ct = u & 7, ntile = u >> 3;
-      const int t = 16 * ntile + lr;
+  for (int mm = 0; mm < nt; ++mm) {
+    {
+      const int ct = wave;
+      const int t = 16 * mm + lr;
       const float gt = s_gam[t];
-      const float4 qs = *reinterpret_cast<const float4*>(s_qks + t * kDk + 16 * ct + 4 * lg);
-      mf32x4_t acc = {gt * qs.x, gt * qs.y, gt * qs.z, gt * qs.w};
+      // M is lower triangular: nodes past this tile do not contribute
+      mf32x4_t acc = gt * qks[mm], acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NP / 4; ++ks) {
-        const float a = s_u[(4 * ks + lg) * kHUP + 16 * ct + lr];
+      for (int ks = 0; ks < 4 * mm + 4; ks += 2) {
         const float bv = s_m[t * MP + 4 * ks + lg];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+        const float bv2 = s_m[t * MP + 4 * ks + 4 + lg];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(rhs[ks], bv, acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(rhs[ks + 1], bv2, acc2, 0, 0, 0);
       }
+      acc += acc2;
       if (t < N) {
         const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * ct + 4 * lg;
         if constexpr (sizeof(TO) == 2) {
