@@ -222,7 +222,10 @@ __device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2
     if (tid == 0) *s_rng = make_int2(lo, hi);
   }
   __syncthreads();
-  return *s_rng;
+  // the same value in every lane: make it wave-uniform, so that what is
+  // derived from it (the split's key range, stage bounds) stays scalar
+  const int2 r = *s_rng;
+  return make_int2(__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -232,6 +235,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 template <typename V>
 __device__ __forceinline__ void pin(V& v) {
   asm volatile("" : "+v"(v));
+}
+
+// x = keep ? x : other, rewriting x's own register, so that a value that
+// passes a branch masked on one side and untouched on the other needs no copy
+// where the sides join
+__device__ __forceinline__ float keep_or(float x, bool keep, float other) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+  asm volatile("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(other), "s"(m));
+  return x;
 }
 
 // The values of lanes l and l ^ S (S = 16 or 32), through the gfx950 lane-swap
@@ -1057,6 +1069,18 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     unsigned char* dst = (half == 0 ? vring : kring) + pre_dst[half] + (wave * kIPW + j) * 1024;
     lds_dma16<false>(pre_base[half] + off, dst);
   };
+  // The page of each half's rows, read from the page cache before the
+  // scores' key reads fill the LDS queue (read after them, it waited behind
+  // them); a stage past the split reads a clamped, unused entry.
+  int pre_page[2];
+  auto fetch_pages = [&](int sv, int sk) __attribute__((always_inline)) {
+    const int st[2] = {sv, sk};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = ((k0 + st[q] * kSK + wave * kRowsW) >> 4) - p0;
+      pre_page[q] = s_pages[min(max(idx, 0), kSplitPages - 1)];
+    }
+  };
   // returns whether the loads are left to P.V
   auto prepare = [&](int sv, int sk) __attribute__((always_inline)) {
     const int st[2] = {sv, sk};
@@ -1070,8 +1094,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
       fast[q] = st[q] < ntiles && !is_node && (base & 15) == 0 && base + kSK <= lim;
       pre_base[q] = kcb;
       if (fast[q]) {
-        const int page = __builtin_amdgcn_readfirstlane(
-            s_pages[((base + wave * kRowsW) >> 4) - p0]);
+        const int page = __builtin_amdgcn_readfirstlane(pre_page[q]);
         pre_base[q] = (q == 0 ? vcb : kcb) +
                       (static_cast<size_t>(page) * Hkv + g) * (16 * C::kRowBytes);
       }
@@ -1100,7 +1123,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
   const uint32_t k_lane = swz<T, D>(lr, lg * 16);
   const uint32_t v_lane = swz<T, D>(4 * lg + (lr >> 2), 8 * (lr & 3));
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-  f32x4_t S[kRT][2 * kKT];  // scores of a stage, from its products to its softmax
+  f32x4_t S[kRT][2 * kKT];  // a stage's scores, masked, then its probabilities (in place)
   bf16x8_t ph[kRT][kKT];  // its probabilities in bf16
 
   // S^T of every row tile for the 16-key quarters of stage `it`: the key
@@ -1151,7 +1174,6 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
   // at most 1, and a wave rescales its accumulators only on stages where
   // some row's maximum grew (a few percent of a long stream).  P goes to
   // bf16 pairs at a time (keys 16 h + 4 lg + i).
-  float sv[kRT][2 * kKT][4];  // the stage's (masked) raw scores, then its probabilities
   float alpha[kRT], neg_m[kRT];
   bool need[kRT];
   auto mask_scores = [&](int it) __attribute__((always_inline)) {
@@ -1160,13 +1182,8 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     const int lim = is_node ? N : k1;
     const bool full = !is_node && base + kSK <= lim &&
                       (window <= 0 || (base >= win_all && base + kSK - 1 <= prng.x));
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-      for (int h = 0; h < 2 * kKT; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[rt][h][i] = S[rt][h][i];
     if (full) return;
+    const float ninf = -INFINITY;
     if (is_node) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
@@ -1180,22 +1197,24 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
             const int dpos = rpos - s_pos[key & (TV_MAX_NODES - 1)];
             bool vis = ok[rt] & (key < lim) & (((aw >> (key & 63)) & 1ull) != 0ull);
             vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-            sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+            S[rt][h][i] = keep_or(S[rt][h][i], vis, ninf);
           }
       }
     } else {
+      // key = c + 4 lg with c = base + 16 h + i wave-uniform: only 4 lg and
+      // the row's position minus 4 lg vary over the lanes
+      const int l4 = 4 * lg;
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const int rpos = s_pos[tn[rt]];
+        const int pr = s_pos[tn[rt]] - l4;
 #pragma unroll
         for (int h = 0; h < 2 * kKT; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = base + 16 * h + 4 * lg + i;
-            const int dpos = rpos - key;
-            bool vis = ok[rt] & (key < lim);
-            vis &= (window <= 0) | ((dpos >= 0) & (dpos < window));
-            sv[rt][h][i] = vis ? sv[rt][h][i] : -INFINITY;
+            const int c = base + 16 * h + i;
+            bool vis = ok[rt] & (l4 < lim - c);
+            vis &= (window <= 0) | ((pr >= c) & (pr < c + window));
+            S[rt][h][i] = keep_or(S[rt][h][i], vis, ninf);
           }
       }
     }
@@ -1209,7 +1228,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     float mt = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2 * kKT; ++h)
-      mt = fmaxf(mt, fmaxf(fmaxf(sv[rt][h][0], sv[rt][h][1]), fmaxf(sv[rt][h][2], sv[rt][h][3])));
+      mt = fmaxf(mt, fmaxf(fmaxf(S[rt][h][0], S[rt][h][1]), fmaxf(S[rt][h][2], S[rt][h][3])));
     mt = pair_max<32>(pair_max<16>(mt));
     const float mc = mt * scale_log2;
     need[rt] = mc > m_run[rt];
@@ -1222,18 +1241,18 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     pin(neg_m[rt]);
   };
   auto item_exp = [&](int rt, int h) __attribute__((always_inline)) {
+    f32x4_t e;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[rt][h][i] = fast_exp2(fmaf(sv[rt][h][i], scale_log2, neg_m[rt]));
-      pin(sv[rt][h][i]);
-    }
+    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(S[rt][h][i], scale_log2, neg_m[rt]));
+    S[rt][h] = e;
+    pin(S[rt][h]);
   };
   auto item_split = [&](int rt, int kt) __attribute__((always_inline)) {
     uint32_t hw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       // fragment elements 2e, 2e + 1: quarter 2 kt + e / 2, keys 4 lg + 2 (e % 2) + 0, 1
-      const f32x2_t f = {sv[rt][2 * kt + e / 2][2 * (e % 2)], sv[rt][2 * kt + e / 2][2 * (e % 2) + 1]};
+      const f32x2_t f = {S[rt][2 * kt + e / 2][2 * (e % 2)], S[rt][2 * kt + e / 2][2 * (e % 2) + 1]};
       hw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
     }
     ph[rt][kt] = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
@@ -1360,6 +1379,7 @@ __global__ __launch_bounds__(64 * kWideWaves, 1) void attn_wide_kernel(
     // softmax of stage it
     for (int it = 1; it < ntiles; ++it) {
       sync(it);
+      fetch_pages(it - 2 + kSlots, it - 1 + kSlots);
       scores(it);
       const bool spread = it - 2 + kSlots < ntiles && prepare(it - 2 + kSlots, it - 1 + kSlots);
       mask_scores(it);
