@@ -114,9 +114,10 @@ __device__ __forceinline__ int gswz(int row, int byte) {
 // (sequence, head).
 //
 // K S0 and Q S0 are one product [Q; K] S0 whose S0 operand never passes
-// through LDS: each wave owns 16 state columns, and every lane loads straight
-// from HBM the eight rows of one column that the matrix-core operand layout
-// gives it.  S0 is fp32; it is split into two bf16 parts S0 = hi + lo (hi its
+// through LDS: each wave owns 16 state columns, loads them from HBM in 16-byte
+// pieces, and a 4 x 4 transpose inside each quad of lanes leaves every lane
+// the eight rows of one column that the matrix-core operand layout gives it.
+// S0 is fp32; it is split into two bf16 parts S0 = hi + lo (hi its
 // round-to-nearest bf16, lo that of the remainder), so two bf16 products with
 // fp32 accumulation carry S0 to ~16 mantissa bits while q and k are used
 // exactly.  The Q rows are formed transposed (S0^T Q^T), which leaves each lane
