@@ -548,12 +548,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, 64 < N <= 128.  One 4-wave workgroup per (sequence, head, 64
-// state columns), wave w computing column tile w; the node count is padded to
-// NP = 16 NT.
+// bf16 inputs, 64 < N <= 128.  One 8-wave workgroup per (sequence, head), wave
+// w owning state columns 16 w .. 16 w + 15; the node count is padded to
+// NP = 16 NT.  The Gram products and the solve run once per head.
 //
-//  1. q and k rows (bf16, exact) into LDS; this block's columns of S0 go
-//     straight into registers in the MFMA operand layout and stay in flight
+//  1. q and k rows (bf16, exact) into LDS; v at this lane's right-hand-side
+//     positions and S0's columns of this wave into registers, in flight
 //     through steps 2-4, which do not need them.
 //  2. Gate products per node, then the Gram tiles [Q; K] K^T on bf16 MFMA,
 //     only the 16 x 16 tiles on or below the block diagonal (ancestors precede
@@ -568,16 +568,16 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 //     the last: M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a.  M overwrites
 //     Y tile by tile (a tile is read only by its own update); one barrier per
 //     block column.
-//  5. [Q; K] S0 for this column block on bf16 MFMA, S0 split into
-//     hi = bf16(S0) and lo = bf16(S0 - hi) (two products: ~16 mantissa bits).
-//  6. Right-hand side beta (V - gamma K S0) from the K S0 accumulators, into
-//     the LDS of [Q; K], which is free by then; then O = gamma Q S0 + M RHS on
-//     fp32 MFMA, starting from the Q S0 accumulators, and the store.
+//  5. [Q; K] S0 on bf16 MFMA from registers, S0 split into hi = bf16(S0) and
+//     lo = bf16(S0 - hi) (two products: ~16 mantissa bits), in the layouts of
+//     the N <= 64 kernel: Q S0 transposed, as the output accumulates; K S0 with
+//     permuted node rows, as the output product's contraction operand.
+//  6. Right-hand side beta (V - gamma K S0) in registers, then
+//     O = gamma Q S0 + M RHS on fp32 MFMA over M's lower-triangular tiles,
+//     and the store.  No barrier after step 4.
 // ---------------------------------------------------------------------------
 
-constexpr int kWC = 64;            // state columns per workgroup
-constexpr int kWCB = kDk / kWC;    // column blocks per (sequence, head)
-constexpr int kWUP = kWC + 4;      // row pitch of the right-hand side (floats)
+constexpr int kTThreads = 512;
 
 // element (r, c) of a 16 x 16 fp32 tile: row-major, column XOR-swizzled by row
 __device__ __forceinline__ int tix(int r, int c) { return r * 16 + (c ^ r); }
@@ -590,12 +590,11 @@ struct GdnLds {
   static constexpr int NP = 16 * NT;
   static constexpr int NTRI = NT * (NT + 1) / 2;
   static constexpr int W = (NP + 63) / 64;
-  static constexpr int kQK = 2 * NP * kRowB;      // [Q; K] bf16, later the RHS
-  static constexpr int kTiles = NTRI * 256 * 4;   // X or Y tiles
-  static constexpr int kScr = 4 * 2 * 256 * 4;    // per wave: two 16 x 16 fp32 tiles
-  static constexpr int kSmall = NP * 4 * 6 + NP * W * 8;  // gate product (4), alpha, beta, gamma; anc
+  static constexpr int kQK = 2 * NP * kRowB;               // [Q; K] bf16
+  static constexpr int kTiles = NTRI * 256 * 4;            // X or Y tiles
+  static constexpr int kScr = (kTThreads / 64) * 2 * 256 * 4;  // per wave: two 16 x 16 fp32 tiles
+  static constexpr int kSmall = NP * 16 + NP * 4 * 3 + NP * W * 8;  // gate product, alpha, beta, gamma; anc
   static constexpr int kBytes = kQK + 2 * kTiles + kScr + kSmall;
-  static_assert(NP * kWUP * 4 <= kQK, "the RHS fits the rows' region");
 };
 
 // 16 x 16 x 16 fp32 product on v_mfma_f32_16x16x4f32: acc += (sa A) B
@@ -632,61 +631,54 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <typename TO, int NT>
-__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1)))
-void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
-                     const float* __restrict__ beta, const float* __restrict__ S0,
-                     const uint64_t* __restrict__ anc, int N, int H, int BH, TO* __restrict__ out) {
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, const float* __restrict__ alpha,
+                    const float* __restrict__ beta, const float* __restrict__ S0,
+                    const uint64_t* __restrict__ anc, int N, int H, TO* __restrict__ out) {
   using L = GdnLds<NT>;
   constexpr int NP = L::NP, NTRI = L::NTRI, W = L::W;
+  constexpr int kWaves = kTThreads / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* r_qk = smem;
-  float* r_u = reinterpret_cast<float*>(smem);  // the RHS, once [Q; K] is no longer read
   float* r_x = reinterpret_cast<float*>(smem + L::kQK);
   float* r_y = r_x + NTRI * 256;
-  float* r_s = r_y + NTRI * 256;                    // scratch tiles
-  float4* s_gp = reinterpret_cast<float4*>(r_s + 4 * 512);  // [NP] (mant, 1/mant, zeros, exponent)
+  float* r_s = r_y + NTRI * 256;                                    // scratch tiles
+  float4* s_gp = reinterpret_cast<float4*>(r_s + kWaves * 512);     // [NP] (mant, 1/mant, zeros, exponent)
   float* s_alpha = reinterpret_cast<float*>(s_gp + NP);
   float* s_beta = s_alpha + NP;
   float* s_gam = s_beta + NP;
   uint64_t* s_anc = reinterpret_cast<uint64_t*>(s_gam + NP);  // [NP][W]
   __shared__ int s_maxdepth;
 
-  int bh, cb;
-  if (!gdn_block(blockIdx.x, BH, kWCB, &bh, &cb)) return;
+  const int bh = blockIdx.x;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int ct = wave;                    // this wave's column tile
-  const int col = cb * kWC + 16 * ct + lr;  // this lane's state column in the outputs
+  const int col = 16 * wave + lr;  // this lane's state column
 
   // ---- 1. loads
   if (tid == 0) s_maxdepth = 1;
   {
     constexpr int kGr = 2 * NP * (kRowB / 16);  // 16-byte granules of [Q; K]
-    constexpr int kPer = kGr / kGThreads;
-    constexpr int kBatch = kPer % 8 == 0 ? 8 : (kPer % 4 == 0 ? 4 : 2);
-    static_assert(kGr % kGThreads == 0 && kPer % kBatch == 0, "granules per thread");
+    constexpr int kPer = (kGr + kTThreads - 1) / kTThreads;
+    uint4 g[kPer];
 #pragma unroll
-    for (int u0 = 0; u0 < kPer; u0 += kBatch) {
-      uint4 g[kBatch];
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kTThreads;
+      const int row = e >> 4, gr = e & 15;
+      const bool isk = row >= NP;
+      const int t = isk ? row - NP : row;
+      g[u] = make_uint4(0, 0, 0, 0);
+      if (e < kGr && t < N)
+        g[u] = *reinterpret_cast<const uint4*>((isk ? k : q) +
+                                               ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
+    }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int e = tid + (u0 + u) * kGThreads;
-        const int row = e >> 4, gr = e & 15;
-        const bool isk = row >= NP;
-        const int t = isk ? row - NP : row;
-        g[u] = make_uint4(0, 0, 0, 0);
-        if (t < N)
-          g[u] = *reinterpret_cast<const uint4*>((isk ? k : q) +
-                                                 ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int e = tid + (u0 + u) * kGThreads;
-        *reinterpret_cast<uint4*>(r_qk + gswz(e >> 4, (e & 15) * 16)) = g[u];
-      }
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kTThreads;
+      if (e < kGr) *reinterpret_cast<uint4*>(r_qk + gswz(e >> 4, (e & 15) * 16)) = g[u];
     }
   }
   // issue order matters: the waits for the rows above and the loads below must
@@ -706,25 +698,26 @@ void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     for (int w = 0; w < W; ++w)
       s_anc[t * W + w] = t < N ? anc_clean(anc[(static_cast<size_t>(b) * N + t) * W + w], t, w) : 0ull;
   }
-  // v at this wave's output positions (row 16 rt + 4 lg + r, column `col`)
+  // v at the right-hand side's positions: column `col` of nodes 16 mt + 4 r + lg
   uint16_t vv[NT][4];
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt)
+  for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * rt + 4 * lg + r;
-      vv[rt][r] = t < N ? v[((static_cast<size_t>(b) * N + t) * H + h) * kDk + col] : static_cast<uint16_t>(0);
+      const int t = 16 * mt + 4 * r + lg;
+      vv[mt][r] = t < N ? v[((static_cast<size_t>(b) * N + t) * H + h) * kDk + col] : static_cast<uint16_t>(0);
     }
   __builtin_amdgcn_sched_barrier(0);
-  // S0 fragments of column tile ct: lane (lr, lg) holds rows 32 ks + 8 lg .. +7
-  // of column `col` (the B operand of v_mfma_f32_16x16x32_bf16)
-  float s0f[4][8];
+  // S0 of this wave's columns in 16-byte loads: load u = 2 ks + hf gives lane
+  // (lr, lg) = (4 q + b, lg) columns 16 w + 4 q .. + 3 of row 32 ks + 8 lg + 4 hf
+  // + b; a 4 x 4 transpose inside each quad (in step 5) then leaves lane
+  // (lr, lg) rows 32 ks + 8 lg .. + 7 of column `col`, the bf16 operand layout
+  float4 s0q[kDk / 16];
   {
-    const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + col;
+    const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s0f[ks][j] = s0[static_cast<size_t>(32 * ks + 8 * lg + j) * kDk];
+    for (int u = 0; u < kDk / 16; ++u)
+      s0q[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
   }
   lds_barrier();
 
@@ -740,39 +733,54 @@ void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (t < N) atomicMax(&s_maxdepth, dpt);
   }
   lds_barrier();
-  for (int u = wave; u < 2 * NTRI; u += 4) {
-    const int part = u >= NTRI, lt = part ? u - NTRI : u;  // Y tiles, then X tiles
-    int rt = 0;
-    while ((rt + 1) * (rt + 2) / 2 <= lt) ++rt;
-    const int kt = lt - rt * (rt + 1) / 2;
-    const int arow = (part ? NP : 0) + 16 * rt + lr, brow = NP + 16 * kt + lr;
-    gf32x4_t g = {0.f, 0.f, 0.f, 0.f};
+  // This wave's tiles u = wave + 8 m, the loop unrolled so that one tile's
+  // LDS reads overlap another's products; the masks and gate ratios are
+  // selects over operands read up front.
 #pragma unroll
-    for (int ks = 0; ks < kDk / 32; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(r_qk + gswz(arow, 2 * (32 * ks + 8 * lg)));
-      const uint4 bk = *reinterpret_cast<const uint4*>(r_qk + gswz(brow, 2 * (32 * ks + 8 * lg)));
-      g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8_t, a),
-                                                   __builtin_bit_cast(gbf16x8_t, bk), g, 0, 0, 0);
-    }
-    // masks and gate ratios: Y over ancestors-or-self, X over strict ancestors
-    const int i = 16 * kt + lr;
-    const float4 gi = s_gp[i];
-    float* dst = (part ? r_x : r_y) + lt * 256;
+  for (int m = 0; m < (2 * NTRI + kWaves - 1) / kWaves; ++m) {
+    const int u = wave + kWaves * m;
+    if (u < 2 * NTRI) {
+      const int part = u >= NTRI, lt = part ? u - NTRI : u;  // Y tiles, then X tiles
+      int rt = 0;
+      while ((rt + 1) * (rt + 2) / 2 <= lt) ++rt;
+      const int kt = lt - rt * (rt + 1) / 2;
+      const int arow = (part ? NP : 0) + 16 * rt + lr, brow = NP + 16 * kt + lr;
+      uint4 a[kDk / 32], bk[kDk / 32];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * rt + 4 * lg + r;
-      const bool on = ((s_anc[t * W + (i >> 6)] >> (i & 63)) & 1ull) && !(part && i == t);
-      float val = 0.0f;
-      if (on) {
-        const float4 gt = s_gp[t];
-        float ratio = 1.0f;
-        if (i != t)
-          ratio = __float_as_int(gt.z) != __float_as_int(gi.z)
-                      ? 0.0f
-                      : ldexpf(gt.x * gi.y, __float_as_int(gt.w) - __float_as_int(gi.w));
-        val = part ? s_beta[t] * ratio * g[r] : ratio * g[r];
+      for (int ks = 0; ks < kDk / 32; ++ks) {
+        a[ks] = *reinterpret_cast<const uint4*>(r_qk + gswz(arow, 2 * (32 * ks + 8 * lg)));
+        bk[ks] = *reinterpret_cast<const uint4*>(r_qk + gswz(brow, 2 * (32 * ks + 8 * lg)));
       }
-      dst[tix(4 * lg + r, lr)] = val;
+      // the mask operands: column node i, row nodes t = 16 rt + 4 lg + r
+      const int i = 16 * kt + lr;
+      const float4 gi = s_gp[i];
+      float4 gt[4];
+      uint64_t at[4];
+      float bt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * rt + 4 * lg + r;
+        gt[r] = s_gp[t];
+        at[r] = s_anc[t * W + (i >> 6)];
+        bt[r] = part ? s_beta[t] : 1.0f;
+      }
+      gf32x4_t g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kDk / 32; ++ks)
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8_t, a[ks]),
+                                                     __builtin_bit_cast(gbf16x8_t, bk[ks]), g, 0, 0, 0);
+      // Y over ancestors-or-self, X over strict ancestors (times beta_t)
+      float* dst = (part ? r_x : r_y) + lt * 256;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * rt + 4 * lg + r;
+        const bool on = ((at[r] >> (i & 63)) & 1ull) && !(part && i == t);
+        const float ratio = i == t ? 1.0f
+                            : (__float_as_int(gt[r].z) != __float_as_int(gi.z)
+                                   ? 0.0f
+                                   : ldexpf(gt[r].x * gi.y, __float_as_int(gt[r].w) - __float_as_int(gi.w)));
+        dst[tix(4 * lg + r, lr)] = on ? bt[r] * ratio * g[r] : 0.0f;
+      }
     }
   }
   lds_barrier();
@@ -784,7 +792,7 @@ void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     while ((1 << J) < hmax) ++J;
     float* mb = r_s + wave * 512;  // this wave's two scratch tiles
     float* pb = mb + 256;
-    for (int bb = wave; bb < NT; bb += 4) {
+    for (int bb = wave; bb < NT; bb += kWaves) {
       float* xb = r_x + ltri(bb, bb) * 256;
       // M = I - X (the first factor), P = X X (the next power)
       const gf32x4_t p = mm16(xb, xb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
@@ -814,7 +822,7 @@ void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   {
     float* tb = r_s + wave * 512;
     for (int a = NT - 1; a >= 0; --a) {
-      for (int t = a + wave; t < NT; t += 4) {
+      for (int t = a + wave; t < NT; t += kWaves) {
         float* yt = r_y + ltri(t, a) * 256;
         gf32x4_t acc = tload(yt, lr, lg);
         for (int c = a + 1; c <= t; ++c)
@@ -829,66 +837,79 @@ void gdn_cols_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     }
   }
 
-  // ---- 5. [Q; K] S0 for this wave's column tile
-  gf32x4_t qs[NT], ksa[NT];
+  // ---- 5. [Q; K] S0 for this wave's columns.  Node tile mt of Q: the product
+  // S0^T Q^T leaves lane (lr, lg) node 16 mt + lr, columns 16 w + 4 lg + r.  Of
+  // K: K S0 with A-row i reading node 4 (i & 3) + (i >> 2) of the tile, which
+  // leaves lane (lr, lg) column `col` of nodes 16 mt + 4 r + lg.
+  gbf16x8_t shi[kDk / 32], slo[kDk / 32];
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    qs[rt] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
-    ksa[rt] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int u = 0; u < kDk / 16; ++u) s0q[u] = quad_transpose(s0q[u], lr & 3);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    gbf16x8_t hi, lo;
+  for (int ks = 0; ks < kDk / 32; ++ks) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      hi[j] = static_cast<__bf16>(s0f[ks][j]);
-      lo[j] = static_cast<__bf16>(s0f[ks][j] - static_cast<float>(hi[j]));
-    }
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      const uint4 aq = *reinterpret_cast<const uint4*>(r_qk + gswz(16 * rt + lr, 2 * (32 * ks + 8 * lg)));
-      const uint4 ak = *reinterpret_cast<const uint4*>(r_qk + gswz(NP + 16 * rt + lr, 2 * (32 * ks + 8 * lg)));
-      const gbf16x8_t q8 = __builtin_bit_cast(gbf16x8_t, aq), k8 = __builtin_bit_cast(gbf16x8_t, ak);
-      qs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q8, hi, qs[rt], 0, 0, 0);
-      qs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q8, lo, qs[rt], 0, 0, 0);
-      ksa[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, hi, ksa[rt], 0, 0, 0);
-      ksa[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, lo, ksa[rt], 0, 0, 0);
+      const float4& fq = s0q[2 * ks + (j >> 2)];
+      const float x = (j & 3) == 0 ? fq.x : (j & 3) == 1 ? fq.y : (j & 3) == 2 ? fq.z : fq.w;
+      const __bf16 hv = static_cast<__bf16>(x);
+      shi[ks][j] = hv;
+      slo[ks][j] = static_cast<__bf16>(x - static_cast<float>(hv));
     }
   }
-  lds_barrier();  // every read of [Q; K] is done: its LDS takes the RHS
-
-  // ---- 6. right-hand side beta (v - gamma K S0), then O = gamma Q S0 + M RHS
+  const int kperm = 4 * (lr & 3) + (lr >> 2);
+  gf32x4_t qs[NT], ksa[NT];
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt)
+  for (int mt = 0; mt < NT; ++mt) {
+    qs[mt] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+    ksa[mt] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDk / 32; ++ks) {
+      const gbf16x8_t q8 = __builtin_bit_cast(
+          gbf16x8_t, *reinterpret_cast<const uint4*>(r_qk + gswz(16 * mt + lr, 2 * (32 * ks + 8 * lg))));
+      const gbf16x8_t k8 = __builtin_bit_cast(
+          gbf16x8_t, *reinterpret_cast<const uint4*>(r_qk + gswz(NP + 16 * mt + kperm, 2 * (32 * ks + 8 * lg))));
+      qs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(slo[ks], q8, qs[mt], 0, 0, 0);
+      qs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(shi[ks], q8, qs[mt], 0, 0, 0);
+      ksa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, slo[ks], ksa[mt], 0, 0, 0);
+      ksa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, shi[ks], ksa[mt], 0, 0, 0);
+    }
+  }
+
+  // ---- 6. right-hand side beta_t (v_t - gamma_t (K S0)_t) in registers: lane
+  // (lr, lg) holds column `col` of node 4 ks + lg for k-step ks of the output
+  // product (rows past N have zero v, k and beta); then O^T = RHS^T M^T +
+  // gamma (Q S0)^T over M's lower-triangular tiles, a lane ending with four
+  // consecutive columns of one node
+  float rhs[NP / 4];
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * rt + 4 * lg + r;
-      r_u[t * kWUP + 16 * ct + lr] = s_beta[t] * (bf16_to_f32(vv[rt][r]) - s_gam[t] * ksa[rt][r]);
+      const int n = 16 * mt + 4 * r + lg;
+      rhs[4 * mt + r] = s_beta[n] * (bf16_to_f32(vv[mt][r]) - s_gam[n] * ksa[mt][r]);
     }
-  lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    gf32x4_t acc;
+    const int t = 16 * rt + lr;
+    gf32x4_t acc = s_gam[t] * qs[rt], acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = s_gam[16 * rt + 4 * lg + r] * qs[rt][r];
     for (int a = 0; a <= rt; ++a) {
-      const float* mt = r_y + ltri(rt, a) * 256;
+      const float* mtile = r_y + ltri(rt, a) * 256;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float am = mt[tix(lr, 4 * ks + lg)];
-        const float bu = r_u[(16 * a + 4 * ks + lg) * kWUP + 16 * ct + lr];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(am, bu, acc, 0, 0, 0);
+      for (int ks = 0; ks < 4; ks += 2) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(rhs[4 * a + ks], mtile[tix(lr, 4 * ks + lg)], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(rhs[4 * a + ks + 1], mtile[tix(lr, 4 * ks + 4 + lg)], acc2,
+                                                    0, 0, 0);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * rt + 4 * lg + r;
-      if (t < N) {
-        const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + col;
-        if constexpr (sizeof(TO) == 2)
-          out[off] = f32_to_bf16(acc[r]);
-        else
-          out[off] = acc[r];
+    acc += acc2;
+    if (t < N) {
+      const size_t off = ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * wave + 4 * lg;
+      if constexpr (sizeof(TO) == 2) {
+        const mbf16x4_t w = {static_cast<__bf16>(acc[0]), static_cast<__bf16>(acc[1]),
+                             static_cast<__bf16>(acc[2]), static_cast<__bf16>(acc[3])};
+        *reinterpret_cast<uint2*>(out + off) = __builtin_bit_cast(uint2, w);
+      } else {
+        *reinterpret_cast<float4*>(out + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
     }
   }
@@ -1089,18 +1110,17 @@ hipError_t max_lds_once(std::atomic<int>* done, const void* fn, int bytes) {
 }
 
 template <typename TO, int NT>
-hipError_t launch_gdn_cols_nt(const void* q, const void* k, const void* v, const float* alpha,
-                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
-                              int H, void* out, hipStream_t stream) {
+hipError_t launch_gdn_tri_nt(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                             int H, void* out, hipStream_t stream) {
   constexpr int lds = GdnLds<NT>::kBytes;
   static_assert(lds + 16 <= 160 * 1024, "LDS budget");
   static std::atomic<int> lds_set[kMaxDevices];
-  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_cols_kernel<TO, NT>), lds);
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_tri_kernel<TO, NT>), lds);
   if (attr != hipSuccess) return attr;
-  const int BH = B * H;
-  hipLaunchKernelGGL((gdn_cols_kernel<TO, NT>), dim3(gdn_grid(BH, kWCB)), dim3(kGThreads), lds, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), alpha, beta, S0, anc, N, H, BH, static_cast<TO*>(out));
+  hipLaunchKernelGGL((gdn_tri_kernel<TO, NT>), dim3(static_cast<unsigned>(B) * H), dim3(kTThreads), lds,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), alpha, beta, S0, anc, N, H, static_cast<TO*>(out));
   return hipGetLastError();
 }
 
@@ -1140,11 +1160,11 @@ hipError_t launch_gdn_head(const void* q, const void* k, const void* v, const fl
 }
 
 template <typename TO>
-hipError_t launch_gdn_cols(const void* q, const void* k, const void* v, const float* alpha,
+hipError_t launch_gdn_tri(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                            int H, void* out, hipStream_t stream) {
 #define TV_GDN_NT(X) \
-  case X: return launch_gdn_cols_nt<TO, X>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+  case X: return launch_gdn_tri_nt<TO, X>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
   switch ((N + 15) / 16) {
     TV_GDN_NT(5);
     TV_GDN_NT(6);
@@ -1181,10 +1201,10 @@ hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* 
   (void)Dv;
   if (dtype == TV_BF16 && out_dtype == TV_BF16)
     return N <= 64 ? launch_gdn_head<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
-                   : launch_gdn_cols<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+                   : launch_gdn_tri<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_BF16 && out_dtype == TV_F32)
     return N <= 64 ? launch_gdn_head<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
-                   : launch_gdn_cols<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+                   : launch_gdn_tri<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_F32 && out_dtype == TV_F32)
     return launch_gdn_f32(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   return hipErrorInvalidValue;
