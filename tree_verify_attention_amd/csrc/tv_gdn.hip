@@ -552,9 +552,10 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 // w owning state columns 16 w .. 16 w + 15; the node count is padded to
 // NP = 16 NT.  The Gram products and the solve run once per head.
 //
-//  1. q and k rows (bf16, exact) into LDS; v at this lane's right-hand-side
-//     positions and S0's columns of this wave into registers, in flight
-//     through steps 2-4, which do not need them.
+//  1. q and k rows (bf16, exact) into LDS; v of this wave's columns into
+//     registers in 16-byte pieces (parked in LDS once the solve is done), and
+//     after the Gram tiles S0's columns of this wave, in flight through steps
+//     2-4, which do not need them.
 //  2. Gate products per node, then the Gram tiles [Q; K] K^T on bf16 MFMA,
 //     only the 16 x 16 tiles on or below the block diagonal (ancestors precede
 //     descendants), each masked and scaled by the gate ratios as it comes out:
@@ -641,9 +642,13 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   constexpr int kWaves = kTThreads / 64;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* r_qk = smem;
-  float* r_x = reinterpret_cast<float*>(smem + L::kQK);
-  float* r_y = r_x + NTRI * 256;
-  float* r_s = r_y + NTRI * 256;                                    // scratch tiles
+  float* r_y = reinterpret_cast<float*>(smem + L::kQK);
+  float* r_x = r_y + NTRI * 256;
+  float* r_s = r_x + NTRI * 256;                                    // scratch tiles
+  // once the solve is done, X and the scratch tiles hold v for the right-hand
+  // side: wave w's 16 columns of every node, 32 bytes per node
+  uint16_t* r_v = reinterpret_cast<uint16_t*>(r_x);
+  static_assert(NTRI * 1024 + kWaves * 2048 >= NP * 32 * kWaves, "v fits X and the scratch tiles");
   float4* s_gp = reinterpret_cast<float4*>(r_s + kWaves * 512);     // [NP] (mant, 1/mant, zeros, exponent)
   float* s_alpha = reinterpret_cast<float*>(s_gp + NP);
   float* s_beta = s_alpha + NP;
@@ -656,7 +661,7 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-  const int col = 16 * wave + lr;  // this lane's state column
+  // lane (lr, lg) owns state column col = 16 wave + lr
 
   // ---- 1. loads
   if (tid == 0) s_maxdepth = 1;
@@ -681,9 +686,18 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       if (e < kGr) *reinterpret_cast<uint4*>(r_qk + gswz(e >> 4, (e & 15) * 16)) = g[u];
     }
   }
-  // issue order matters: the waits for the rows above and the loads below must
-  // not include S0's loads, which stay in flight until step 5
-  __builtin_amdgcn_sched_barrier(0);
+  // v of this wave's columns, 16 bytes (8 columns of one node) per load:
+  // granule e = lane + 64 u is node e / 2, columns 16 w + 8 (e % 2) .. + 7
+  constexpr int kVPer = (2 * NP + 63) / 64;
+  uint4 vg[kVPer];
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) {
+    const int e = lane + 64 * u, t = e >> 1;
+    vg[u] = make_uint4(0, 0, 0, 0);
+    if (t < N)
+      vg[u] = *reinterpret_cast<const uint4*>(v + ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * wave +
+                                              8 * (e & 1));
+  }
   if (tid < NP) {
     const int t = tid;
     float a = 1.0f, be = 0.0f;
@@ -697,27 +711,6 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int w = 0; w < W; ++w)
       s_anc[t * W + w] = t < N ? anc_clean(anc[(static_cast<size_t>(b) * N + t) * W + w], t, w) : 0ull;
-  }
-  // v at the right-hand side's positions: column `col` of nodes 16 mt + 4 r + lg
-  uint16_t vv[NT][4];
-#pragma unroll
-  for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * mt + 4 * r + lg;
-      vv[mt][r] = t < N ? v[((static_cast<size_t>(b) * N + t) * H + h) * kDk + col] : static_cast<uint16_t>(0);
-    }
-  __builtin_amdgcn_sched_barrier(0);
-  // S0 of this wave's columns in 16-byte loads: load u = 2 ks + hf gives lane
-  // (lr, lg) = (4 q + b, lg) columns 16 w + 4 q .. + 3 of row 32 ks + 8 lg + 4 hf
-  // + b; a 4 x 4 transpose inside each quad (in step 5) then leaves lane
-  // (lr, lg) rows 32 ks + 8 lg .. + 7 of column `col`, the bf16 operand layout
-  float4 s0q[kDk / 16];
-  {
-    const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
-#pragma unroll
-    for (int u = 0; u < kDk / 16; ++u)
-      s0q[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
   }
   lds_barrier();
 
@@ -739,10 +732,12 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
   for (int m = 0; m < (2 * NTRI + kWaves - 1) / kWaves; ++m) {
     const int u = wave + kWaves * m;
-    if (u < 2 * NTRI) {
+    if ((2 * NTRI) % kWaves == 0 || u < 2 * NTRI) {
       const int part = u >= NTRI, lt = part ? u - NTRI : u;  // Y tiles, then X tiles
-      int rt = 0;
-      while ((rt + 1) * (rt + 2) / 2 <= lt) ++rt;
+      // row tile rt: the largest with rt (rt + 1) / 2 <= lt
+      int rt = static_cast<int>((__builtin_sqrtf(static_cast<float>(8 * lt + 1)) - 1.0f) * 0.5f);
+      rt += (rt + 1) * (rt + 2) / 2 <= lt ? 1 : 0;
+      rt -= rt * (rt + 1) / 2 > lt ? 1 : 0;
       const int kt = lt - rt * (rt + 1) / 2;
       const int arow = (part ? NP : 0) + 16 * rt + lr, brow = NP + 16 * kt + lr;
       uint4 a[kDk / 32], bk[kDk / 32];
@@ -782,6 +777,19 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         dst[tix(4 * lg + r, lr)] = on ? bt[r] * ratio * g[r] : 0.0f;
       }
     }
+  }
+  // S0 goes out once the Gram tiles are issued (with the rows above it held
+  // back the rows' own loads) and stays in flight through steps 3 and 4.  S0
+  // of this wave's columns in 16-byte loads: load u = 2 ks + hf gives lane
+  // (lr, lg) = (4 q + b, lg) columns 16 w + 4 q .. + 3 of row 32 ks + 8 lg +
+  // 4 hf + b; a 4 x 4 transpose inside each quad (in step 5) then leaves lane
+  // (lr, lg) rows 32 ks + 8 lg .. + 7 of column `col`, the bf16 operand layout
+  float4 s0q[kDk / 16];
+  {
+    const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
+#pragma unroll
+    for (int u = 0; u < kDk / 16; ++u)
+      s0q[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
   }
   lds_barrier();
 
@@ -836,6 +844,14 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       lds_barrier();
     }
   }
+  // v into this wave's part of X and the scratch tiles (free since the
+  // barrier above); only this wave reads it back
+  uint16_t* vw = r_v + wave * NP * 16;
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) {
+    const int e = lane + 64 * u;
+    if (e < 2 * NP) *reinterpret_cast<uint4*>(vw + (e >> 1) * 16 + 8 * (e & 1)) = vg[u];
+  }
 
   // ---- 5. [Q; K] S0 for this wave's columns.  Node tile mt of Q: the product
   // S0^T Q^T leaves lane (lr, lg) node 16 mt + lr, columns 16 w + 4 lg + r.  Of
@@ -879,13 +895,14 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // product (rows past N have zero v, k and beta); then O^T = RHS^T M^T +
   // gamma (Q S0)^T over M's lower-triangular tiles, a lane ending with four
   // consecutive columns of one node
+  wave_lds_sync();  // this wave's v is in LDS
   float rhs[NP / 4];
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = 16 * mt + 4 * r + lg;
-      rhs[4 * mt + r] = s_beta[n] * (bf16_to_f32(vv[mt][r]) - s_gam[n] * ksa[mt][r]);
+      rhs[4 * mt + r] = s_beta[n] * (bf16_to_f32(vw[n * 16 + lr]) - s_gam[n] * ksa[mt][r]);
     }
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
