@@ -726,55 +726,70 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (t < N) atomicMax(&s_maxdepth, dpt);
   }
   lds_barrier();
-  // This wave's tiles u = wave + 8 m, the loop unrolled so that one tile's
-  // LDS reads overlap another's products; the masks and gate ratios are
-  // selects over operands read up front.
+  // Waves 0-3 form Y's tiles, waves 4-7 X's.  Wave p of a part takes the
+  // block rows p and NT - 1 - p (NT + 1 tiles: balanced), so a row's A
+  // operand (its bf16 q or k rows) and its mask operands are read once for
+  // all of the row's tiles; the next tile's key rows are read before the
+  // current tile's products.  The masks and gate ratios are selects.
+  {
+    const int part = wave >> 2, p = wave & 3;
 #pragma unroll
-  for (int m = 0; m < (2 * NTRI + kWaves - 1) / kWaves; ++m) {
-    const int u = wave + kWaves * m;
-    if ((2 * NTRI) % kWaves == 0 || u < 2 * NTRI) {
-      const int part = u >= NTRI, lt = part ? u - NTRI : u;  // Y tiles, then X tiles
-      // row tile rt: the largest with rt (rt + 1) / 2 <= lt
-      int rt = static_cast<int>((__builtin_sqrtf(static_cast<float>(8 * lt + 1)) - 1.0f) * 0.5f);
-      rt += (rt + 1) * (rt + 2) / 2 <= lt ? 1 : 0;
-      rt -= rt * (rt + 1) / 2 > lt ? 1 : 0;
-      const int kt = lt - rt * (rt + 1) / 2;
-      const int arow = (part ? NP : 0) + 16 * rt + lr, brow = NP + 16 * kt + lr;
-      uint4 a[kDk / 32], bk[kDk / 32];
+    for (int hr = 0; hr < 2; ++hr) {
+      const int rt = hr == 0 ? p : NT - 1 - p;
+      if (p < (NT + 1) / 2 && !(hr == 1 && rt == p)) {
+        const int arow = (part ? NP : 0) + 16 * rt + lr, t0 = 16 * rt + 4 * lg;
+        uint4 a[kDk / 32];
 #pragma unroll
-      for (int ks = 0; ks < kDk / 32; ++ks) {
-        a[ks] = *reinterpret_cast<const uint4*>(r_qk + gswz(arow, 2 * (32 * ks + 8 * lg)));
-        bk[ks] = *reinterpret_cast<const uint4*>(r_qk + gswz(brow, 2 * (32 * ks + 8 * lg)));
-      }
-      // the mask operands: column node i, row nodes t = 16 rt + 4 lg + r
-      const int i = 16 * kt + lr;
-      const float4 gi = s_gp[i];
-      float4 gt[4];
-      uint64_t at[4];
-      float bt[4];
+        for (int ks = 0; ks < kDk / 32; ++ks)
+          a[ks] = *reinterpret_cast<const uint4*>(r_qk + gswz(arow, 2 * (32 * ks + 8 * lg)));
+        float4 gt[4];
+        uint64_t at[4][W];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * rt + 4 * lg + r;
-        gt[r] = s_gp[t];
-        at[r] = s_anc[t * W + (i >> 6)];
-        bt[r] = part ? s_beta[t] : 1.0f;
-      }
-      gf32x4_t g = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 4; ++r) {
+          gt[r] = s_gp[t0 + r];
 #pragma unroll
-      for (int ks = 0; ks < kDk / 32; ++ks)
-        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8_t, a[ks]),
-                                                     __builtin_bit_cast(gbf16x8_t, bk[ks]), g, 0, 0, 0);
-      // Y over ancestors-or-self, X over strict ancestors (times beta_t)
-      float* dst = (part ? r_x : r_y) + lt * 256;
+          for (int w = 0; w < W; ++w) at[r][w] = s_anc[(t0 + r) * W + w];
+        }
+        const float4 bt = part ? *reinterpret_cast<const float4*>(s_beta + t0) : make_float4(1.f, 1.f, 1.f, 1.f);
+        const float bts[4] = {bt.x, bt.y, bt.z, bt.w};
+        uint4 bk[2][kDk / 32];
+        float4 gi[2];
+        auto read_col = [&](int kt, int sl) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * rt + 4 * lg + r;
-        const bool on = ((at[r] >> (i & 63)) & 1ull) && !(part && i == t);
-        const float ratio = i == t ? 1.0f
-                            : (__float_as_int(gt[r].z) != __float_as_int(gi.z)
-                                   ? 0.0f
-                                   : ldexpf(gt[r].x * gi.y, __float_as_int(gt[r].w) - __float_as_int(gi.w)));
-        dst[tix(4 * lg + r, lr)] = on ? bt[r] * ratio * g[r] : 0.0f;
+          for (int ks = 0; ks < kDk / 32; ++ks)
+            bk[sl][ks] = *reinterpret_cast<const uint4*>(r_qk + gswz(NP + 16 * kt + lr, 2 * (32 * ks + 8 * lg)));
+          gi[sl] = s_gp[16 * kt + lr];
+        };
+        read_col(0, 0);
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt) {
+          if (kt <= rt) {
+            if (kt + 1 <= rt) read_col(kt + 1, (kt + 1) & 1);
+            const int sl = kt & 1;
+            gf32x4_t g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < kDk / 32; ++ks)
+              g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8_t, a[ks]),
+                                                           __builtin_bit_cast(gbf16x8_t, bk[sl][ks]), g, 0, 0, 0);
+            // Y over ancestors-or-self, X over strict ancestors (times beta_t)
+            const int i = 16 * kt + lr;
+            float* dst = (part ? r_x : r_y) + ltri(rt, kt) * 256;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = t0 + r;
+              uint64_t aw = at[r][0];
+#pragma unroll
+              for (int w = 1; w < W; ++w) aw = (kt >> 2) == w ? at[r][w] : aw;
+              const bool on = ((aw >> (i & 63)) & 1ull) && !(part && i == t);
+              // gamma_t / gamma_i: 0 when the path below i holds a zero gate
+              float ratio = __builtin_amdgcn_ldexpf(gt[r].x * gi[sl].y,
+                                                    __float_as_int(gt[r].w) - __float_as_int(gi[sl].w));
+              ratio = __float_as_int(gt[r].z) != __float_as_int(gi[sl].z) ? 0.0f : ratio;
+              ratio = i == t ? 1.0f : ratio;
+              dst[tix(4 * lg + r, lr)] = on ? bts[r] * ratio * g[r] : 0.0f;
+            }
+          }
+        }
       }
     }
   }
