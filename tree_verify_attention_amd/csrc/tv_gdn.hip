@@ -624,6 +624,25 @@ __device__ __forceinline__ void tstore(float* T, gf32x4_t v, int lr, int lg) {
 // for the wave's LDS operations only (global loads stay in flight)
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// A 4 x 4 transpose between the register index and the lane group: register
+// j of lane (lr, lg) ends with what register lg of lane (lr, j) held.  Two
+// gfx950 lane swaps exchange the halves (lane groups 0-1 against 2-3), two
+// more the neighbouring groups.
+__device__ __forceinline__ gf32x4_t lg_transpose(gf32x4_t v) {
+  uint32_t x0 = __float_as_uint(v[0]), x1 = __float_as_uint(v[1]);
+  uint32_t x2 = __float_as_uint(v[2]), x3 = __float_as_uint(v[3]);
+  const auto s02 = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
+  x0 = s02[0];
+  x2 = s02[1];
+  x1 = s13[0];
+  x3 = s13[1];
+  const auto s01 = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
+  return gf32x4_t{__uint_as_float(s01[0]), __uint_as_float(s01[1]), __uint_as_float(s23[0]),
+                  __uint_as_float(s23[1])};
+}
+
 // Workgroup barrier over LDS only: unlike __syncthreads it does not wait for
 // the wave's outstanding global loads, so S0's loads stay in flight across it
 __device__ __forceinline__ void lds_barrier() {
@@ -841,23 +860,52 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   lds_barrier();
 
-  // ---- 4. M = Y (I + X)^-1, block column a from the last, over Y
+  // ---- 4. M = Y (I + X)^-1 by block rows: row t of M depends only on row t
+  // of Y and on X, so each wave takes one block row and no barrier is needed
+  // until the row is done.  Inside the row, right-looking and transposed:
+  // accT[a] = (Y_ta - sum_{c > a} M_tc X_ca)^T stays in registers; for c
+  // from t down, M_tc^T = D_c^T accT[c] (stored as M_tc over Y_tc), then
+  // accT[a] -= X_ca^T M_tc^T for every a < c, products that do not depend on
+  // one another.  A transpose between register index and lane group turns an
+  // accumulator into the next product's B operand without LDS.  Waves w and
+  // w + 4 share a SIMD and take rows NT - 1 - w and w, which balances it.
   {
-    float* tb = r_s + wave * 512;
-    for (int a = NT - 1; a >= 0; --a) {
-      for (int t = a + wave; t < NT; t += kWaves) {
-        float* yt = r_y + ltri(t, a) * 256;
-        gf32x4_t acc = tload(yt, lr, lg);
-        for (int c = a + 1; c <= t; ++c)
-          acc = mm16(r_y + ltri(t, c) * 256, r_x + ltri(c, a) * 256, acc, lr, lg, -1.0f);
-        tstore(tb, acc, lr, lg);
-        wave_lds_sync();
-        const gf32x4_t mt = mm16(tb, r_x + ltri(a, a) * 256, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
-        wave_lds_sync();
-        tstore(yt, mt, lr, lg);
+    const int t = wave < 4 ? NT - 1 - wave : (wave - 4 < NT - 4 ? wave - 4 : -1);
+    if (t >= 0) {
+      const float* yrow = r_y + ltri(t, 0) * 256;  // the row's tiles lie one after another
+      gf32x4_t accT[NT];
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        accT[a] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (a <= t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) accT[a][j] = yrow[a * 256 + tix(lr, 4 * lg + j)];
       }
-      lds_barrier();
+#pragma unroll
+      for (int c = NT - 1; c >= 0; --c) {
+        if (c <= t) {
+          const gf32x4_t bt = lg_transpose(accT[c]);
+          const float* dc = r_x + ltri(c, c) * 256;
+          gf32x4_t mt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            mt = __builtin_amdgcn_mfma_f32_16x16x4f32(dc[tix(4 * ks + lg, lr)], bt[ks], mt, 0, 0, 0);
+          float* yt = r_y + ltri(t, c) * 256;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yt[tix(lr, 4 * lg + j)] = mt[j];
+          const gf32x4_t mb = lg_transpose(mt);
+#pragma unroll
+          for (int a2 = 0; a2 < NT; ++a2)
+            if (a2 < c) {
+              const float* xca = r_x + ltri(c, a2) * 256;
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks)
+                accT[a2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-xca[tix(4 * ks + lg, lr)], mb[ks], accT[a2], 0, 0, 0);
+            }
+        }
+      }
     }
+    lds_barrier();
   }
   // v into this wave's part of X and the scratch tiles (free since the
   // barrier above); only this wave reads it back
