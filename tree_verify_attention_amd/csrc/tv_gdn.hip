@@ -650,6 +650,50 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Block row T of M = Y (I + X)^-1 (step 4 of the kernel below), with T a
+// compile-time constant so that the row's steps are straight-line code.
+// accT[a] = (Y_Ta - sum_{c > a} M_Tc X_ca)^T in registers; for c from T down,
+// M_Tc^T = D_c^T accT[c] is stored as M_Tc over Y_Tc, then accT[a] -= X_ca^T
+// M_Tc^T for every a < c.
+template <int T>
+__device__ __forceinline__ void gdn_row_solve(float* r_y, const float* r_x, int lr, int lg) {
+  float* yrow = r_y + ltri(T, 0) * 256;  // the row's tiles lie one after another
+  gf32x4_t accT[T + 1];
+#pragma unroll
+  for (int a = 0; a <= T; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) accT[a][j] = yrow[a * 256 + tix(lr, 4 * lg + j)];
+#pragma unroll
+  for (int c = T; c >= 0; --c) {
+    const gf32x4_t bt = lg_transpose(accT[c]);
+    const float* dc = r_x + ltri(c, c) * 256;
+    gf32x4_t mt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) mt = __builtin_amdgcn_mfma_f32_16x16x4f32(dc[tix(4 * ks + lg, lr)], bt[ks], mt, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) yrow[c * 256 + tix(lr, 4 * lg + j)] = mt[j];
+    const gf32x4_t mb = lg_transpose(mt);
+#pragma unroll
+    for (int a = 0; a < c; ++a) {
+      const float* xca = r_x + ltri(c, a) * 256;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        accT[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(-xca[tix(4 * ks + lg, lr)], mb[ks], accT[a], 0, 0, 0);
+    }
+  }
+}
+
+// the wave-uniform row t (or none, t < 0) to its specialised path
+template <int NT, int K = 0>
+__device__ __forceinline__ void gdn_row_solve_pick(int t, float* r_y, const float* r_x, int lr, int lg) {
+  if constexpr (K < NT) {
+    if (t == K)
+      gdn_row_solve<K>(r_y, r_x, lr, lg);
+    else
+      gdn_row_solve_pick<NT, K + 1>(t, r_y, r_x, lr, lg);
+  }
+}
+
 template <typename TO, int NT>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -861,50 +905,16 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   lds_barrier();
 
   // ---- 4. M = Y (I + X)^-1 by block rows: row t of M depends only on row t
-  // of Y and on X, so each wave takes one block row and no barrier is needed
-  // until the row is done.  Inside the row, right-looking and transposed:
-  // accT[a] = (Y_ta - sum_{c > a} M_tc X_ca)^T stays in registers; for c
-  // from t down, M_tc^T = D_c^T accT[c] (stored as M_tc over Y_tc), then
-  // accT[a] -= X_ca^T M_tc^T for every a < c, products that do not depend on
-  // one another.  A transpose between register index and lane group turns an
-  // accumulator into the next product's B operand without LDS.  Waves w and
-  // w + 4 share a SIMD and take rows NT - 1 - w and w, which balances it.
+  // of Y and on X, so each wave takes one block row (gdn_row_solve) and no
+  // barrier is needed until the rows are done.  Inside a row the products are
+  // right-looking and transposed, so that the updates of one step do not
+  // depend on one another, and a transpose between register index and lane
+  // group turns an accumulator into the next product's B operand without
+  // LDS.  Waves w and w + 4 share a SIMD and take rows NT - 1 - w and w,
+  // which balances it.
   {
     const int t = wave < 4 ? NT - 1 - wave : (wave - 4 < NT - 4 ? wave - 4 : -1);
-    if (t >= 0) {
-      const float* yrow = r_y + ltri(t, 0) * 256;  // the row's tiles lie one after another
-      gf32x4_t accT[NT];
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        accT[a] = gf32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (a <= t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) accT[a][j] = yrow[a * 256 + tix(lr, 4 * lg + j)];
-      }
-#pragma unroll
-      for (int c = NT - 1; c >= 0; --c) {
-        if (c <= t) {
-          const gf32x4_t bt = lg_transpose(accT[c]);
-          const float* dc = r_x + ltri(c, c) * 256;
-          gf32x4_t mt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            mt = __builtin_amdgcn_mfma_f32_16x16x4f32(dc[tix(4 * ks + lg, lr)], bt[ks], mt, 0, 0, 0);
-          float* yt = r_y + ltri(t, c) * 256;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) yt[tix(lr, 4 * lg + j)] = mt[j];
-          const gf32x4_t mb = lg_transpose(mt);
-#pragma unroll
-          for (int a2 = 0; a2 < NT; ++a2)
-            if (a2 < c) {
-              const float* xca = r_x + ltri(c, a2) * 256;
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks)
-                accT[a2] = __builtin_amdgcn_mfma_f32_16x16x4f32(-xca[tix(4 * ks + lg, lr)], mb[ks], accT[a2], 0, 0, 0);
-            }
-        }
-      }
-    }
+    gdn_row_solve_pick<NT>(t, r_y, r_x, lr, lg);
     lds_barrier();
   }
   // v into this wave's part of X and the scratch tiles (free since the
