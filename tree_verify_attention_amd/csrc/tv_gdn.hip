@@ -550,7 +550,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 // ---------------------------------------------------------------------------
 // bf16 inputs, 64 < N <= 128.  One 8-wave workgroup per (sequence, head), wave
 // w owning state columns 16 w .. 16 w + 15; the node count is padded to
-// NP = 16 NT.  The Gram products and the solve run once per head.
+// NP = 16 NT, NT even (96 or 128 nodes).  The Gram products and the solve run
+// once per head.
 //
 //  1. q and k rows (bf16, exact) into LDS; v of this wave's columns into
 //     registers in 16-byte pieces (parked in LDS once the solve is done), and
@@ -559,23 +560,25 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 //  2. Gate products per node, then the Gram tiles [Q; K] K^T on bf16 MFMA,
 //     only the 16 x 16 tiles on or below the block diagonal (ancestors precede
 //     descendants), each masked and scaled by the gate ratios as it comes out:
-//     Y and X in LDS.
+//     Y and X in LDS.  A wave forms the tiles of two block rows (one of Y's
+//     parts or X's), reading each row's operands once.
 //  3. Diagonal blocks D_b = (I + X_bb)^-1.  X_bb couples a node only to its
 //     strict ancestors inside the block, so X_bb^h = 0 for chains of at most h
 //     nodes and the inverse is the product of (I + (-X_bb)^(2^j)),
 //     j < ceil(log2 h): at most four steps, each two 16 x 16 fp32 MFMA
 //     products in one wave.
-//  4. M = Y (I + X)^-1 by block back-substitution over block columns a from
-//     the last: M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a.  M overwrites
-//     Y tile by tile (a tile is read only by its own update); one barrier per
-//     block column.
+//  4. M = Y (I + X)^-1, one block row per wave (a row of M needs only its row
+//     of Y and X): M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a on fp32
+//     MFMA, the row's partial sums in registers.  M goes over Y as bf16 hi and
+//     lo parts.
 //  5. [Q; K] S0 on bf16 MFMA from registers, S0 split into hi = bf16(S0) and
-//     lo = bf16(S0 - hi) (two products: ~16 mantissa bits), in the layouts of
-//     the N <= 64 kernel: Q S0 transposed, as the output accumulates; K S0 with
-//     permuted node rows, as the output product's contraction operand.
-//  6. Right-hand side beta (V - gamma K S0) in registers, then
-//     O = gamma Q S0 + M RHS on fp32 MFMA over M's lower-triangular tiles,
-//     and the store.  No barrier after step 4.
+//     lo = bf16(S0 - hi) (two products: ~16 mantissa bits): Q S0 transposed,
+//     as the output accumulates; K S0 with permuted node rows, which leaves
+//     the right-hand side in the output product's operand layout.
+//  6. Right-hand side beta (V - gamma K S0) in registers, split into bf16 hi
+//     and lo parts, then O = gamma Q S0 + M RHS on bf16 MFMA over 32-node
+//     chunks of M's lower-triangular tiles (three products each), and the
+//     store.  No barrier after step 4.
 // ---------------------------------------------------------------------------
 
 constexpr int kTThreads = 512;
@@ -650,11 +653,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Byte offset of element (r, c) in the bf16 hi or lo half of a 16 x 16 tile of
+// M: row-major, the two 16-byte halves of a row exchanged in rows 8-15, so
+// that 16 lanes reading one half of each of 16 rows spread over the banks.
+__device__ __forceinline__ int mbyte(int r, int c) { return r * 32 + (((c >> 3) ^ (r >> 3)) << 4) + (c & 7) * 2; }
+
 // Block row T of M = Y (I + X)^-1 (step 4 of the kernel below), with T a
 // compile-time constant so that the row's steps are straight-line code.
 // accT[a] = (Y_Ta - sum_{c > a} M_Tc X_ca)^T in registers; for c from T down,
-// M_Tc^T = D_c^T accT[c] is stored as M_Tc over Y_Tc, then accT[a] -= X_ca^T
-// M_Tc^T for every a < c.
+// M_Tc^T = D_c^T accT[c] is stored over Y_Tc as bf16 hi and lo parts of M_Tc
+// (the output product's operands), then accT[a] -= X_ca^T M_Tc^T for every
+// a < c with M_Tc in fp32.
 template <int T>
 __device__ __forceinline__ void gdn_row_solve(float* r_y, const float* r_x, int lr, int lg) {
   float* yrow = r_y + ltri(T, 0) * 256;  // the row's tiles lie one after another
@@ -670,8 +679,16 @@ __device__ __forceinline__ void gdn_row_solve(float* r_y, const float* r_x, int 
     gf32x4_t mt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) mt = __builtin_amdgcn_mfma_f32_16x16x4f32(dc[tix(4 * ks + lg, lr)], bt[ks], mt, 0, 0, 0);
+    // M_Tc[lr][4 lg + j] in bf16 hi and lo parts for the output product
+    mbf16x4_t mh, ml;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) yrow[c * 256 + tix(lr, 4 * lg + j)] = mt[j];
+    for (int j = 0; j < 4; ++j) {
+      mh[j] = static_cast<__bf16>(mt[j]);
+      ml[j] = static_cast<__bf16>(mt[j] - static_cast<float>(mh[j]));
+    }
+    unsigned char* tb = reinterpret_cast<unsigned char*>(yrow + c * 256);
+    *reinterpret_cast<uint2*>(tb + mbyte(lr, 4 * lg)) = __builtin_bit_cast(uint2, mh);
+    *reinterpret_cast<uint2*>(tb + 512 + mbyte(lr, 4 * lg)) = __builtin_bit_cast(uint2, ml);
     const gf32x4_t mb = lg_transpose(mt);
 #pragma unroll
     for (int a = 0; a < c; ++a) {
@@ -712,6 +729,7 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // side: wave w's 16 columns of every node, 32 bytes per node
   uint16_t* r_v = reinterpret_cast<uint16_t*>(r_x);
   static_assert(NTRI * 1024 + kWaves * 2048 >= NP * 32 * kWaves, "v fits X and the scratch tiles");
+  static_assert(NT % 2 == 0, "node tiles come in pairs (32-node chunks of the output product)");
   float4* s_gp = reinterpret_cast<float4*>(r_s + kWaves * 512);     // [NP] (mant, 1/mant, zeros, exponent)
   float* s_alpha = reinterpret_cast<float*>(s_gp + NP);
   float* s_beta = s_alpha + NP;
@@ -928,8 +946,10 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
   // ---- 5. [Q; K] S0 for this wave's columns.  Node tile mt of Q: the product
   // S0^T Q^T leaves lane (lr, lg) node 16 mt + lr, columns 16 w + 4 lg + r.  Of
-  // K: K S0 with A-row i reading node 4 (i & 3) + (i >> 2) of the tile, which
-  // leaves lane (lr, lg) column `col` of nodes 16 mt + 4 r + lg.
+  // K: K S0 with A-row i of tile mt reading node 32 (mt / 2) + 8 (i / 4) +
+  // 4 (mt % 2) + i % 4, which leaves lane (lr, lg) column `col` of nodes
+  // 32 c + 8 lg + j, j < 8, in tiles 2c and 2c + 1: the A-operand layout of
+  // the output product over 32-node chunks.
   gbf16x8_t shi[kDk / 32], slo[kDk / 32];
 #pragma unroll
   for (int u = 0; u < kDk / 16; ++u) s0q[u] = quad_transpose(s0q[u], lr & 3);
@@ -944,7 +964,6 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       slo[ks][j] = static_cast<__bf16>(x - static_cast<float>(hv));
     }
   }
-  const int kperm = 4 * (lr & 3) + (lr >> 2);
   gf32x4_t qs[NT], ksa[NT];
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
@@ -954,8 +973,9 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     for (int ks = 0; ks < kDk / 32; ++ks) {
       const gbf16x8_t q8 = __builtin_bit_cast(
           gbf16x8_t, *reinterpret_cast<const uint4*>(r_qk + gswz(16 * mt + lr, 2 * (32 * ks + 8 * lg))));
+      const int knode = 32 * (mt >> 1) + 8 * (lr >> 2) + 4 * (mt & 1) + (lr & 3);
       const gbf16x8_t k8 = __builtin_bit_cast(
-          gbf16x8_t, *reinterpret_cast<const uint4*>(r_qk + gswz(NP + 16 * mt + kperm, 2 * (32 * ks + 8 * lg))));
+          gbf16x8_t, *reinterpret_cast<const uint4*>(r_qk + gswz(NP + knode, 2 * (32 * ks + 8 * lg))));
       qs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(slo[ks], q8, qs[mt], 0, 0, 0);
       qs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(shi[ks], q8, qs[mt], 0, 0, 0);
       ksa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, slo[ks], ksa[mt], 0, 0, 0);
@@ -963,32 +983,51 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
   }
 
-  // ---- 6. right-hand side beta_t (v_t - gamma_t (K S0)_t) in registers: lane
-  // (lr, lg) holds column `col` of node 4 ks + lg for k-step ks of the output
-  // product (rows past N have zero v, k and beta); then O^T = RHS^T M^T +
-  // gamma (Q S0)^T over M's lower-triangular tiles, a lane ending with four
-  // consecutive columns of one node
+  // ---- 6. right-hand side RHS = beta (V - gamma K S0) in registers, split
+  // into bf16 hi and lo parts: lane (lr, lg) holds column `col` of nodes
+  // 32 c + 8 lg + j of chunk c (rows past N have zero v, k and beta).  Then
+  // O^T = RHS^T M^T + gamma (Q S0)^T on bf16 MFMA over 32-node chunks of M's
+  // lower-triangular tiles, three products per chunk (hi hi, hi lo, lo hi:
+  // about 16 mantissa bits), a lane ending with four consecutive columns of
+  // one node
   wave_lds_sync();  // this wave's v is in LDS
-  float rhs[NP / 4];
+  constexpr int NH = NT / 2;
+  gbf16x8_t rh[NH], rl[NH];
 #pragma unroll
-  for (int mt = 0; mt < NT; ++mt)
+  for (int c = 0; c < NH; ++c) {
+    const int n0 = 32 * c + 8 * lg;
+    const float4 b0 = *reinterpret_cast<const float4*>(s_beta + n0);
+    const float4 b1 = *reinterpret_cast<const float4*>(s_beta + n0 + 4);
+    const float4 g0 = *reinterpret_cast<const float4*>(s_gam + n0);
+    const float4 g1 = *reinterpret_cast<const float4*>(s_gam + n0 + 4);
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = 16 * mt + 4 * r + lg;
-      rhs[4 * mt + r] = s_beta[n] * (bf16_to_f32(vw[n * 16 + lr]) - s_gam[n] * ksa[mt][r]);
+    for (int j = 0; j < 8; ++j) {
+      const float ks0 = j < 4 ? ksa[2 * c][j & 3] : ksa[2 * c + 1][j & 3];
+      const float x = bv[j] * (bf16_to_f32(vw[(n0 + j) * 16 + lr]) - gv[j] * ks0);
+      const __bf16 hv = static_cast<__bf16>(x);
+      rh[c][j] = hv;
+      rl[c][j] = static_cast<__bf16>(x - static_cast<float>(hv));
     }
+  }
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     const int t = 16 * rt + lr;
     gf32x4_t acc = s_gam[t] * qs[rt], acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int a = 0; a <= rt; ++a) {
-      const float* mtile = r_y + ltri(rt, a) * 256;
-#pragma unroll
-      for (int ks = 0; ks < 4; ks += 2) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(rhs[4 * a + ks], mtile[tix(lr, 4 * ks + lg)], acc, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(rhs[4 * a + ks + 1], mtile[tix(lr, 4 * ks + 4 + lg)], acc2,
-                                                    0, 0, 0);
+    for (int c = 0; c < NH; ++c) {
+      if (2 * c <= rt) {
+        // lane (lr, lg): row t, nodes 32 c + 8 lg .. + 7 of tile 2c + lg / 2,
+        // none past the diagonal tile
+        const int a = 2 * c + (lg >> 1);
+        const unsigned char* tb = reinterpret_cast<const unsigned char*>(r_y + ltri(rt, a <= rt ? a : rt) * 256);
+        uint4 mh = *reinterpret_cast<const uint4*>(tb + mbyte(lr, 8 * (lg & 1)));
+        uint4 ml = *reinterpret_cast<const uint4*>(tb + 512 + mbyte(lr, 8 * (lg & 1)));
+        if (2 * c + 1 > rt && a > rt) mh = ml = make_uint4(0, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh[c], __builtin_bit_cast(gbf16x8_t, mh), acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh[c], __builtin_bit_cast(gbf16x8_t, ml), acc2, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl[c], __builtin_bit_cast(gbf16x8_t, mh), acc2, 0, 0, 0);
       }
     }
     acc += acc2;
@@ -1253,13 +1292,11 @@ template <typename TO>
 hipError_t launch_gdn_tri(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                            int H, void* out, hipStream_t stream) {
-#define TV_GDN_NT(X) \
-  case X: return launch_gdn_tri_nt<TO, X>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
-  switch ((N + 15) / 16) {
-    TV_GDN_NT(5);
-    TV_GDN_NT(6);
-    TV_GDN_NT(7);
-    TV_GDN_NT(8);
+#define TV_GDN_NT(X, NT) \
+  case X: return launch_gdn_tri_nt<TO, NT>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+  switch ((N + 31) / 32) {  // node tiles in pairs: the output product takes 32 nodes per step
+    TV_GDN_NT(3, 6);
+    TV_GDN_NT(4, 8);
     default: return hipErrorInvalidValue;
   }
 #undef TV_GDN_NT
