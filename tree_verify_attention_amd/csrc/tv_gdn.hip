@@ -62,41 +62,6 @@ __device__ __forceinline__ uint64_t anc_clean(uint64_t w, int t, int word) {
   return (w & below) | self;
 }
 
-// Product of the gates over an ancestor set, exact at zero gates and free of
-// underflow: the number of zero gates, and the product of the others as
-// mant * 2^ex with |mant| in [0.5, 1).  Gates are multiplied in increasing node
-// order, so a node's running product passes through its ancestors' products
-// bit for bit and a ratio of two of them is the segment's product to within
-// a few ulp.
-struct GateProd {
-  int zeros;
-  int ex;
-  float mant;
-  __device__ float value() const { return zeros ? 0.0f : ldexpf(mant, ex); }
-};
-
-template <int W>
-__device__ __forceinline__ GateProd gate_product(const float* alpha, const uint64_t* set) {
-  GateProd g{0, 0, 1.0f};
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    uint64_t m = set[w];
-    while (m) {
-      const float a = alpha[64 * w + __ffsll(static_cast<unsigned long long>(m)) - 1];
-      m &= m - 1;
-      if (a == 0.0f) {
-        ++g.zeros;
-      } else {
-        int ea, em;
-        g.mant *= frexpf(a, &ea);
-        g.mant = frexpf(g.mant, &em);
-        g.ex += ea + em;
-      }
-    }
-  }
-  return g;
-}
-
 typedef __bf16 gbf16x8_t __attribute__((ext_vector_type(8)));
 typedef float gf32x4_t __attribute__((ext_vector_type(4)));
 
@@ -744,28 +709,33 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   // lane (lr, lg) owns state column col = 16 wave + lr
 
-  // ---- 1. loads
+  // ---- 1. loads: the per-node gates and ancestor words first, then q and k
+  // rows into LDS, then v of this wave's columns, which stays in flight
   if (tid == 0) s_maxdepth = 1;
-  {
-    constexpr int kGr = 2 * NP * (kRowB / 16);  // 16-byte granules of [Q; K]
-    constexpr int kPer = (kGr + kTThreads - 1) / kTThreads;
-    uint4 g[kPer];
+  float g_a = 1.0f, g_b = 0.0f;
+  uint64_t g_w[W];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kTThreads;
-      const int row = e >> 4, gr = e & 15;
-      const bool isk = row >= NP;
-      const int t = isk ? row - NP : row;
-      g[u] = make_uint4(0, 0, 0, 0);
-      if (e < kGr && t < N)
-        g[u] = *reinterpret_cast<const uint4*>((isk ? k : q) +
-                                               ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
-    }
+  for (int w = 0; w < W; ++w) g_w[w] = 0ull;
+  if (tid < N) {
+    const size_t nh = (static_cast<size_t>(b) * N + tid) * H + h;
+    g_a = alpha[nh];
+    g_b = beta[nh];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kTThreads;
-      if (e < kGr) *reinterpret_cast<uint4*>(r_qk + gswz(e >> 4, (e & 15) * 16)) = g[u];
-    }
+    for (int w = 0; w < W; ++w) g_w[w] = anc[(static_cast<size_t>(b) * N + tid) * W + w];
+  }
+  constexpr int kGr = 2 * NP * (kRowB / 16);  // 16-byte granules of [Q; K]
+  constexpr int kPer = (kGr + kTThreads - 1) / kTThreads;
+  uint4 g[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = tid + u * kTThreads;
+    const int row = e >> 4, gr = e & 15;
+    const bool isk = row >= NP;
+    const int t = isk ? row - NP : row;
+    g[u] = make_uint4(0, 0, 0, 0);
+    if (e < kGr && t < N)
+      g[u] = *reinterpret_cast<const uint4*>((isk ? k : q) +
+                                             ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
   }
   // v of this wave's columns, 16 bytes (8 columns of one node) per load:
   // granule e = lane + 64 u is node e / 2, columns 16 w + 8 (e % 2) .. + 7
@@ -779,32 +749,77 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       vg[u] = *reinterpret_cast<const uint4*>(v + ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * wave +
                                               8 * (e & 1));
   }
-  if (tid < NP) {
-    const int t = tid;
-    float a = 1.0f, be = 0.0f;
-    if (t < N) {
-      const size_t nh = (static_cast<size_t>(b) * N + t) * H + h;
-      a = alpha[nh];
-      be = beta[nh];
-    }
-    s_alpha[t] = a;
-    s_beta[t] = be;
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-      s_anc[t * W + w] = t < N ? anc_clean(anc[(static_cast<size_t>(b) * N + t) * W + w], t, w) : 0ull;
+  for (int u = 0; u < kPer; ++u) {
+    const int e = tid + u * kTThreads;
+    if (e < kGr) *reinterpret_cast<uint4*>(r_qk + gswz(e >> 4, (e & 15) * 16)) = g[u];
+  }
+  if (tid < NP) {
+    s_alpha[tid] = g_a;
+    s_beta[tid] = g_b;
+#pragma unroll
+    for (int w = 0; w < W; ++w) s_anc[tid * W + w] = tid < N ? anc_clean(g_w[w], tid, w) : 0ull;
   }
   lds_barrier();
 
-  // ---- 2. gate products per node, then the masked Gram tiles
-  if (tid < NP) {
-    const int t = tid;
-    const GateProd gp = gate_product<W>(s_alpha, s_anc + t * W);
-    s_gam[t] = gp.value();
-    s_gp[t] = make_float4(gp.mant, 1.0f / gp.mant, __int_as_float(gp.zeros), __int_as_float(gp.ex));
-    int dpt = 0;
+  // ---- 2. gate products per node, four lanes per node: lane q of a quad
+  // takes the ancestors in nodes 32 q .. 32 q + 31 (zero count, mantissa and
+  // exponent, factors in node order), and the quad combines its four parts;
+  // then the masked Gram tiles
+  {
+    const int t = tid >> 2, qd = tid & 3;
+    int zeros = 0, ex = 0, dpt = 0;
+    float mant = 1.0f;
+    if (t < NP) {
+      uint32_t m = static_cast<uint32_t>(s_anc[t * W + (qd >> 1)] >> (32 * (qd & 1)));
+      dpt = __popc(m);
+      while (m) {
+        const float al = s_alpha[32 * qd + __ffs(m) - 1];
+        m &= m - 1;
+        if (al == 0.0f) {
+          ++zeros;
+        } else {
+          int ea, em;
+          mant *= frexpf(al, &ea);
+          mant = frexpf(mant, &em);
+          ex += ea + em;
+        }
+      }
+    }
+    // parts 0 and 1, 2 and 3, then the two pairs
+    {
+      const float om = quad_dpp<0xb1>(mant);
+      const int oz = __float_as_int(quad_dpp<0xb1>(__int_as_float(zeros)));
+      const int oe = __float_as_int(quad_dpp<0xb1>(__int_as_float(ex)));
+      const int od = __float_as_int(quad_dpp<0xb1>(__int_as_float(dpt)));
+      int em;
+      mant = frexpf(mant * om, &em);
+      ex += oe + em;
+      zeros += oz;
+      dpt += od;
+    }
+    {
+      const float om = quad_dpp<0x4e>(mant);
+      const int oz = __float_as_int(quad_dpp<0x4e>(__int_as_float(zeros)));
+      const int oe = __float_as_int(quad_dpp<0x4e>(__int_as_float(ex)));
+      const int od = __float_as_int(quad_dpp<0x4e>(__int_as_float(dpt)));
+      int em;
+      mant = frexpf(mant * om, &em);
+      ex += oe + em;
+      zeros += oz;
+      dpt += od;
+    }
+    if (t < NP && qd == 0) {
+      s_gam[t] = zeros ? 0.0f : ldexpf(mant, ex);
+      s_gp[t] = make_float4(mant, 1.0f / mant, __int_as_float(zeros), __int_as_float(ex));
+    }
+    // the deepest node of the wave (bit by bit over ballots), one LDS max per wave
+    const int d = t < N ? dpt : 0;
+    int dm = 0;
 #pragma unroll
-    for (int w = 0; w < W; ++w) dpt += __popcll(s_anc[t * W + w]);
-    if (t < N) atomicMax(&s_maxdepth, dpt);
+    for (int bit = 7; bit >= 0; --bit)
+      if (__ballot(d >= (dm | (1 << bit)))) dm |= 1 << bit;
+    if (lane == 0 && dm > 0) atomicMax(&s_maxdepth, dm);
   }
   lds_barrier();
   // Waves 0-3 form Y's tiles, waves 4-7 X's.  Wave p of a part takes the
