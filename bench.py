@@ -74,6 +74,10 @@ def parse():
                     help="instead of the verify step, time tree_verify_attn alone on the full-size "
                          "shapes of this attention workload (2: batch 8 leaf-sibling trees, "
                          "4: DDTree-shaped batch 64) and print one JSON line for that kernel")
+    ap.add_argument("--gdn-only", type=int, default=0,
+                    help="instead of the verify step, time tree_gdn_verify alone on the verify-cost "
+                         "curve's GDN shape (B=32, H=16, Dk=Dv=128, bf16, spine-first trees) with this "
+                         "many nodes, warm calls, and print one JSON line for that kernel")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "(the known-size reference for HBM byte counters)")
@@ -720,6 +724,36 @@ def attn_only(args, dev) -> dict:
             "frac_of_bf16_mfma_2500TFLOPs": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}
 
 
+def gdn_only(args, dev) -> dict:
+    """tree_gdn_verify alone, inputs resident in HBM, on the verify-cost
+    curve's GDN shape with `args.gdn_only` nodes: K warm calls timed with
+    events on the current stream."""
+    import tree_verify_attention_amd as tv
+    from synth import workloads as W
+    B, N = 32, args.gdn_only
+    trees = W.make_trees(3, "spine_first", B, N, 1000, max_depth=min(8, N), tag=1000 + N)
+    g = W.gdn_inputs(3, B=B, N=N, H=16, Dk=128, Dv=128, tree="spine_first", dtype=torch.bfloat16,
+                     trees=trees, device=dev)
+    m = tv.tree_mask_build(torch.from_numpy(trees.parent).to(dev), torch.full((B,), 1, dtype=torch.int32,
+                                                                            device=dev))
+    out = torch.empty_like(g.v)
+    call = lambda: tv.tree_gdn_verify(g.q, g.k, g.v, g.alpha, g.beta, g.S0, m["anc"], out=out)
+    for _ in range(args.warmup):
+        call()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        call()
+    z.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(z) / args.steps
+    nbytes = sum(t.numel() * t.element_size() for t in (g.q, g.k, g.v, g.alpha, g.beta, g.S0, out, m["anc"]))
+    return {"gdn_only_nodes": N, "B": B, "H": 16, "Dk": 128, "Dv": 128, "steps": args.steps,
+            "warmup": args.warmup, "us_per_call": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -732,6 +766,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.attn_only:
         print(json.dumps(attn_only(args, dev)), flush=True)
+        return
+    if args.gdn_only:
+        print(json.dumps(gdn_only(args, dev)), flush=True)
         return
     if args.config:
         step = Step(dev) if args.config == 3 else None
