@@ -79,6 +79,19 @@ def test_chain_depths_per_node_tile(lib, N):
     check(lib, x, f"chain of {N}")
 
 
+@pytest.mark.parametrize("tree", ["chain", "random_parent"])
+@pytest.mark.parametrize("N", [96, 97])
+def test_past_64_padding_boundary(lib, tree, N):
+    """bf16 inputs on both sides of the past-64 kernel's padding step (96
+    nodes in six 16-node tiles, 97 in eight): chains fill every diagonal
+    block and reach the deepest block row of the back-substitution; random
+    trees mix short and long paths.  The state is large enough that its low
+    bf16 part matters."""
+    x = W.gdn_inputs(55, B=2, N=N, H=3, Dk=128, Dv=128, tree=tree, dtype=torch.bfloat16, device=DEV,
+                     s0_std=0.5)
+    check(lib, x, f"{tree} of {N}")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("N", [64, 128])
 def test_strong_state_and_gates(lib, dtype, N):
