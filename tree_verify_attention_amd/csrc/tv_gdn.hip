@@ -248,6 +248,27 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     gb = beta[nh];
     gw = anc[static_cast<size_t>(b) * N + tid];
   }
+  // S0 goes out in three batches: the first right after the small loads
+  // are issued (behind them in the memory pipeline, so it does not hold them
+  // back), the others between the phases that do not need it, so that no
+  // wave stalls long on a full memory pipeline (issued all at once, or ahead
+  // of the gates and ancestor words, S0 delayed the small loads and the
+  // kernel took longer).  Wave w owns state columns 16w .. 16w + 15.  Load
+  // u = 2 ks + hf gives lane (lr, lg) = (4 q + b, lg) the four columns
+  // 16 w + 4 q .. + 3 of row 32 ks + 8 lg + 4 hf + b (16 rows of 64 bytes per
+  // instruction; 16-byte loads keep the instruction count low, which matters
+  // while misses are slow); a 4 x 4 transpose inside each quad of lanes then
+  // leaves lane (lr, lg) rows 32 ks + 8 lg + j, j < 8, of column 16 w + lr:
+  // the bf16 operand layout of the state products.
+  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
+  float4 f[kDk / 16];
+  auto s0_issue = [&](int u0, int u1) {
+#pragma unroll
+    for (int u = 0; u < kDk / 16; ++u)
+      if (u >= u0 && u < u1)
+        f[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
+  };
+  s0_issue(0, 3);
 #pragma unroll
   for (int u = 0; u < kQKPer; ++u) {
     const int e = tid + u * kMThreads;
@@ -310,25 +331,6 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
     if (t == 0) s_steps = rounds;
   }
   __syncthreads();
-  // S0 goes out once the small loads are in (issued with them, it would
-  // delay them: every workgroup's S0 competes for HBM at the same moment),
-  // in three batches between the phases that do not need it, so that no
-  // wave stalls long on a full memory pipeline.  Wave w owns state columns
-  // 16w .. 16w + 15.  Load u = 2 ks + hf gives lane (lr, lg) = (4 q + b, lg)
-  // the four columns 16 w + 4 q .. + 3 of row 32 ks + 8 lg + 4 hf + b (16
-  // rows of 64 bytes per instruction; 16-byte loads keep the instruction count
-  // low, which matters while misses are slow); a 4 x 4 transpose inside each
-  // quad of lanes then leaves lane (lr, lg) rows 32 ks + 8 lg + j, j < 8, of
-  // column 16 w + lr: the bf16 operand layout of the state products.
-  const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
-  float4 f[kDk / 16];
-  auto s0_issue = [&](int u0, int u1) {
-#pragma unroll
-    for (int u = 0; u < kDk / 16; ++u)
-      if (u >= u0 && u < u1)
-        f[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
-  };
-  s0_issue(0, 3);
 
   // ---- phase 1: the Gram products [Q; K] K^T on MFMA (exact bf16 products)
   constexpr int ngram = NP * NP / 128;  // 2NP / 16 row tiles x NP / 16 key tiles
