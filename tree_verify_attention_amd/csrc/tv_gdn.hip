@@ -891,12 +891,13 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       }
     }
   }
-  // S0 goes out once the Gram tiles are issued (with the rows above it held
-  // back the rows' own loads) and stays in flight through steps 3 and 4.  S0
-  // of this wave's columns in 16-byte loads: load u = 2 ks + hf gives lane
-  // (lr, lg) = (4 q + b, lg) columns 16 w + 4 q .. + 3 of row 32 ks + 8 lg +
-  // 4 hf + b; a 4 x 4 transpose inside each quad (in step 5) then leaves lane
-  // (lr, lg) rows 32 ks + 8 lg .. + 7 of column `col`, the bf16 operand layout
+  // S0 goes out once the Gram tiles are formed and stays in flight through
+  // steps 3 and 4, which do not need it (issued before the gate products it
+  // was no faster).  S0 of this wave's columns in 16-byte loads: load
+  // u = 2 ks + hf gives lane (lr, lg) = (4 q + b, lg) columns 16 w + 4 q ..
+  // + 3 of row 32 ks + 8 lg + 4 hf + b; a 4 x 4 transpose inside each quad
+  // (in step 5) then leaves lane (lr, lg) rows 32 ks + 8 lg .. + 7 of column
+  // `col`, the bf16 operand layout
   float4 s0q[kDk / 16];
   {
     const float* s0 = S0 + static_cast<size_t>(bh) * kDk * kDk + 16 * wave + 4 * (lr >> 2);
@@ -945,8 +946,8 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // right-looking and transposed, so that the updates of one step do not
   // depend on one another, and a transpose between register index and lane
   // group turns an accumulator into the next product's B operand without
-  // LDS.  Waves w and w + 4 share a SIMD and take rows NT - 1 - w and w,
-  // which balances it.
+  // LDS.  Waves w and w + 4 take rows NT - 1 - w and w, which balances the
+  // SIMD that the two waves share when waves are dealt to SIMDs in turn.
   {
     const int t = wave < 4 ? NT - 1 - wave : (wave - 4 < NT - 4 ? wave - 4 : -1);
     gdn_row_solve_pick<NT>(t, r_y, r_x, lr, lg);
