@@ -527,17 +527,19 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 //  2. Gate products per node, then the Gram tiles [Q; K] K^T on bf16 MFMA,
 //     only the 16 x 16 tiles on or below the block diagonal (ancestors precede
 //     descendants), each masked and scaled by the gate ratios as it comes out:
-//     Y and X in LDS.  A wave forms the tiles of two block rows (one of Y's
-//     parts or X's), reading each row's operands once.
+//     Y in LDS in fp32, X transposed in bf16 hi and lo parts.  A wave forms
+//     the tiles of two block rows (one of Y's parts or X's), reading each
+//     row's operands once.
 //  3. Diagonal blocks D_b = (I + X_bb)^-1.  X_bb couples a node only to its
 //     strict ancestors inside the block, so X_bb^h = 0 for chains of at most h
 //     nodes and the inverse is the product of (I + (-X_bb)^(2^j)),
 //     j < ceil(log2 h): at most four steps, each two 16 x 16 fp32 MFMA
-//     products in one wave.
+//     products in one wave; D_b goes over X_bb in X's hi/lo form.
 //  4. M = Y (I + X)^-1, one block row per wave (a row of M needs only its row
-//     of Y and X): M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a on fp32
-//     MFMA, the row's partial sums in registers.  M goes over Y as bf16 hi and
-//     lo parts.
+//     of Y and X): M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a, each
+//     product three bf16 MFMAs on hi/lo parts (about 16 mantissa bits), the
+//     row's partial sums in fp32 registers.  M goes over Y as bf16 hi and lo
+//     parts.
 //  5. [Q; K] S0 on bf16 MFMA from registers, S0 split into hi = bf16(S0) and
 //     lo = bf16(S0 - hi) (two products: ~16 mantissa bits): Q S0 transposed,
 //     as the output accumulates; K S0 with permuted node rows, which leaves
@@ -594,23 +596,41 @@ __device__ __forceinline__ void tstore(float* T, gf32x4_t v, int lr, int lg) {
 // for the wave's LDS operations only (global loads stay in flight)
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// A 4 x 4 transpose between the register index and the lane group: register
-// j of lane (lr, lg) ends with what register lg of lane (lr, j) held.  Two
-// gfx950 lane swaps exchange the halves (lane groups 0-1 against 2-3), two
-// more the neighbouring groups.
-__device__ __forceinline__ gf32x4_t lg_transpose(gf32x4_t v) {
-  uint32_t x0 = __float_as_uint(v[0]), x1 = __float_as_uint(v[1]);
-  uint32_t x2 = __float_as_uint(v[2]), x3 = __float_as_uint(v[3]);
-  const auto s02 = __builtin_amdgcn_permlane32_swap(x0, x2, false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(x1, x3, false, false);
-  x0 = s02[0];
-  x2 = s02[1];
-  x1 = s13[0];
-  x3 = s13[1];
-  const auto s01 = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
-  const auto s23 = __builtin_amdgcn_permlane16_swap(x2, x3, false, false);
-  return gf32x4_t{__uint_as_float(s01[0]), __uint_as_float(s01[1]), __uint_as_float(s23[0]),
-                  __uint_as_float(s23[1])};
+typedef short gs16x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 hi and lo parts of four fp32 values: hi = bf16(x) (round to nearest
+// even), lo = bf16(x - hi); hi + lo carries x to about 16 mantissa bits
+__device__ __forceinline__ void split_hilo(gf32x4_t x, gs16x4_t& hi, gs16x4_t& lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const __bf16 h = static_cast<__bf16>(x[j]);
+    hi[j] = __builtin_bit_cast(short, h);
+    lo[j] = __builtin_bit_cast(short, static_cast<__bf16>(x[j] - static_cast<float>(h)));
+  }
+}
+
+// 16 x 16 x 16 product of hi/lo parts on bf16 MFMA (hi hi + hi lo + lo hi):
+// acc += A B, lane (lr, lg) giving A[lr][4 lg + j] and B[4 lg + j][lr]
+__device__ __forceinline__ gf32x4_t mm16_hilo(gs16x4_t ah, gs16x4_t al, gs16x4_t bh, gs16x4_t bl, gf32x4_t acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+}
+
+// A 16 x 16 tile of X (or of a diagonal inverse D) kept transposed as the A
+// operand of mm16_hilo: bf16 hi part at byte 0, lo part at byte 512, element
+// (r, c) of the transpose at r * 32 + c * 2.  Lane (lr, lg) reads or writes
+// the four elements (lr, 4 lg .. 4 lg + 3) = the tile's (4 lg + j, lr), which
+// is also where an accumulator holds them.
+__device__ __forceinline__ void at_read(const unsigned char* t, int lr, int lg, gs16x4_t& hi, gs16x4_t& lo) {
+  hi = *reinterpret_cast<const gs16x4_t*>(t + lr * 32 + lg * 8);
+  lo = *reinterpret_cast<const gs16x4_t*>(t + 512 + lr * 32 + lg * 8);
+}
+__device__ __forceinline__ void at_write(unsigned char* t, int lr, int lg, gf32x4_t x) {
+  gs16x4_t hi, lo;
+  split_hilo(x, hi, lo);
+  *reinterpret_cast<gs16x4_t*>(t + lr * 32 + lg * 8) = hi;
+  *reinterpret_cast<gs16x4_t*>(t + 512 + lr * 32 + lg * 8) = lo;
 }
 
 // Workgroup barrier over LDS only: unlike __syncthreads it does not wait for
@@ -627,12 +647,13 @@ __device__ __forceinline__ int mbyte(int r, int c) { return r * 32 + (((c >> 3) 
 
 // Block row T of M = Y (I + X)^-1 (step 4 of the kernel below), with T a
 // compile-time constant so that the row's steps are straight-line code.
-// accT[a] = (Y_Ta - sum_{c > a} M_Tc X_ca)^T in registers; for c from T down,
-// M_Tc^T = D_c^T accT[c] is stored over Y_Tc as bf16 hi and lo parts of M_Tc
-// (the output product's operands), then accT[a] -= X_ca^T M_Tc^T for every
-// a < c with M_Tc in fp32.
+// accT[a] = (Y_Ta - sum_{c > a} M_Tc X_ca)^T in registers (fp32, the
+// accumulator layout, which is also the B-operand layout of mm16_hilo); for c
+// from T down, M_Tc^T = D_c^T accT[c] is stored over Y_Tc as bf16 hi and lo
+// parts of M_Tc (the output product's operands), then accT[a] -= X_ca^T
+// M_Tc^T for every a < c.  X and D are read as transposed hi/lo tiles.
 template <int T>
-__device__ __forceinline__ void gdn_row_solve(float* r_y, const float* r_x, int lr, int lg) {
+__device__ __forceinline__ void gdn_row_solve(float* r_y, const unsigned char* r_xt, int lr, int lg) {
   float* yrow = r_y + ltri(T, 0) * 256;  // the row's tiles lie one after another
   gf32x4_t accT[T + 1];
 #pragma unroll
@@ -641,11 +662,10 @@ __device__ __forceinline__ void gdn_row_solve(float* r_y, const float* r_x, int 
     for (int j = 0; j < 4; ++j) accT[a][j] = yrow[a * 256 + tix(lr, 4 * lg + j)];
 #pragma unroll
   for (int c = T; c >= 0; --c) {
-    const gf32x4_t bt = lg_transpose(accT[c]);
-    const float* dc = r_x + ltri(c, c) * 256;
-    gf32x4_t mt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) mt = __builtin_amdgcn_mfma_f32_16x16x4f32(dc[tix(4 * ks + lg, lr)], bt[ks], mt, 0, 0, 0);
+    gs16x4_t bh, bl, dh, dl;
+    split_hilo(accT[c], bh, bl);
+    at_read(r_xt + ltri(c, c) * 1024, lr, lg, dh, dl);
+    const gf32x4_t mt = mm16_hilo(dh, dl, bh, bl, gf32x4_t{0.f, 0.f, 0.f, 0.f});
     // M_Tc[lr][4 lg + j] in bf16 hi and lo parts for the output product
     mbf16x4_t mh, ml;
 #pragma unroll
@@ -656,25 +676,27 @@ __device__ __forceinline__ void gdn_row_solve(float* r_y, const float* r_x, int 
     unsigned char* tb = reinterpret_cast<unsigned char*>(yrow + c * 256);
     *reinterpret_cast<uint2*>(tb + mbyte(lr, 4 * lg)) = __builtin_bit_cast(uint2, mh);
     *reinterpret_cast<uint2*>(tb + 512 + mbyte(lr, 4 * lg)) = __builtin_bit_cast(uint2, ml);
-    const gf32x4_t mb = lg_transpose(mt);
+    if (c > 0) {
+      gs16x4_t nh, nl;  // -M_Tc^T, the updates' B operand
+      split_hilo(-mt, nh, nl);
 #pragma unroll
-    for (int a = 0; a < c; ++a) {
-      const float* xca = r_x + ltri(c, a) * 256;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        accT[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(-xca[tix(4 * ks + lg, lr)], mb[ks], accT[a], 0, 0, 0);
+      for (int a = 0; a < c; ++a) {
+        gs16x4_t xh, xl;
+        at_read(r_xt + ltri(c, a) * 1024, lr, lg, xh, xl);
+        accT[a] = mm16_hilo(xh, xl, nh, nl, accT[a]);
+      }
     }
   }
 }
 
 // the wave-uniform row t (or none, t < 0) to its specialised path
 template <int NT, int K = 0>
-__device__ __forceinline__ void gdn_row_solve_pick(int t, float* r_y, const float* r_x, int lr, int lg) {
+__device__ __forceinline__ void gdn_row_solve_pick(int t, float* r_y, const unsigned char* r_xt, int lr, int lg) {
   if constexpr (K < NT) {
     if (t == K)
-      gdn_row_solve<K>(r_y, r_x, lr, lg);
+      gdn_row_solve<K>(r_y, r_xt, lr, lg);
     else
-      gdn_row_solve_pick<NT, K + 1>(t, r_y, r_x, lr, lg);
+      gdn_row_solve_pick<NT, K + 1>(t, r_y, r_xt, lr, lg);
   }
 }
 
@@ -692,6 +714,8 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   float* r_y = reinterpret_cast<float*>(smem + L::kQK);
   float* r_x = r_y + NTRI * 256;
   float* r_s = r_x + NTRI * 256;                                    // scratch tiles
+  // X's tiles (and the diagonal inverses over them) transposed in bf16 hi/lo parts
+  unsigned char* r_xt = reinterpret_cast<unsigned char*>(r_x);
   // once the solve is done, X and the scratch tiles hold v for the right-hand
   // side: wave w's 16 columns of every node, 32 bytes per node
   uint16_t* r_v = reinterpret_cast<uint16_t*>(r_x);
@@ -740,16 +764,17 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                              ((static_cast<size_t>(b) * N + t) * H + h) * kDk + gr * 8);
   }
   // v of this wave's columns, 16 bytes (8 columns of one node) per load:
-  // granule e = lane + 64 u is node e / 2, columns 16 w + 8 (e % 2) .. + 7
+  // granule e = lane + 64 u is node e / 2, columns 16 w + 8 (e % 2) .. + 7.
+  // Nodes past N read node N - 1 and are zeroed when v is parked: loads
+  // under a condition would be waited for at once (their registers join
+  // the zero default's), and v is to stay in flight through steps 2-4.
   constexpr int kVPer = (2 * NP + 63) / 64;
   uint4 vg[kVPer];
 #pragma unroll
   for (int u = 0; u < kVPer; ++u) {
-    const int e = lane + 64 * u, t = e >> 1;
-    vg[u] = make_uint4(0, 0, 0, 0);
-    if (t < N)
-      vg[u] = *reinterpret_cast<const uint4*>(v + ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * wave +
-                                              8 * (e & 1));
+    const int e = lane + 64 * u, t = min(e >> 1, N - 1);
+    vg[u] = *reinterpret_cast<const uint4*>(v + ((static_cast<size_t>(b) * N + t) * H + h) * kDk + 16 * wave +
+                                            8 * (e & 1));
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
@@ -869,9 +894,11 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             for (int ks = 0; ks < kDk / 32; ++ks)
               g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8_t, a[ks]),
                                                            __builtin_bit_cast(gbf16x8_t, bk[sl][ks]), g, 0, 0, 0);
-            // Y over ancestors-or-self, X over strict ancestors (times beta_t)
+            // Y over ancestors-or-self, X over strict ancestors (times beta_t);
+            // Y in fp32, X transposed in bf16 hi/lo parts (the operand form of
+            // the back-substitution)
             const int i = 16 * kt + lr;
-            float* dst = (part ? r_x : r_y) + ltri(rt, kt) * 256;
+            gf32x4_t val;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int t = t0 + r;
@@ -884,7 +911,14 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                                     __float_as_int(gt[r].w) - __float_as_int(gi[sl].w));
               ratio = __float_as_int(gt[r].z) != __float_as_int(gi[sl].z) ? 0.0f : ratio;
               ratio = i == t ? 1.0f : ratio;
-              dst[tix(4 * lg + r, lr)] = on ? bts[r] * ratio * g[r] : 0.0f;
+              val[r] = on ? bts[r] * ratio * g[r] : 0.0f;
+            }
+            if (part) {
+              at_write(r_xt + ltri(rt, kt) * 1024, lr, lg, val);
+            } else {
+              float* dst = r_y + ltri(rt, kt) * 256;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) dst[tix(4 * lg + r, lr)] = val[r];
             }
           }
         }
@@ -907,7 +941,9 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   }
   lds_barrier();
 
-  // ---- 3. inverse diagonal blocks, written over X's diagonal tiles
+  // ---- 3. inverse diagonal blocks, from X's diagonal tiles (hi + lo, in
+  // fp32 in the wave's two scratch tiles) and written back over them in the
+  // same transposed hi/lo form, the back-substitution's A operands
   {
     const int hmax = min(16, s_maxdepth);
     int J = 1;
@@ -915,12 +951,21 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     float* mb = r_s + wave * 512;  // this wave's two scratch tiles
     float* pb = mb + 256;
     for (int bb = wave; bb < NT; bb += kWaves) {
-      float* xb = r_x + ltri(bb, bb) * 256;
-      // M = I - X (the first factor), P = X X (the next power)
-      const gf32x4_t p = mm16(xb, xb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
-      gf32x4_t mm = tload(xb, lr, lg);
+      unsigned char* xt = r_xt + ltri(bb, bb) * 1024;
+      gs16x4_t xh, xl;
+      at_read(xt, lr, lg, xh, xl);
+      gf32x4_t xv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mm[r] = (4 * lg + r == lr ? 1.0f : 0.0f) - mm[r];
+      for (int r = 0; r < 4; ++r)
+        xv[r] = __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<uint16_t>(xh[r])) << 16) +
+                __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<uint16_t>(xl[r])) << 16);
+      tstore(mb, xv, lr, lg);
+      wave_lds_sync();
+      const gf32x4_t p = mm16(mb, mb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
+      gf32x4_t mm;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mm[r] = (4 * lg + r == lr ? 1.0f : 0.0f) - xv[r];
+      wave_lds_sync();
       tstore(mb, mm, lr, lg);
       tstore(pb, p, lr, lg);
       wave_lds_sync();
@@ -934,7 +979,7 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         if (j + 1 < J) tstore(pb, p2, lr, lg);
         wave_lds_sync();
       }
-      tstore(xb, tload(mb, lr, lg), lr, lg);
+      at_write(xt, lr, lg, tload(mb, lr, lg));
       wave_lds_sync();
     }
   }
@@ -950,7 +995,7 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // SIMD that the two waves share when waves are dealt to SIMDs in turn.
   {
     const int t = wave < 4 ? NT - 1 - wave : (wave - 4 < NT - 4 ? wave - 4 : -1);
-    gdn_row_solve_pick<NT>(t, r_y, r_x, lr, lg);
+    gdn_row_solve_pick<NT>(t, r_y, r_xt, lr, lg);
     lds_barrier();
   }
   // v into this wave's part of X and the scratch tiles (free since the
@@ -959,7 +1004,8 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
   for (int u = 0; u < kVPer; ++u) {
     const int e = lane + 64 * u;
-    if (e < 2 * NP) *reinterpret_cast<uint4*>(vw + (e >> 1) * 16 + 8 * (e & 1)) = vg[u];
+    if (e < 2 * NP)
+      *reinterpret_cast<uint4*>(vw + (e >> 1) * 16 + 8 * (e & 1)) = (e >> 1) < N ? vg[u] : make_uint4(0, 0, 0, 0);
   }
 
   // ---- 5. [Q; K] S0 for this wave's columns.  Node tile mt of Q: the product
