@@ -849,13 +849,15 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     if (lane == 0 && dm > 0) atomicMax(&s_maxdepth, dm);
   }
   lds_barrier();
-  // Waves 0-3 form Y's tiles, waves 4-7 X's.  Wave p of a part takes the
+  // Waves 0-3 form X's tiles, waves 4-7 Y's (X's cost more, the beta factor
+  // and the hi/lo stores, and of the two waves of a SIMD the older one runs
+  // first, so the pair ends closer together).  Wave p of a part takes the
   // block rows p and NT - 1 - p (NT + 1 tiles: balanced), so a row's A
   // operand (its bf16 q or k rows) and its mask operands are read once for
   // all of the row's tiles; the next tile's key rows are read before the
   // current tile's products.  The masks and gate ratios are selects.
   {
-    const int part = wave >> 2, p = wave & 3;
+    const int part = 1 - (wave >> 2), p = wave & 3;
 #pragma unroll
     for (int hr = 0; hr < 2; ++hr) {
       const int rt = hr == 0 ? p : NT - 1 - p;
