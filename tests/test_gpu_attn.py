@@ -189,6 +189,27 @@ def test_c2_full_size_all_outputs(lib):
     _unit_check(lib, x, 0, _all_units(x), "c2")
 
 
+def test_stream_shares_within_the_page_cache(lib):
+    """A global layer large enough that two stream workgroups per CU would
+    each take more key tiles (about 516 of 32 keys) than the page cache covers
+    (1024 pages of 16 keys): the plan grows the grid instead, so no segment
+    reads the block table per refill.  The workspace size query reveals the
+    grid; sampled units spread over the batch and both ends of the kv heads
+    are compared with the oracle (segment boundaries and merges included)."""
+    B, N, Hq, Hkv, D, ctx = 32, 16, 16, 8, 64, 33000
+    x = W.attn_inputs(3, B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, ctx_lo=ctx, ctx_hi=ctx, tree="spine_first",
+                      dtype=torch.bfloat16, device=DEV, kv_on_device=True)
+    rows = (Hq // Hkv) * N
+    units = B * Hkv
+    ws = lib.tree_verify_attn_workspace_size(B, N, Hq, Hkv, D, ctx, 0)
+    wg = ws // (rows * (D * 4 + 8)) - units + 1
+    tiles = units * ((ctx + 31) // 32 + (N + 31) // 32)
+    say(f"attn stream cap: {tiles} tiles over {wg} workgroups")
+    assert -(-tiles // wg) <= 512
+    sample = [(b, g) for b in (0, 7, 13, 20, 31) for g in (0, 3, 7)]
+    _unit_check(lib, x, 0, sample, "stream cap")
+
+
 def test_c4_full_size_all_outputs(lib):
     """The DDTree batch at full size: every output element, i.e. all 64 nodes
     x 8 query heads (both 256-row groups of the wide-tile kernel) of all 512

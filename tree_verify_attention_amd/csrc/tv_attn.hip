@@ -1893,8 +1893,19 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_ctx_len, int wi
     // a full grid of two workgroups per CU pairs workgroup w with w + CUs; the
     // pair and XCD weights were measured on 256 CUs in 8 XCDs and apply only
     // there (equal shares elsewhere)
-    const bool full = TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus() && device_cus() == 256 &&
-                      device_xcds() == 8;
+    bool full = TV_ATTN_STREAM_WG_PER_CU == 2 && wg == 2ll * device_cus() && device_cus() == 256 &&
+                device_xcds() == 8;
+    // a share spans at most the page cache's worth of key tiles (weighted
+    // shares run up to about 12% over the average), so every segment's page
+    // indices fit the cache: larger batches get more workgroups, with equal
+    // shares, rather than a block-table read per refill
+    const long long cap = static_cast<long long>(kMaxPages) * 16 / kTile;
+    const long long avg = (tiles + wg - 1) / wg;
+    if ((full ? avg * 115 / 100 + 1 : avg) > cap) {
+      wg = (tiles + cap - 1) / cap;
+      full = false;
+      p.stream_wg = static_cast<int>(wg);
+    }
     p.stream_pm = full ? TV_ATTN_PAIR_PM : 500;
     p.stream_xm = full ? TV_ATTN_XCD_PM : 1000;
     p.nsplit = 1;
