@@ -991,26 +991,18 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // of Y and on X, so each wave takes one block row (gdn_row_solve) and no
   // barrier is needed until the rows are done.  Inside a row the products are
   // right-looking and transposed, so that the updates of one step do not
-  // depend on one another, and a transpose between register index and lane
-  // group turns an accumulator into the next product's B operand without
-  // LDS.  Waves w and w + 4 take rows NT - 1 - w and w, which balances the
-  // SIMD that the two waves share when waves are dealt to SIMDs in turn.
+  // depend on one another, and an accumulator feeds the next product as its
+  // B operand straight from registers.  Waves w and w + 4 take rows
+  // NT - 1 - w and w, which balances the SIMD that the two waves share when
+  // waves are dealt to SIMDs in turn.
   {
     const int t = wave < 4 ? NT - 1 - wave : (wave - 4 < NT - 4 ? wave - 4 : -1);
     gdn_row_solve_pick<NT>(t, r_y, r_xt, lr, lg);
-    lds_barrier();
   }
-  // v into this wave's part of X and the scratch tiles (free since the
-  // barrier above); only this wave reads it back
-  uint16_t* vw = r_v + wave * NP * 16;
-#pragma unroll
-  for (int u = 0; u < kVPer; ++u) {
-    const int e = lane + 64 * u;
-    if (e < 2 * NP)
-      *reinterpret_cast<uint4*>(vw + (e >> 1) * 16 + 8 * (e & 1)) = (e >> 1) < N ? vg[u] : make_uint4(0, 0, 0, 0);
-  }
-
-  // ---- 5. [Q; K] S0 for this wave's columns.  Node tile mt of Q: the product
+  // ---- 5. [Q; K] S0 for this wave's columns, right after its block row (a
+  // wave whose row is short forms them while the longer row of the other
+  // wave on its SIMD is still running its chain of dependent products; they
+  // read only the q and k rows).  Node tile mt of Q: the product
   // S0^T Q^T leaves lane (lr, lg) node 16 mt + lr, columns 16 w + 4 lg + r.  Of
   // K: K S0 with A-row i of tile mt reading node 32 (mt / 2) + 8 (i / 4) +
   // 4 (mt % 2) + i % 4, which leaves lane (lr, lg) column `col` of nodes
@@ -1047,6 +1039,17 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
       ksa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, slo[ks], ksa[mt], 0, 0, 0);
       ksa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k8, shi[ks], ksa[mt], 0, 0, 0);
     }
+  }
+
+  lds_barrier();  // every block row of M is done, X is free
+  // v into this wave's part of X and the scratch tiles (free since the
+  // barrier above); only this wave reads it back
+  uint16_t* vw = r_v + wave * NP * 16;
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) {
+    const int e = lane + 64 * u;
+    if (e < 2 * NP)
+      *reinterpret_cast<uint4*>(vw + (e >> 1) * 16 + 8 * (e & 1)) = (e >> 1) < N ? vg[u] : make_uint4(0, 0, 0, 0);
   }
 
   // ---- 6. right-hand side RHS = beta (V - gamma K S0) in registers, split
