@@ -530,11 +530,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 //     Y in LDS in fp32, X transposed in bf16 hi and lo parts.  A wave forms
 //     the tiles of two block rows (one of Y's parts or X's), reading each
 //     row's operands once.
-//  3. Diagonal blocks D_b = (I + X_bb)^-1.  X_bb couples a node only to its
-//     strict ancestors inside the block, so X_bb^h = 0 for chains of at most h
-//     nodes and the inverse is the product of (I + (-X_bb)^(2^j)),
+//  3. Diagonal blocks D_b = (I + X_bb)^-1, formed by the wave that formed
+//     X_bb, right after its block row (no barrier).  X_bb couples a node only
+//     to its strict ancestors inside the block, so X_bb^h = 0 for chains of
+//     at most h nodes and the inverse is the product of (I + (-X_bb)^(2^j)),
 //     j < ceil(log2 h): at most four steps, each two 16 x 16 fp32 MFMA
-//     products in one wave; D_b goes over X_bb in X's hi/lo form.
+//     products; D_b goes where X_bb would, in X's hi/lo form.
 //  4. M = Y (I + X)^-1, one block row per wave (a row of M needs only its row
 //     of Y and X): M_ta = (Y_ta - sum_{a < c <= t} M_tc X_ca) D_a, each
 //     product three bf16 MFMAs on hi/lo parts (about 16 mantissa bits), the
@@ -856,6 +857,41 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
   // operand (its bf16 q or k rows) and its mask operands are read once for
   // all of the row's tiles; the next tile's key rows are read before the
   // current tile's products.  The masks and gate ratios are selects.
+  // (I + X_bb)^-1 of a diagonal block from X_bb in the accumulator layout
+  // (lane (lr, lg) holding rows 4 lg .. + 3 of column lr): X_bb couples a node
+  // only to its strict ancestors inside the block, so X_bb^h = 0 for chains
+  // of at most h nodes and the inverse is the product of (I + (-X_bb)^(2^j)),
+  // j < ceil(log2 h), at most four steps of two 16 x 16 fp32 MFMA products,
+  // through the wave's two scratch tiles
+  const int hmax = min(16, s_maxdepth);
+  int J = 1;
+  while ((1 << J) < hmax) ++J;
+  float* mb = r_s + wave * 512;
+  float* pb = mb + 256;
+  auto invert_diag = [&](gf32x4_t xv) __attribute__((always_inline)) {
+    tstore(mb, xv, lr, lg);
+    wave_lds_sync();
+    // M = I - X (the first factor), P = X X (the next power)
+    const gf32x4_t p = mm16(mb, mb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
+    gf32x4_t mm;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mm[r] = (4 * lg + r == lr ? 1.0f : 0.0f) - xv[r];
+    wave_lds_sync();
+    tstore(mb, mm, lr, lg);
+    tstore(pb, p, lr, lg);
+    wave_lds_sync();
+    for (int j = 1; j < J; ++j) {
+      // M <- M + M P, and P <- P P for the next step
+      const gf32x4_t m2 = mm16(mb, pb, tload(mb, lr, lg), lr, lg);
+      gf32x4_t p2 = p;
+      if (j + 1 < J) p2 = mm16(pb, pb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
+      wave_lds_sync();
+      tstore(mb, m2, lr, lg);
+      if (j + 1 < J) tstore(pb, p2, lr, lg);
+      wave_lds_sync();
+    }
+    return tload(mb, lr, lg);
+  };
   {
     const int part = 1 - (wave >> 2), p = wave & 3;
 #pragma unroll
@@ -886,6 +922,7 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
           gi[sl] = s_gp[16 * kt + lr];
         };
         read_col(0, 0);
+        gf32x4_t diag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt) {
           if (kt <= rt) {
@@ -916,7 +953,10 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
               val[r] = on ? bts[r] * ratio * g[r] : 0.0f;
             }
             if (part) {
-              at_write(r_xt + ltri(rt, kt) * 1024, lr, lg, val);
+              if (kt == rt)
+                diag = val;  // inverted below, after the row
+              else
+                at_write(r_xt + ltri(rt, kt) * 1024, lr, lg, val);
             } else {
               float* dst = r_y + ltri(rt, kt) * 256;
 #pragma unroll
@@ -924,6 +964,9 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
           }
         }
+        // X's diagonal tile becomes D_rt = (I + X_rt,rt)^-1, in the same
+        // transposed hi/lo form, right here: no other wave needs X_rt,rt
+        if (part) at_write(r_xt + ltri(rt, rt) * 1024, lr, lg, invert_diag(diag));
       }
     }
   }
@@ -940,50 +983,6 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
     for (int u = 0; u < kDk / 16; ++u)
       s0q[u] = *reinterpret_cast<const float4*>(s0 + (32 * (u >> 1) + 8 * lg + 4 * (u & 1) + (lr & 3)) * kDk);
-  }
-  lds_barrier();
-
-  // ---- 3. inverse diagonal blocks, from X's diagonal tiles (hi + lo, in
-  // fp32 in the wave's two scratch tiles) and written back over them in the
-  // same transposed hi/lo form, the back-substitution's A operands
-  {
-    const int hmax = min(16, s_maxdepth);
-    int J = 1;
-    while ((1 << J) < hmax) ++J;
-    float* mb = r_s + wave * 512;  // this wave's two scratch tiles
-    float* pb = mb + 256;
-    for (int bb = wave; bb < NT; bb += kWaves) {
-      unsigned char* xt = r_xt + ltri(bb, bb) * 1024;
-      gs16x4_t xh, xl;
-      at_read(xt, lr, lg, xh, xl);
-      gf32x4_t xv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        xv[r] = __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<uint16_t>(xh[r])) << 16) +
-                __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<uint16_t>(xl[r])) << 16);
-      tstore(mb, xv, lr, lg);
-      wave_lds_sync();
-      const gf32x4_t p = mm16(mb, mb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
-      gf32x4_t mm;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mm[r] = (4 * lg + r == lr ? 1.0f : 0.0f) - xv[r];
-      wave_lds_sync();
-      tstore(mb, mm, lr, lg);
-      tstore(pb, p, lr, lg);
-      wave_lds_sync();
-      for (int j = 1; j < J; ++j) {
-        // M <- M + M P, and P <- P P for the next step
-        const gf32x4_t m2 = mm16(mb, pb, tload(mb, lr, lg), lr, lg);
-        gf32x4_t p2 = p;
-        if (j + 1 < J) p2 = mm16(pb, pb, gf32x4_t{0.f, 0.f, 0.f, 0.f}, lr, lg);
-        wave_lds_sync();
-        tstore(mb, m2, lr, lg);
-        if (j + 1 < J) tstore(pb, p2, lr, lg);
-        wave_lds_sync();
-      }
-      at_write(xt, lr, lg, tload(mb, lr, lg));
-      wave_lds_sync();
-    }
   }
   lds_barrier();
 
