@@ -70,10 +70,12 @@ def test_trees(lib, dtype, tree, N):
 
 @pytest.mark.parametrize("N", [2, 15, 16, 17, 31, 33, 48, 49, 63])
 def test_chain_depths_per_node_tile(lib, N):
-    """bf16 chains over every padded node count of the N <= 64 kernel (16, 32,
-    48, 64) and depths just below, at and above a power of two: the gate
-    products along a path take ceil(log2 depth) doubling rounds and the solve
-    as many steps.  The state is large enough that its low bf16 part matters."""
+    """bf16 chains over the padded node counts of the dense kernel (16, 32)
+    and of the block-triangular kernel from 33 nodes (64), across the switch
+    between them, with depths just below, at and above a power of two: the
+    dense kernel's gate products take ceil(log2 depth) doubling rounds and
+    its solve as many steps.  The state is large enough that its low bf16
+    part matters."""
     x = W.gdn_inputs(52, B=2, N=N, H=3, Dk=128, Dv=128, tree="chain", dtype=torch.bfloat16,
                      device=DEV, s0_std=0.5)
     check(lib, x, f"chain of {N}")

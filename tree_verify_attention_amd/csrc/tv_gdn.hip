@@ -17,14 +17,25 @@
 // the state's columns over workgroups: S0 is still read once in total, while
 // the small node-by-node terms are formed again per column block.
 //
-// Three kernels.  bf16 inputs up to 64 nodes: one 8-wave workgroup per
+// Three kernels.  bf16 inputs up to 32 nodes: one 8-wave workgroup per
 // (sequence, head), the dense products on MFMA and the solve as a product of
-// matrix powers.  bf16 inputs past 64 nodes: workgroups of 64 state columns,
-// a blocked solve on MFMA.  fp32 inputs: every product as fp32 FMAs, the
+// matrix powers.  bf16 inputs past 32 nodes: one 8-wave workgroup per
+// (sequence, head) too, only the tiles on or below the block diagonal, and a
+// block-row solve on MFMA.  fp32 inputs: every product as fp32 FMAs, the
 // solve level by level over depth.
 #include <atomic>
 
 #include "tv_internal.h"
+
+// bf16 trees of at least this many nodes take the block-triangular kernel
+// (gdn_tri_kernel); smaller ones the dense one (gdn_head_kernel), which fits
+// two workgroups per CU up to 32 nodes.  Measured warm at H = 16: from 33
+// nodes on the block-triangular kernel is faster at B = 16 and B = 32 (at 56
+// nodes 13.9 against 20.0 us and 26.4 against 39.6 us); at 32 nodes and B = 32
+// the dense kernel is (15.0 against 20.9 us).
+#ifndef TV_GDN_TRI_FROM
+#define TV_GDN_TRI_FROM 33
+#endif
 
 namespace tv {
 
@@ -75,8 +86,8 @@ __device__ __forceinline__ int gswz(int row, int byte) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, N <= 64: the dense products on MFMA, one 8-wave workgroup per
-// (sequence, head).
+// bf16 inputs, N < TV_GDN_TRI_FROM (up to 64 supported): the dense products on
+// MFMA, one 8-wave workgroup per (sequence, head).
 //
 // K S0 and Q S0 are one product [Q; K] S0 whose S0 operand never passes
 // through LDS: each wave owns 16 state columns, loads them from HBM in 16-byte
@@ -515,9 +526,10 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(kM <=
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, 64 < N <= 128.  One 8-wave workgroup per (sequence, head), wave
-// w owning state columns 16 w .. 16 w + 15; the node count is padded to
-// NP = 16 NT, NT even (96 or 128 nodes).  The Gram products and the solve run
+// bf16 inputs, 32 < N <= 128 (see TV_GDN_TRI_FROM).  One 8-wave workgroup
+// per (sequence, head), wave w owning state columns 16 w .. 16 w + 15; the
+// node count is padded to NP = 16 NT, NT even (64, 96 or 128 nodes; 32 when
+// the threshold is lowered).  The Gram products and the solve run
 // once per head.
 //
 //  1. q and k rows (bf16, exact) into LDS; v of this wave's columns into
@@ -799,7 +811,8 @@ void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     int zeros = 0, ex = 0, dpt = 0;
     float mant = 1.0f;
     if (t < NP) {
-      uint32_t m = static_cast<uint32_t>(s_anc[t * W + (qd >> 1)] >> (32 * (qd & 1)));
+      // (a quarter past the node words holds no node)
+      uint32_t m = (qd >> 1) < W ? static_cast<uint32_t>(s_anc[t * W + (qd >> 1)] >> (32 * (qd & 1))) : 0u;
       dpt = __popc(m);
       while (m) {
         const float al = s_alpha[32 * qd + __ffs(m) - 1];
@@ -1363,6 +1376,8 @@ hipError_t launch_gdn_tri(const void* q, const void* k, const void* v, const flo
 #define TV_GDN_NT(X, NT) \
   case X: return launch_gdn_tri_nt<TO, NT>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
   switch ((N + 31) / 32) {  // node tiles in pairs: the output product takes 32 nodes per step
+    TV_GDN_NT(1, 2);
+    TV_GDN_NT(2, 4);
     TV_GDN_NT(3, 6);
     TV_GDN_NT(4, 8);
     default: return hipErrorInvalidValue;
@@ -1395,11 +1410,11 @@ hipError_t launch_gdn(const void* q, const void* k, const void* v, const float* 
   (void)Dk;
   (void)Dv;
   if (dtype == TV_BF16 && out_dtype == TV_BF16)
-    return N <= 64 ? launch_gdn_head<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
-                   : launch_gdn_tri<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    return N < TV_GDN_TRI_FROM ? launch_gdn_head<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+                               : launch_gdn_tri<uint16_t>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_BF16 && out_dtype == TV_F32)
-    return N <= 64 ? launch_gdn_head<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
-                   : launch_gdn_tri<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+    return N < TV_GDN_TRI_FROM ? launch_gdn_head<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream)
+                               : launch_gdn_tri<float>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   if (dtype == TV_F32 && out_dtype == TV_F32)
     return launch_gdn_f32(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
   return hipErrorInvalidValue;
