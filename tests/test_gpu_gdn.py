@@ -58,6 +58,16 @@ def test_step_batch_two_per_cu(lib):
     check(lib, x, "step batch")
 
 
+@pytest.mark.parametrize("tree,N", [("spine_first", 48), ("random_parent", 64)])
+def test_more_heads_than_cus_past_32_nodes(lib, tree, N):
+    """32 sequences x 16 heads = 512 workgroups at 33-64 nodes: the
+    block-triangular kernel then runs two workgroups per CU (its 128-register
+    build), a launch the smaller test grids do not reach."""
+    x = W.gdn_inputs(56, B=32, N=N, H=16, Dk=128, Dv=128, tree=tree, dtype=torch.bfloat16, device=DEV,
+                     s0_std=0.5)
+    check(lib, x, f"{tree} of {N}, 512 workgroups")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("tree,N", [("chain", 64), ("star", 17), ("random_parent", 64),
                                     ("random_parent", 1), ("leaf_sibling", 32), ("spine_first", 40),

@@ -713,8 +713,8 @@ __device__ __forceinline__ void gdn_row_solve_pick(int t, float* r_y, const unsi
   }
 }
 
-template <typename TO, int NT>
-__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename TO, int NT, int kOcc>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(kOcc)))
 void gdn_tri_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                     const uint16_t* __restrict__ v, const float* __restrict__ alpha,
                     const float* __restrict__ beta, const float* __restrict__ S0,
@@ -1319,19 +1319,36 @@ hipError_t max_lds_once(std::atomic<int>* done, const void* fn, int bytes) {
   return e;
 }
 
+template <typename TO, int NT, int kOcc>
+hipError_t launch_gdn_tri_occ(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
+                              int H, void* out, hipStream_t stream) {
+  constexpr int lds = GdnLds<NT>::kBytes;
+  static_assert(lds + 16 <= 160 * 1024, "LDS budget");
+  static_assert(kOcc == 2 || 2 * (lds + 16) <= 160 * 1024, "two workgroups per CU fit the LDS");
+  static std::atomic<int> lds_set[kMaxDevices];
+  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_tri_kernel<TO, NT, kOcc>), lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gdn_tri_kernel<TO, NT, kOcc>), dim3(static_cast<unsigned>(B) * H), dim3(kTThreads), lds,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), alpha, beta, S0, anc, N, H, static_cast<TO*>(out));
+  return hipGetLastError();
+}
+
+// Up to 64 padded nodes the kernel's LDS leaves room for two workgroups per
+// CU, and a register budget of 128 (four waves per SIMD, a few spilled
+// registers) lets them run together: faster once the grid has more
+// workgroups than CUs (B = 32, H = 16, 40 nodes: 22.0 against 25.0 us), slower
+// when every workgroup has a CU to itself (B = 16: 14.4 against 13.1 us).
 template <typename TO, int NT>
 hipError_t launch_gdn_tri_nt(const void* q, const void* k, const void* v, const float* alpha,
                              const float* beta, const float* S0, const uint64_t* anc, int B, int N,
                              int H, void* out, hipStream_t stream) {
-  constexpr int lds = GdnLds<NT>::kBytes;
-  static_assert(lds + 16 <= 160 * 1024, "LDS budget");
-  static std::atomic<int> lds_set[kMaxDevices];
-  const hipError_t attr = max_lds_once(lds_set, reinterpret_cast<const void*>(&gdn_tri_kernel<TO, NT>), lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gdn_tri_kernel<TO, NT>), dim3(static_cast<unsigned>(B) * H), dim3(kTThreads), lds,
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), alpha, beta, S0, anc, N, H, static_cast<TO*>(out));
-  return hipGetLastError();
+  if constexpr (NT <= 4) {
+    if (static_cast<long long>(B) * H > device_cus())
+      return launch_gdn_tri_occ<TO, NT, 4>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
+  }
+  return launch_gdn_tri_occ<TO, NT, 2>(q, k, v, alpha, beta, S0, anc, B, N, H, out, stream);
 }
 
 // A grid that fits the CUs one workgroup each asks for more LDS than half a
