@@ -208,11 +208,16 @@ __device__ __forceinline__ int2 tree_pos_range(const int32_t* pos_b, int N, int2
   const int tid = threadIdx.x;
   if (tid < 64) {
     int lo = 0x7fffffff, hi = -0x7fffffff;
+    // unconditional loads (node N - 1 past the tree), then selects: under a
+    // condition each load would be waited for in its own branch
+    int pv[TV_MAX_NODES / 64];
 #pragma unroll
-    for (int i = tid; i < TV_MAX_NODES; i += 64) {
-      const int v = i < N ? pos_b[i] : 0;
-      lo = i < N ? min(lo, v) : lo;
-      hi = i < N ? max(hi, v) : hi;
+    for (int j = 0; j < TV_MAX_NODES / 64; ++j) pv[j] = pos_b[max(min(tid + 64 * j, N - 1), 0)];
+#pragma unroll
+    for (int j = 0; j < TV_MAX_NODES / 64; ++j) {
+      const int i = tid + 64 * j;
+      lo = i < N ? min(lo, pv[j]) : lo;
+      hi = i < N ? max(hi, pv[j]) : hi;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -334,24 +339,40 @@ __device__ __forceinline__ RowIn<T, D> row_in(const T* __restrict__ q,
 }
 
 // page indices [p0, p0 + npages) of one sequence into s_pages (as far as it
-// reaches), clamped into the pool; all loads go out before the first store
+// reaches), clamped into the pool; all loads go out before the first store.
+// The loads are unconditional (lanes past the range read its last entry):
+// under a condition the compiler waits for each load inside its branch, one
+// memory round trip after another.
+template <int NT, int kPages>
+struct PageLoads {
+  static constexpr int kPer = kPages / NT;
+  static_assert(kPer * NT == kPages, "page cache layout");
+  int n;
+  int v[kPer];
+};
+template <int NT, int kPages>
+__device__ __forceinline__ PageLoads<NT, kPages> pages_issue(const int32_t* __restrict__ bt_b, int p0, int npages) {
+  PageLoads<NT, kPages> pl;
+  pl.n = min(npages, kPages);
+  // an empty range reads the row's first entry (p0 may lie past the row) and
+  // stores nothing
+  const int base = pl.n > 0 ? p0 : 0, last = max(pl.n - 1, 0);
+#pragma unroll
+  for (int k = 0; k < pl.kPer; ++k) pl.v[k] = bt_b[base + min(static_cast<int>(threadIdx.x) + k * NT, last)];
+  return pl;
+}
+template <int NT, int kPages>
+__device__ __forceinline__ void pages_store(int* s_pages, const PageLoads<NT, kPages>& pl, int num_blocks) {
+#pragma unroll
+  for (int k = 0; k < pl.kPer; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < pl.n) s_pages[i] = min(max(pl.v[k], 0), num_blocks - 1);
+  }
+}
 template <int NT, int kPages>
 __device__ __forceinline__ void fill_pages(int* s_pages, const int32_t* __restrict__ bt_b, int p0,
                                            int npages, int num_blocks) {
-  constexpr int kPer = kPages / NT;
-  static_assert(kPer * NT == kPages, "page cache layout");
-  const int n = min(npages, kPages);
-  int v[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = threadIdx.x + k * NT;
-    v[k] = i < n ? bt_b[p0 + i] : 0;
-  }
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i < n) s_pages[i] = min(max(v[k], 0), num_blocks - 1);
-  }
+  pages_store<NT, kPages>(s_pages, pages_issue<NT, kPages>(bt_b, p0, npages), num_blocks);
 }
 
 // One segment of the key stream of one (sequence, kv head, row group): the
@@ -1423,14 +1444,19 @@ __device__ __forceinline__ void stream_prefix(const int32_t* ctx_len, int max_ct
                                               int* s_pref, int* s_ctx = nullptr) {
   const int tid = threadIdx.x;
   const int ntn = (N + kTile - 1) / kTile;
-  // each thread owns up to 4 consecutive sequences
+  // each thread owns up to 4 consecutive sequences; the four context lengths
+  // are loaded unconditionally (the last sequence's past B), so they are in
+  // flight together rather than one round trip after another
+  int raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = ctx_len[min(tid * 4 + i, B - 1)];
   int own[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = tid * 4 + i;
     int tl = 0;
     if (b < B) {
-      const int ctx = min(max(ctx_len[b], 0), max_ctx);
+      const int ctx = min(max(raw[i], 0), max_ctx);
       if (s_ctx) s_ctx[b] = ctx;
       tl = (ctx + kTile - 1) / kTile + ntn;
     }
@@ -1580,12 +1606,14 @@ __global__ __launch_bounds__(kThreads, (stream_min_wg<T, D>())) void attn_stream
     __syncthreads();  // the previous segment is done with every LDS buffer
     const int32_t* pos_b = pos + static_cast<size_t>(b) * N;
     const int2 prng = make_int2(0, 0);  // position range: only windows use it
-    // the query rows and the page indices go out together
-    const RowIn<T, D> ri = row_in<T, D>(q, pos_b, anc, b, g, 0, N, Hq, G, rows);
+    // the page indices, then the query rows, go out together; the page
+    // stores wait only for the former
     const int32_t* bt_b = bt + static_cast<size_t>(b) * max_blocks;
     const int p0 = k0 >> 4;
     const int npages = k1 > k0 ? ((k1 - 1) >> 4) - p0 + 1 : 0;
-    fill_pages<kThreads, kMaxPages>(s_pages, bt_b, p0, npages, num_blocks);
+    const PageLoads<kThreads, kMaxPages> pl = pages_issue<kThreads, kMaxPages>(bt_b, p0, npages);
+    const RowIn<T, D> ri = row_in<T, D>(q, pos_b, anc, b, g, 0, N, Hq, G, rows);
+    pages_store<kThreads, kMaxPages>(s_pages, pl, num_blocks);
 
     attn_segment<T, TO, D, 1, kMaxPages>(ri, kn, vn, kc, vc, bt_b, num_blocks, anc, pos_b, N, Hq, Hkv, G, rows,
                            0, scale_log2, b, g, 0, k0, k1, n0, n1, prng,
