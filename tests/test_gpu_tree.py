@@ -44,6 +44,20 @@ def test_topk_ties(lib, dtype):
     _check_topk(lib, x.to(dtype).to(DEV), 16)
 
 
+@pytest.mark.parametrize("dtype,V,sigma,K", [
+    (torch.bfloat16, 3 * 16384 + 8 * 300, 1.0, 16),  # three whole passes, a ragged one, every element queued
+    (torch.bfloat16, 3 * 16384 + 8 * 300, 8.0, 8),
+    (torch.float32, 3 * 8192 + 4 * 77, 1.0, 5),
+    (torch.bfloat16, 3 * 16384 + 8 * 300 + 3, 1.0, 3),  # rows not 16-byte multiples: element by element
+])
+def test_topk_passes_and_queue_load(lib, dtype, V, sigma, K):
+    """Rows of several passes of 4 chunks a thread, a partial pass and a tail;
+    sigma 1 puts every element within the fp64 band, so each pass fills the
+    wave's queue to its bound."""
+    say(f"topk passes V={V} sigma={sigma} K={K} {dtype}")
+    _check_topk(lib, W.draft_logits(74, 2, 2, V, dtype, sigma=sigma, device=DEV), K)
+
+
 def test_topk_full_vocabulary(lib):
     """Rows of the DDTree workload's vocabulary (262144), bf16, sigma 8."""
     x = W.draft_logits(72, 2, 8, 262144, torch.bfloat16, device=DEV, on_device=True)

@@ -59,15 +59,18 @@ __device__ __forceinline__ float elem(const T* p, size_t i) {
 // s: all of them together weigh at most V e^-kBig of the row's sum (the row
 // maximum alone weighs 1), so the fp32 rounding there stays far below fp32's
 // resolution of the result.  The larger elements are queued in LDS, one value
-// per entry, and the wave sums their exp in fp64, 64 at a time (one per lane),
-// against a wave-uniform reference.  Each wave keeps one sorted list of its K
-// best (lane k < K holds entry k): an element is a candidate only if it beats
-// the list's last entry, which the whole wave knows, so after the first few
-// chunks a chunk costs a compare and a ballot per element; the rare candidates
-// enter one at a time by a lane-parallel insertion.  The waves' lists and sums
-// merge at the end.
+// per entry (the input's own bits), and once per pass the wave sums their exp
+// in fp64, 64 at a time (one per lane), against a wave-uniform reference; the
+// next pass's loads are in flight meanwhile.  Each wave keeps one sorted list
+// of its K best (lane k < K holds entry k): an element is a candidate only if
+// it beats the list's last entry, which the whole wave knows, so after the
+// first few chunks a chunk costs a compare and a ballot; candidates enter one
+// at a time by a lane-parallel insertion, element slot by element slot, and
+// after each insertion the ones still waiting are checked again against the
+// new last entry.  The waves'
+// lists and sums merge at the end.
 constexpr float kBig = 22.0f;  // natural-log distance below the running max summed in fp32
-constexpr int kQ = 1024;       // queued values per wave: a power of two >= 63 + 64 * 16
+constexpr int kU = 4;          // 16-byte chunks per thread and pass
 
 // order-preserving map of a float onto a signed int (for an LDS atomicMax)
 __device__ __forceinline__ int f2ord(float f) {
@@ -75,6 +78,25 @@ __device__ __forceinline__ int f2ord(float f) {
   return i >= 0 ? i : i ^ 0x7fffffff;
 }
 __device__ __forceinline__ float ord2f(int i) { return __int_as_float(i >= 0 ? i : i ^ 0x7fffffff); }
+
+// one DPP lane exchange of a 32-bit value (a lane whose source does not exist
+// keeps `old`)
+template <int kCtrl>
+__device__ __forceinline__ int dpp(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, kCtrl, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// the wave's maximum, in every lane: the rows of 16 lanes reduce by quad
+// exchanges and rotations, then the four row maxima are read out
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp<0xb1>(0, __float_as_int(v))));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(dpp<0x4e>(0, __float_as_int(v))));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(dpp<0x124>(0, __float_as_int(v))));  // row_ror 4
+  v = fmaxf(v, __int_as_float(dpp<0x128>(0, __float_as_int(v))));  // row_ror 8
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
 
 template <typename T>
 __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4))) void draft_topk_kernel(const T* __restrict__ logits,
@@ -84,9 +106,13 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr int nw = kTopkThreads / 64;
   constexpr int E = 16 / static_cast<int>(sizeof(T));  // elements per chunk
-  static_assert(kQ >= 63 + 64 * E && (kQ & (kQ - 1)) == 0, "queue capacity");
-  __shared__ float s_q[nw][kQ];  // queued large elements
-  __shared__ int s_rowmax;       // the workgroup's running max (order-preserving int)
+  // queue entries per wave: the input's bits (8 KB a wave); a pass pushes at
+  // most 64 * E * kU and at most 63 are left after a drain.  The 64 entries
+  // past the queue are where the lanes with nothing to queue write.
+  constexpr int kQ = 8192 / static_cast<int>(sizeof(T));
+  static_assert(kQ >= 63 + 64 * E * kU, "queue capacity");
+  __shared__ T s_q[nw][kQ + 64];  // queued large elements
+  __shared__ int s_rowmax;   // the workgroup's running max (order-preserving int)
   const size_t row = blockIdx.x;
   const T* p = logits + row * static_cast<size_t>(V);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -97,62 +123,81 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
   int wi = 0x7fffffff;
   float thr = -INFINITY;  // the list's entry K - 1 (wave-uniform)
   int thr_i = 0x7fffffff;
-  auto consider = [&](float v, int idx) __attribute__((always_inline)) {
-    uint64_t mask = __ballot(cand_before(v, idx, thr, thr_i));
-    while (mask != 0ull) {
-      const int src = __ffsll(static_cast<unsigned long long>(mask)) - 1;
-      mask &= mask - 1ull;
-      const float cv = __shfl(v, src, 64);
-      const int ci = __shfl(idx, src, 64);
-      if (!cand_before(cv, ci, thr, thr_i)) continue;  // the list moved on
-      // entries after the insertion point move down one lane
-      const uint64_t worse = __ballot(lane < K && cand_before(cv, ci, wv, wi));
-      const int pos = __ffsll(static_cast<unsigned long long>(worse)) - 1;
-      const float up_v = __shfl_up(wv, 1, 64);
-      const int up_i = __shfl_up(wi, 1, 64);
-      if (lane < K && lane >= pos) {
-        wv = lane == pos ? cv : up_v;
-        wi = lane == pos ? ci : up_i;
+  // offer the elements x[k] (index i0 + k) of the lanes with `ok` set to the
+  // wave list, element slot by element slot; every lane of the wave calls it
+  auto offer = [&](const float* x, int n, bool ok, int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+      uint64_t todo = __ballot(ok && x[k] >= thr);
+      while (todo != 0ull) {
+        const int src = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+        todo &= todo - 1ull;
+        const float cv = readlane_f(x[k], src);
+        const int ci = __builtin_amdgcn_readlane(i0, src) + k;
+        if (!cand_before(cv, ci, thr, thr_i)) continue;  // a tie with a lower index
+        // entries after the insertion point move down one lane (K <= 16: row 0)
+        const uint64_t worse = __ballot(lane < K && cand_before(cv, ci, wv, wi));
+        const int pos = __ffsll(static_cast<unsigned long long>(worse)) - 1;
+        const float up_v = __int_as_float(dpp<0x111>(__float_as_int(wv), __float_as_int(wv)));  // row_shr 1
+        const int up_i = dpp<0x111>(wi, wi);
+        if (lane < K && lane >= pos) {
+          wv = lane == pos ? cv : up_v;
+          wi = lane == pos ? ci : up_i;
+        }
+        thr = readlane_f(wv, K - 1);
+        thr_i = __builtin_amdgcn_readlane(wi, K - 1);
+        todo &= __ballot(ok && x[k] >= thr);
       }
-      thr = __shfl(wv, K - 1, 64);
-      thr_i = __shfl(wi, K - 1, 64);
     }
   };
   float m = -INFINITY, s = 0.0f;  // running max and fp32 sum of the small elements' exp(x - m)
-  float base = -INFINITY;         // the workgroup's max as last seen (wave-uniform)
+  float base = -INFINITY;         // the workgroup's max as last seen
   double S = 0.0;                 // fp64 sum of the queued elements' exp(x - R)
   float R = -INFINITY;            // its reference (wave-uniform)
-  int qhead = 0, qtail = 0;       // the wave's queue (wave-uniform)
+  int qtail = 0;                  // the wave's queue length (wave-uniform)
 
-  // queue the values of the lanes with `big` set (one ballot)
+  auto to_q = [](float x) -> T {
+    if constexpr (sizeof(T) == 2) return static_cast<T>(__float_as_uint(x) >> 16);
+    else return x;
+  };
+  auto from_q = [](T q) -> float {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(static_cast<uint32_t>(q) << 16);
+    else return q;
+  };
+  // queue the values of the lanes with `big` set (one ballot, no branch)
   auto push = [&](float x, bool big) __attribute__((always_inline)) {
     const uint64_t b = __ballot(big);
-    if (b != 0ull) {
-      const int slot = qtail + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                   static_cast<uint32_t>(b >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
-      if (big) s_q[wave][slot & (kQ - 1)] = x;
-      qtail += __popcll(b);
-    }
+    const int slot = qtail + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                 static_cast<uint32_t>(b >> 32),
+                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+    s_q[wave][big ? slot : kQ + lane] = to_q(x);
+    qtail += __popcll(b);
   };
-  // every full batch of 64 queued values: their exp in fp64, the reference
-  // moved up to the batch's maximum first
+  // every full batch of 64 queued values (every value, if `all`): their exp in
+  // fp64, the reference moved up to the batch's maximum first; the rest moves
+  // to the front of the queue
   auto drain = [&](bool all) __attribute__((always_inline)) {
-    if (qtail - qhead < (all ? 1 : 64)) return;
+    if (qtail < (all ? 1 : 64)) return;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's queue writes are in
+    int qhead = 0;
     while (qtail - qhead >= (all ? 1 : 64)) {
       const int n = min(64, qtail - qhead);
-      const float x = lane < n ? s_q[wave][(qhead + lane) & (kQ - 1)] : -INFINITY;
-      float bm = x;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off, 64));
+      const float q = from_q(s_q[wave][qhead + lane]);
+      const float x = lane < n ? q : -INFINITY;
+      const float bm = wave_max(x);
       if (bm > R) {
         if (R != -INFINITY) S *= exp(static_cast<double>(R) - static_cast<double>(bm));
         R = bm;
       }
-      if (lane < n) S += exp(static_cast<double>(x) - static_cast<double>(R));
+      S += exp(lane < n ? static_cast<double>(x) - static_cast<double>(R) : -INFINITY);
       qhead += n;
     }
+    const int left = qtail - qhead;
+    if (left > 0) {
+      const T v = s_q[wave][qhead + lane];  // read by the whole wave before any write
+      if (lane < left) s_q[wave][lane] = v;
+    }
+    qtail = left;
   };
 
   const bool vec = ((static_cast<size_t>(V) * sizeof(T)) % 16 == 0) &&
@@ -194,30 +239,27 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
     }
 #pragma unroll
     for (int k = 0; k < E; ++k) push(x[k], big[k]);
-    drain(false);
-    if (__ballot(valid && cm >= thr) != 0ull) {
-#pragma unroll
-      for (int k = 0; k < E; ++k) consider(valid ? x[k] : -INFINITY, valid ? c * E + k : 0x7fffffff);
-    }
+    if (__ballot(valid && cm >= thr) != 0ull) offer(x, E, valid, c * E);
   };
   // share the running max: publish the wave's, read the workgroup's
   auto share_max = [&]() __attribute__((always_inline)) {
-    float wm = m;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
+    const float wm = wave_max(m);
     if (lane == 0) atomicMax(&s_rowmax, f2ord(wm));
-    base = fmaxf(base, ord2f(__shfl(s_rowmax, 0, 64)));
+    base = fmaxf(base, ord2f(s_rowmax));
   };
-  // kU loads in flight per thread, then their chunks; the loop bounds are
-  // wave-uniform (cw = the wave's first chunk of a pass)
-  constexpr int kU = 8;
+  // passes of kU chunks per thread; the loop bounds are wave-uniform (cw =
+  // the wave's first chunk of a pass).  The next pass's loads are issued
+  // before this one is absorbed (from the same pass again where there is no
+  // next: in bounds, unused).
+  constexpr int kPass = kU * kTopkThreads;
   const u32x4_t* pc = reinterpret_cast<const u32x4_t*>(p);
+  auto full = [&](int c) { return c + 63 + (kU - 1) * kTopkThreads < nchunk; };
   int cw = wave * 64;
+  bool have = full(cw);
   {
     // the first pass: the maximum of its chunks is shared before any of them
     // is classified (the running max knows nothing yet); the barrier is
     // reached by every wave, with or without a first pass
-    const bool have = cw + 63 + (kU - 1) * kTopkThreads < nchunk;
     u32x4_t r[kU];
     float lm = -INFINITY;
     if (have) {
@@ -235,41 +277,44 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
         }
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lm = fmaxf(lm, __shfl_xor(lm, off, 64));
+    lm = wave_max(lm);
     if (lane == 0) atomicMax(&s_rowmax, f2ord(lm));
     __syncthreads();
     base = ord2f(s_rowmax);
-    if (have) {
+    while (have) {
+      const int cn = cw + kPass;
+      const bool more = full(cn);
+      const int cl = more ? cn : cw;
+      u32x4_t rn[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) rn[u] = __builtin_nontemporal_load(pc + cl + lane + u * kTopkThreads);
 #pragma unroll
       for (int u = 0; u < kU; ++u) absorb(r[u], cw + lane + u * kTopkThreads, true);
       share_max();
-      cw += kU * kTopkThreads;
+      drain(false);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) r[u] = rn[u];
+      cw = cn;
+      have = more;
     }
-  }
-  for (; cw + 63 + (kU - 1) * kTopkThreads < nchunk; cw += kU * kTopkThreads) {
-    u32x4_t r[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) r[u] = __builtin_nontemporal_load(pc + cw + lane + u * kTopkThreads);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) absorb(r[u], cw + lane + u * kTopkThreads, true);
-    share_max();
   }
   for (; cw < nchunk; cw += kTopkThreads) {
     const int c = cw + lane;
     const bool ok = c < nchunk;
-    const u32x4_t r = ok ? __builtin_nontemporal_load(pc + c) : u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t r = __builtin_nontemporal_load(pc + (ok ? c : 0));
     absorb(r, c, ok);
+    drain(false);
   }
   // elements past the last whole chunk (or every element without 16-byte
   // rows): all go to the queue; the loop runs while any lane of the wave has one
   for (int v0 = nchunk * E + (tid & ~63); v0 < V; v0 += kTopkThreads) {
     const int v = v0 + lane;
-    const float x = v < V ? elem(p, v) : -INFINITY;
+    const float xv = elem(p, v < V ? v : 0);
+    const float x = v < V ? xv : -INFINITY;
     m = fmaxf(m, x);
     push(x, v < V);
     drain(false);
-    consider(x, v < V ? v : 0x7fffffff);
+    offer(&x, 1, v < V, v);
   }
   drain(true);
 
