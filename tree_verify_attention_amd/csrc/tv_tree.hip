@@ -106,12 +106,18 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
   constexpr float kLog2e = 1.4426950408889634f;
   constexpr int nw = kTopkThreads / 64;
   constexpr int E = 16 / static_cast<int>(sizeof(T));  // elements per chunk
-  // queue entries per wave: the input's bits (8 KB a wave); a pass pushes at
-  // most 64 * E * kU and at most 63 are left after a drain.  The 64 entries
-  // past the queue are where the lanes with nothing to queue write.
-  constexpr int kQ = 8192 / static_cast<int>(sizeof(T));
-  static_assert(kQ >= 63 + 64 * E * kU, "queue capacity");
-  __shared__ T s_q[nw][kQ + 64];  // queued large elements
+  // Two queues per wave.  Chunks: a chunk with an element at or above its cut
+  // (the lane's cut when the chunk was absorbed) is queued whole, with that
+  // cut; a pass queues at most 64 * kU and a drain leaves at most 63.
+  // Elements: the queued chunks are split 64 at a time, their elements at or
+  // above the cut queued one per entry (the input's bits) and summed in fp64,
+  // 64 at a time.  The 64 entries past each queue are where the lanes with
+  // nothing to queue write.
+  constexpr int kCQ = 64 * kU + 63;
+  constexpr int kEQ = 64 * E + 63;
+  __shared__ u32x4_t s_qc[nw][kCQ + 64];  // queued chunks
+  __shared__ float s_qcut[nw][kCQ + 64];  // and their cuts
+  __shared__ T s_qe[nw][kEQ + 64];        // queued elements
   __shared__ int s_rowmax;   // the workgroup's running max (order-preserving int)
   const size_t row = blockIdx.x;
   const T* p = logits + row * static_cast<size_t>(V);
@@ -121,8 +127,11 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
 
   float wv = -INFINITY;  // this lane's entry of the wave list (lanes < K)
   int wi = 0x7fffffff;
-  float thr = -INFINITY;  // the list's entry K - 1 (wave-uniform)
+  float thr = -INFINITY;  // the list's entry K - 1, or the floor if that is lower (wave-uniform)
   int thr_i = 0x7fffffff;
+  // a value at least K elements of the wave reach (found in the first pass):
+  // nothing below it can enter the list
+  float floor_v = -INFINITY;
   // offer the elements x[k] (index i0 + k) of the lanes with `ok` set to the
   // wave list, element slot by element slot; every lane of the wave calls it
   auto offer = [&](const float* x, int n, bool ok, int i0) __attribute__((always_inline)) {
@@ -146,6 +155,10 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
         }
         thr = readlane_f(wv, K - 1);
         thr_i = __builtin_amdgcn_readlane(wi, K - 1);
+        if (thr < floor_v) {
+          thr = floor_v;
+          thr_i = 0x7fffffff;
+        }
         todo &= __ballot(ok && x[k] >= thr);
       }
     }
@@ -153,8 +166,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
   float m = -INFINITY, s = 0.0f;  // running max and fp32 sum of the small elements' exp(x - m)
   float base = -INFINITY;         // the workgroup's max as last seen
   double S = 0.0;                 // fp64 sum of the queued elements' exp(x - R)
-  float R = -INFINITY;            // its reference (wave-uniform)
-  int qtail = 0;                  // the wave's queue length (wave-uniform)
+  float R = -INFINITY;            // its reference (wave-uniform, never below a queued element)
+  int cq = 0, eq = 0;             // the wave's queue lengths (wave-uniform)
 
   auto to_q = [](float x) -> T {
     if constexpr (sizeof(T) == 2) return static_cast<T>(__float_as_uint(x) >> 16);
@@ -164,50 +177,7 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
     if constexpr (sizeof(T) == 2) return __uint_as_float(static_cast<uint32_t>(q) << 16);
     else return q;
   };
-  // queue the values of the lanes with `big` set (one ballot, no branch)
-  auto push = [&](float x, bool big) __attribute__((always_inline)) {
-    const uint64_t b = __ballot(big);
-    const int slot = qtail + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                 static_cast<uint32_t>(b >> 32),
-                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
-    s_q[wave][big ? slot : kQ + lane] = to_q(x);
-    qtail += __popcll(b);
-  };
-  // every full batch of 64 queued values (every value, if `all`): their exp in
-  // fp64, the reference moved up to the batch's maximum first; the rest moves
-  // to the front of the queue
-  auto drain = [&](bool all) __attribute__((always_inline)) {
-    if (qtail < (all ? 1 : 64)) return;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's queue writes are in
-    int qhead = 0;
-    while (qtail - qhead >= (all ? 1 : 64)) {
-      const int n = min(64, qtail - qhead);
-      const float q = from_q(s_q[wave][qhead + lane]);
-      const float x = lane < n ? q : -INFINITY;
-      const float bm = wave_max(x);
-      if (bm > R) {
-        if (R != -INFINITY) S *= exp(static_cast<double>(R) - static_cast<double>(bm));
-        R = bm;
-      }
-      S += exp(lane < n ? static_cast<double>(x) - static_cast<double>(R) : -INFINITY);
-      qhead += n;
-    }
-    const int left = qtail - qhead;
-    if (left > 0) {
-      const T v = s_q[wave][qhead + lane];  // read by the whole wave before any write
-      if (lane < left) s_q[wave][lane] = v;
-    }
-    qtail = left;
-  };
-
-  const bool vec = ((static_cast<size_t>(V) * sizeof(T)) % 16 == 0) &&
-                   ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
-  const int nchunk = vec ? V / E : 0;
-  // one chunk: the running max and sums absorb it, and its elements are
-  // offered to the wave list.  Called by the whole wave (the list lives in its
-  // first K lanes); a lane without a chunk offers nothing.
-  auto absorb = [&](const u32x4_t raw, int c, bool valid) __attribute__((always_inline)) {
-    float x[E];
+  auto unpack = [](const u32x4_t raw, float* x) __attribute__((always_inline)) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -218,27 +188,119 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
 #pragma unroll
       for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(raw[k]);
     }
+  };
+  // the lane's rank among the lanes of `b` (one ballot's lanes)
+  auto rank = [&](uint64_t b) __attribute__((always_inline)) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u)));
+  };
+  // queue the element of the lanes with `big` set (one ballot, no branch)
+  auto push_elem = [&](float x, bool big) __attribute__((always_inline)) {
+    const uint64_t b = __ballot(big);
+    s_qe[wave][big ? eq + rank(b) : kEQ + lane] = to_q(x);
+    eq += __popcll(b);
+  };
+  // queue the chunk of the lanes with `any` set, with its cut
+  auto push_chunk = [&](const u32x4_t raw, float cut, bool any) __attribute__((always_inline)) {
+    const uint64_t b = __ballot(any);
+    const int a = any ? cq + rank(b) : kCQ + lane;
+    s_qc[wave][a] = raw;
+    s_qcut[wave][a] = cut;
+    cq += __popcll(b);
+  };
+  // every full batch of 64 queued elements (every element, if `all`): their
+  // exp in fp64 against R, two batches at a time where there are two (two
+  // independent chains); the rest moves to the front of the queue.  R is
+  // first raised to the wave's running max, which bounds every queued element
+  // (each is at most the running max of the lane that absorbed it).
+  auto sum_elems = [&](bool all) __attribute__((always_inline)) {
+    if (eq < (all ? 1 : 64)) return;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's queue writes are in
+    const float wm = readlane_f(wave_max(m), 0);
+    if (wm > R) {
+      if (R != -INFINITY) S *= exp(static_cast<double>(R) - static_cast<double>(wm));
+      R = wm;
+    }
+    const double Rd = static_cast<double>(R);
+    int h = 0;
+    for (; eq - h >= 128; h += 128) {
+      const float x0 = from_q(s_qe[wave][h + lane]);
+      const float x1 = from_q(s_qe[wave][h + 64 + lane]);
+      S += exp(static_cast<double>(x0) - Rd) + exp(static_cast<double>(x1) - Rd);
+    }
+    while (eq - h >= (all ? 1 : 64)) {
+      const int n = min(64, eq - h);
+      const float q = from_q(s_qe[wave][h + lane]);
+      S += exp(lane < n ? static_cast<double>(q) - Rd : -INFINITY);
+      h += n;
+    }
+    const int left = eq - h;
+    if (left > 0) {
+      const T v = s_qe[wave][h + lane];  // read by the whole wave before any write
+      if (lane < left) s_qe[wave][lane] = v;
+    }
+    eq = left;
+  };
+  // every full batch of 64 queued chunks (every chunk, if `all`): their
+  // elements at or above the cut go to the element queue, which is summed
+  // after each batch; the rest moves to the front of the queue
+  auto drain = [&](bool all) __attribute__((always_inline)) {
+    if (cq >= (all ? 1 : 64)) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's queue writes are in
+      int h = 0;
+      while (cq - h >= (all ? 1 : 64)) {
+        const int n = min(64, cq - h);
+        const u32x4_t raw = s_qc[wave][h + lane];
+        const float cut = s_qcut[wave][h + lane];
+        float x[E];
+        unpack(raw, x);
+#pragma unroll
+        for (int k = 0; k < E; ++k) push_elem(x[k], lane < n && !(x[k] < cut));
+        sum_elems(false);
+        h += n;
+      }
+      const int left = cq - h;
+      if (left > 0) {
+        const u32x4_t raw = s_qc[wave][h + lane];  // read by the whole wave before any write
+        const float cut = s_qcut[wave][h + lane];
+        if (lane < left) {
+          s_qc[wave][lane] = raw;
+          s_qcut[wave][lane] = cut;
+        }
+      }
+      cq = left;
+    }
+    if (all) sum_elems(true);
+  };
+
+  const bool vec = ((static_cast<size_t>(V) * sizeof(T)) % 16 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  const int nchunk = vec ? V / E : 0;
+  // one chunk: the running max and sums absorb it, and its elements are
+  // offered to the wave list.  Called by the whole wave (the list lives in its
+  // first K lanes); a lane without a chunk offers nothing.
+  auto absorb = [&](const u32x4_t raw, int c, bool valid) __attribute__((always_inline)) {
+    float x[E];
+    unpack(raw, x);
     float cm = x[0];
 #pragma unroll
     for (int k = 1; k < E; ++k) cm = fmaxf(cm, x[k]);
-    bool big[E];
+    bool any = false;
+    float cut = 0.0f;
     if (valid) {
       const float nm = fmaxf(m, cm);
-      const float cut = fmaxf(nm, base) - kBig;
+      cut = fmaxf(nm, base) - kBig;
       float add = 0.0f;
 #pragma unroll
       for (int k = 0; k < E; ++k) {
-        big[k] = !(x[k] < cut);
-        if (!big[k]) add += __builtin_amdgcn_exp2f((x[k] - nm) * kLog2e);
+        const bool big = !(x[k] < cut);
+        any = any || big;
+        if (!big) add += __builtin_amdgcn_exp2f((x[k] - nm) * kLog2e);
       }
       s = (m == -INFINITY ? 0.0f : s * __builtin_amdgcn_exp2f((m - nm) * kLog2e)) + add;
       m = nm;
-    } else {
-#pragma unroll
-      for (int k = 0; k < E; ++k) big[k] = false;
     }
-#pragma unroll
-    for (int k = 0; k < E; ++k) push(x[k], big[k]);
+    push_chunk(raw, cut, any);
     if (__ballot(valid && cm >= thr) != 0ull) offer(x, E, valid, c * E);
   };
   // share the running max: publish the wave's, read the workgroup's
@@ -277,6 +339,17 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
         }
       }
     }
+    if (have) {
+      // the floor: the K-th largest lane maximum of this pass (one lane
+      // leaves per round, so equal maxima count separately)
+      float t = lm;
+      for (int j = 0; j < K; ++j) {
+        floor_v = readlane_f(wave_max(t), 0);
+        const uint64_t hb = __ballot(t == floor_v);
+        if (lane == __ffsll(static_cast<unsigned long long>(hb)) - 1) t = -INFINITY;
+      }
+      thr = floor_v;
+    }
     lm = wave_max(lm);
     if (lane == 0) atomicMax(&s_rowmax, f2ord(lm));
     __syncthreads();
@@ -312,8 +385,8 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
     const float xv = elem(p, v < V ? v : 0);
     const float x = v < V ? xv : -INFINITY;
     m = fmaxf(m, x);
-    push(x, v < V);
-    drain(false);
+    push_elem(x, v < V);
+    sum_elems(false);
     offer(&x, 1, v < V, v);
   }
   drain(true);
