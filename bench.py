@@ -74,6 +74,9 @@ def parse():
                     help="instead of the verify step, time tree_verify_attn alone on the full-size "
                          "shapes of this attention workload (2: batch 8 leaf-sibling trees, "
                          "4: DDTree-shaped batch 64) and print one JSON line for that kernel")
+    ap.add_argument("--tree-only", action="store_true",
+                    help="time only draft-tree construction (top-k and growth) at the DDTree shape, "
+                         "--steps calls each, and print one JSON line")
     ap.add_argument("--gdn-only", type=int, default=0,
                     help="instead of the verify step, time tree_gdn_verify alone on the verify-cost "
                          "curve's GDN shape (B=32, H=16, Dk=Dv=128, bf16, spine-first trees) with this "
@@ -754,6 +757,31 @@ def gdn_only(args, dev) -> dict:
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def copy_probe(mib: int, dev) -> int:
+    """Three plain device copies of `mib` MiB: the reference for scaling the
+    HBM byte counters of a profiled run.  Returns the bytes per copy."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
+
+
+def tree_only(args, dev) -> dict:
+    """Draft-tree construction alone (tree_draft_topk, then tree_build with
+    w = 1 and 8), on the DDTree workload's shape, inputs resident in HBM."""
+    import types
+    import tree_verify_attention_amd as tv
+    tv.load()
+    out = {"tree_only": True, **tree_construction(types.SimpleNamespace(tv=tv), dev, args.steps)}
+    if args.copy_probe_mib > 0:
+        out["copy_probe_bytes"] = copy_probe(args.copy_probe_mib, dev)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -769,6 +797,9 @@ def main():
         return
     if args.gdn_only:
         print(json.dumps(gdn_only(args, dev)), flush=True)
+        return
+    if args.tree_only:
+        print(json.dumps(tree_only(args, dev)), flush=True)
         return
     if args.config:
         step = Step(dev) if args.config == 3 else None
@@ -855,14 +886,7 @@ def main():
         out["next_rows"]["cost_curve"] = cost_curve(step, dev, min(args.steps, 20))
         out["next_rows"]["tree_construction"] = tree_construction(step, dev, min(args.steps, 20))
     if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_probe_bytes"] = n
+        out["copy_probe_bytes"] = copy_probe(args.copy_probe_mib, dev)
     if not args.no_cpu_baseline:
         log("oracle on the host")
         out["cpu_baseline"] = cpu_baseline(step, args.cpu_sample_seqs, args.cpu_1t_seqs)
