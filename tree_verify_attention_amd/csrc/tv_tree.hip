@@ -25,8 +25,9 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKMax = TV_TREE_MAX_TOPK;  // per-thread candidate list length
 
 // order of the top-k selection: larger value first, then lower index
+// (bitwise operators: straight-line compares, no short-circuit branches)
 __device__ __forceinline__ bool cand_before(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+  return (av > bv) | ((av == bv) & (ai < bi));
 }
 
 // the wave's best (value, index) pair and the lane that holds it
@@ -464,9 +465,6 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(4)
   }
 }
 
-// Pool of queued candidates (slot = push counter) and popped nodes, in LDS.
-constexpr int kPoolMax = TV_TREE_MAX_TOPK + 2 * TV_MAX_NODES;
-
 __device__ __forceinline__ int meta_pack(int depth, int rank, int parent) {
   return ((parent + 1) << 10) | (depth << 5) | rank;
 }
@@ -474,16 +472,23 @@ __device__ __forceinline__ int meta_depth(int m) { return (m >> 5) & 31; }
 __device__ __forceinline__ int meta_rank(int m) { return m & 31; }
 __device__ __forceinline__ int meta_parent(int m) { return (m >> 10) - 1; }
 
-// One wave per sequence.  The queue is kept sorted in LDS (best score first,
-// equal scores by lower slot; a slot is the push counter), so a round is a few
-// lane-parallel steps whatever w is:
+// One wave per sequence.  The queue lives in registers, sorted (best score
+// first, equal scores by lower slot; a slot is the push counter): entry
+// e = 64 r + lane is held by `lane` in register r, with its slot, its
+// (depth, rank, parent) and its parent's score.  Only the best N - n entries
+// are kept (n = nodes popped so far): insertions only push an entry down, so
+// one ranked N - n or lower is never popped.  A round is a few lane-parallel
+// steps whatever w is:
 //  1. the round's min(w, budget left, queued) candidates are the queue's
 //     first entries, in pop order;
 //  2. each popped node's successors, its next sibling (depth >= 2) and its
-//     first child (below the maximum depth), get slots in pop order;
+//     first child (below the maximum depth), get slots in pop order (a prefix
+//     count over the popped entries);
 //  3. the rest of the queue and the new candidates merge: an entry's place is
 //     its place in its own group plus the number of entries of the other group
-//     that sort before it.
+//     that sort before it.  The candidates are visited one at a time (their
+//     values read out of their lanes), each compared with every queued entry
+//     at once; the merged queue is scattered through LDS and read back.
 // The popped nodes are then flattened by depth (stable) and their parents
 // renumbered.
 __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restrict__ cand_tok,
@@ -494,14 +499,14 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ depth,
                                                         float* __restrict__ score,
                                                         int32_t* __restrict__ num_nodes) {
-  __shared__ float q_score[2][kPoolMax];  // sorted queue (two buffers): score
-  __shared__ int q_slot[2][kPoolMax];     // and slot
-  __shared__ int p_meta[kPoolMax];        // per slot: depth, rank, parent
-  __shared__ float c_score[2 * TV_MAX_NODES];  // a round's new candidates, in push order
-  __shared__ int c_slot[2 * TV_MAX_NODES];
-  __shared__ float n_score[TV_MAX_NODES];
-  __shared__ int n_meta[TV_MAX_NODES];
+  static_assert(TV_MAX_NODES <= 128, "two queue entries per lane");
   __shared__ float s_lp[TV_TREE_MAX_DEPTH * TV_TREE_MAX_TOPK];
+  __shared__ float n_score[TV_MAX_NODES];  // popped nodes, in pop order
+  __shared__ int n_meta[TV_MAX_NODES];
+  __shared__ float x_score[TV_MAX_NODES];  // the merged queue, scattered by place
+  __shared__ int x_slot[TV_MAX_NODES];
+  __shared__ int x_meta[TV_MAX_NODES];
+  __shared__ float x_ps[TV_MAX_NODES];
   __shared__ int s_new[TV_MAX_NODES];
   const int b = blockIdx.x, lane = threadIdx.x;
   const float* lp_b = cand_lp + static_cast<size_t>(b) * L * K;
@@ -509,96 +514,172 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restric
   __syncthreads();
   // the roots: the K depth-1 candidates in rank order (slots 0 .. K - 1), whose
   // log-probabilities decrease: they are the sorted queue (ties keep rank order)
-  for (int r = lane; r < K; r += 64) {
-    q_score[0][r] = s_lp[r];
-    q_slot[0][r] = r;
-    p_meta[r] = meta_pack(1, r, -1);
+  int queued = min(K, N);
+  float qs[2], qp[2];
+  int qsl[2], qm[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = 64 * r + lane;
+    const float v = s_lp[min(e, L * K - 1)];
+    qs[r] = e < queued ? v : -INFINITY;
+    qsl[r] = e;
+    qm[r] = meta_pack(1, e < K ? e : 0, -1);
+    qp[r] = 0.0f;
   }
-  int cur = 0;      // buffer holding the queue
-  int queued = K;   // its length
-  int pushed = K;   // slots used
-  int n = 0;        // popped nodes
-  __syncthreads();
+  int pushed = K;  // slots used
+  int n = 0;       // popped nodes
   while (n < N && queued > 0) {
     const int take = min(min(w, N - n), queued);
-    // 1. pop the first `take` entries
-    for (int t = lane; t < take; t += 64) {
-      const int sl = q_slot[cur][t];
-      n_score[n + t] = q_score[cur][t];
-      n_meta[n + t] = p_meta[sl];
-    }
-    __syncthreads();
-    // 2. successors in pop order: a prefix count over the popped nodes
-    int base = 0;
-    for (int t0 = 0; t0 < take; t0 += 64) {
-      const int t = t0 + lane;
-      int d = 0, r = 0, par = -1;
-      bool sib = false, child = false;
-      if (t < take) {
-        const int m = n_meta[n + t];
-        d = meta_depth(m);
-        r = meta_rank(m);
-        par = meta_parent(m);
-        sib = d >= 2 && r + 1 < K;
-        child = d < L;
-      }
-      const int cnt = static_cast<int>(sib) + static_cast<int>(child);
-      // exclusive prefix sum of cnt over the lanes (two ballots)
-      const uint64_t b1 = __ballot(cnt >= 1), b2 = __ballot(cnt >= 2);
-      const uint32_t lo1 = static_cast<uint32_t>(b1), hi1 = static_cast<uint32_t>(b1 >> 32);
-      const uint32_t lo2 = static_cast<uint32_t>(b2), hi2 = static_cast<uint32_t>(b2 >> 32);
-      const int before = static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi1, __builtin_amdgcn_mbcnt_lo(lo1, 0u)) +
-                                          __builtin_amdgcn_mbcnt_hi(hi2, __builtin_amdgcn_mbcnt_lo(lo2, 0u)));
-      int c = base + before;
-      if (sib) {
-        c_score[c] = n_score[par] + s_lp[(d - 1) * K + r + 1];
-        c_slot[c] = pushed + c;
-        p_meta[pushed + c] = meta_pack(d, r + 1, par);
-        ++c;
-      }
-      if (child) {
-        c_score[c] = n_score[n + t] + s_lp[d * K];
-        c_slot[c] = pushed + c;
-        p_meta[pushed + c] = meta_pack(d + 1, 0, n + t);
-      }
-      base += __popcll(b1) + __popcll(b2);
-    }
-    __syncthreads();
-    // 3. merge the rest of the queue (entries take .. queued - 1) with the new
-    // candidates into the other buffer
-    const int rest = queued - take, nc = base;
-    const int nxt = cur ^ 1;
-    for (int e = lane; e < rest; e += 64) {
-      const float v = q_score[cur][take + e];
-      const int sl = q_slot[cur][take + e];
-      int pos = e;
-      for (int j = 0; j < nc; ++j) pos += cand_before(c_score[j], c_slot[j], v, sl);
-      q_score[nxt][pos] = v;
-      q_slot[nxt][pos] = sl;
-    }
-    // a new candidate's place: the entries of either group before it, counted
-    // across the lanes (one ballot per 64 entries)
-    for (int j = 0; j < nc; ++j) {
-      const float v = c_score[j];
-      const int sl = c_slot[j];
-      int pos = 0;
-      for (int e0 = 0; e0 < rest; e0 += 64) {
-        const int e = e0 + lane;
-        pos += __popcll(__ballot(e < rest && cand_before(q_score[cur][take + e], q_slot[cur][take + e], v, sl)));
-      }
-      for (int i0 = 0; i0 < nc; i0 += 64) {
-        const int i2 = i0 + lane;
-        pos += __popcll(__ballot(i2 < nc && cand_before(c_score[i2], c_slot[i2], v, sl)));
-      }
+    const int cap = N - n - take;  // entries worth keeping after this round
+    int nc;
+    if (take == 1) {
+      // one pop (entry 0) and at most two candidates, all wave-uniform: every
+      // comparison in one straight-line block
+      const float ps = readlane_f(qs[0], 0), pp = readlane_f(qp[0], 0);
+      const int pm = __builtin_amdgcn_readlane(qm[0], 0);
       if (lane == 0) {
-        q_score[nxt][pos] = v;
-        q_slot[nxt][pos] = sl;
+        n_score[n] = ps;
+        n_meta[n] = pm;
+      }
+      const int d = meta_depth(pm), rk = meta_rank(pm), par = meta_parent(pm);
+      const bool sib = (d >= 2) & (rk + 1 < K), child = d < L;
+      const float s_sib = pp + s_lp[min(max((d - 1) * K + rk + 1, 0), L * K - 1)];
+      const float s_child = ps + s_lp[min(d * K, L * K - 1)];
+      const int sl_sib = pushed, sl_child = pushed + static_cast<int>(sib);
+      int pos_sib = static_cast<int>(child & cand_before(s_child, sl_child, s_sib, sl_sib));
+      int pos_child = static_cast<int>(sib & cand_before(s_sib, sl_sib, s_child, sl_child));
+      bool rest[2];
+      int below[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e = 64 * r + lane;
+        rest[r] = (e >= 1) & (e < queued);
+        below[r] = e - 1 + static_cast<int>(sib & cand_before(s_sib, sl_sib, qs[r], qsl[r])) +
+                   static_cast<int>(child & cand_before(s_child, sl_child, qs[r], qsl[r]));
+        pos_sib += __popcll(__ballot(rest[r] & cand_before(qs[r], qsl[r], s_sib, sl_sib)));
+        pos_child += __popcll(__ballot(rest[r] & cand_before(qs[r], qsl[r], s_child, sl_child)));
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (rest[r] & (below[r] < cap)) {
+          x_score[below[r]] = qs[r];
+          x_slot[below[r]] = qsl[r];
+          x_meta[below[r]] = qm[r];
+          x_ps[below[r]] = qp[r];
+        }
+      }
+      // lane 0 places the sibling, lane 1 the child
+      const bool mine = lane == 0 ? sib & (pos_sib < cap) : (lane == 1) & child & (pos_child < cap);
+      if (mine) {
+        const int at = lane == 0 ? pos_sib : pos_child;
+        x_score[at] = lane == 0 ? s_sib : s_child;
+        x_slot[at] = lane == 0 ? sl_sib : sl_child;
+        x_meta[at] = lane == 0 ? meta_pack(d, rk + 1, par) : meta_pack(d + 1, 0, n);
+        x_ps[at] = lane == 0 ? pp : ps;
+      }
+      nc = static_cast<int>(sib) + static_cast<int>(child);
+    } else {
+      // 1, 2. pop entries 0 .. take - 1; their successors, candidate v = 2 r
+      // (sibling) or 2 r + 1 (child) of the lane's entry in register r
+      float cs[4], cp[4];
+      int cm[4], csl[4];
+      bool cv[4];
+      int base = 0;
+  #pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e = 64 * r + lane;
+        const bool pop = e < take;
+        if (pop) {
+          n_score[n + e] = qs[r];
+          n_meta[n + e] = qm[r];
+        }
+        const int d = meta_depth(qm[r]), rk = meta_rank(qm[r]), par = meta_parent(qm[r]);
+        const float lp_sib = s_lp[min(max((d - 1) * K + rk + 1, 0), L * K - 1)];
+        const float lp_child = s_lp[min(d * K, L * K - 1)];
+        cv[2 * r] = pop && d >= 2 && rk + 1 < K;
+        cv[2 * r + 1] = pop && d < L;
+        cs[2 * r] = qp[r] + lp_sib;
+        cm[2 * r] = meta_pack(d, rk + 1, par);
+        cp[2 * r] = qp[r];
+        cs[2 * r + 1] = qs[r] + lp_child;
+        cm[2 * r + 1] = meta_pack(d + 1, 0, n + e);
+        cp[2 * r + 1] = qs[r];
+        // slots in pop order, the sibling first: an exclusive prefix count of
+        // the successors over the lanes (two ballots)
+        const int cnt = static_cast<int>(cv[2 * r]) + static_cast<int>(cv[2 * r + 1]);
+        const uint64_t b1 = __ballot(cnt >= 1), b2 = __ballot(cnt >= 2);
+        const int before =
+            static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b1 >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b1), 0u)) +
+                             __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b2 >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b2), 0u)));
+        csl[2 * r] = pushed + base + before;
+        csl[2 * r + 1] = pushed + base + before + static_cast<int>(cv[2 * r]);
+        base += __popcll(b1) + __popcll(b2);
+      }
+      nc = base;
+      // 3. merge.  A queued entry e >= take keeps its order among the rest and
+      // moves down by the candidates that sort before it.
+      bool rest[2];
+      int below[2];
+  #pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e = 64 * r + lane;
+        rest[r] = e >= take && e < queued;
+        below[r] = e - take;
+      }
+  #pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint64_t todo = __ballot(cv[v]);
+        while (todo != 0ull) {
+          const int src = __ffsll(static_cast<unsigned long long>(todo)) - 1;
+          todo &= todo - 1ull;
+          const float c_s = readlane_f(cs[v], src);
+          const int c_sl = __builtin_amdgcn_readlane(csl[v], src);
+          // its place: the rest and the candidates that sort before it
+          int pos = 0;
+  #pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            pos += __popcll(__ballot(rest[r] & cand_before(qs[r], qsl[r], c_s, c_sl)));
+            below[r] += static_cast<int>(rest[r] & cand_before(c_s, c_sl, qs[r], qsl[r]));
+          }
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) pos += __popcll(__ballot(cv[u] & cand_before(cs[u], csl[u], c_s, c_sl)));
+          if ((lane == src) & (pos < cap)) {
+            x_score[pos] = cs[v];
+            x_slot[pos] = csl[v];
+            x_meta[pos] = cm[v];
+            x_ps[pos] = cp[v];
+          }
+        }
+      }
+  #pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (rest[r] && below[r] < cap) {
+          x_score[below[r]] = qs[r];
+          x_slot[below[r]] = qsl[r];
+          x_meta[below[r]] = qm[r];
+          x_ps[below[r]] = qp[r];
+        }
       }
     }
-    cur = nxt;
-    queued = rest + nc;
+    queued = min(queued - take + nc, cap);
     pushed += nc;
     n += take;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = 64 * r + lane;
+      const int i = min(e, TV_MAX_NODES - 1);
+      const float v = x_score[i];
+      const int sl = x_slot[i], m = x_meta[i];
+      const float ps = x_ps[i];
+      const bool ok = e < queued;
+      qs[r] = ok ? v : -INFINITY;
+      qsl[r] = ok ? sl : 0x7fffffff;
+      qm[r] = ok ? m : meta_pack(1, 0, -1);
+      qp[r] = ok ? ps : 0.0f;
+    }
     __syncthreads();
   }
 
