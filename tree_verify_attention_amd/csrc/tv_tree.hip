@@ -596,8 +596,8 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restric
         const int d = meta_depth(qm[r]), rk = meta_rank(qm[r]), par = meta_parent(qm[r]);
         const float lp_sib = s_lp[min(max((d - 1) * K + rk + 1, 0), L * K - 1)];
         const float lp_child = s_lp[min(d * K, L * K - 1)];
-        cv[2 * r] = pop && d >= 2 && rk + 1 < K;
-        cv[2 * r + 1] = pop && d < L;
+        cv[2 * r] = pop & (d >= 2) & (rk + 1 < K);
+        cv[2 * r + 1] = pop & (d < L);
         cs[2 * r] = qp[r] + lp_sib;
         cm[2 * r] = meta_pack(d, rk + 1, par);
         cp[2 * r] = qp[r];
@@ -618,44 +618,53 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const int32_t* __restric
         base += __popcll(b1) + __popcll(b2);
       }
       nc = base;
-      // 3. merge.  A queued entry e >= take keeps its order among the rest and
-      // moves down by the candidates that sort before it.
+      // 3. merge, lane-parallel: each lane ranks its own queued entries and
+      // candidates against the other group, whose members are read out one
+      // at a time.  A queued entry e >= take keeps its order among the rest
+      // and moves down by the candidates that sort before it; a candidate's
+      // place is the queued entries and the candidates before it.
       bool rest[2];
       int below[2];
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int e = 64 * r + lane;
-        rest[r] = e >= take && e < queued;
+        rest[r] = (e >= take) & (e < queued);
         below[r] = e - take;
       }
-  #pragma unroll
+      int pos[4] = {0, 0, 0, 0};
+#pragma unroll
       for (int v = 0; v < 4; ++v) {
-        uint64_t todo = __ballot(cv[v]);
-        while (todo != 0ull) {
-          const int src = __ffsll(static_cast<unsigned long long>(todo)) - 1;
-          todo &= todo - 1ull;
+        const int nsrc = v < 2 ? min(take, 64) : take - 64;  // the popped lanes of register v / 2
+        for (int src = 0; src < nsrc; ++src) {
+          if (__builtin_amdgcn_readlane(static_cast<int>(cv[v]), src) == 0) continue;
           const float c_s = readlane_f(cs[v], src);
           const int c_sl = __builtin_amdgcn_readlane(csl[v], src);
-          // its place: the rest and the candidates that sort before it
-          int pos = 0;
-  #pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            pos += __popcll(__ballot(rest[r] & cand_before(qs[r], qsl[r], c_s, c_sl)));
-            below[r] += static_cast<int>(rest[r] & cand_before(c_s, c_sl, qs[r], qsl[r]));
-          }
-  #pragma unroll
-          for (int u = 0; u < 4; ++u) pos += __popcll(__ballot(cv[u] & cand_before(cs[u], csl[u], c_s, c_sl)));
-          if ((lane == src) & (pos < cap)) {
-            x_score[pos] = cs[v];
-            x_slot[pos] = csl[v];
-            x_meta[pos] = cm[v];
-            x_ps[pos] = cp[v];
-          }
+#pragma unroll
+          for (int r = 0; r < 2; ++r) below[r] += static_cast<int>(cand_before(c_s, c_sl, qs[r], qsl[r]));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) pos[u] += static_cast<int>(cand_before(c_s, c_sl, cs[u], csl[u]));
         }
       }
-  #pragma unroll
+      for (int j = take; j < queued; ++j) {
+        const float q0 = readlane_f(qs[0], j & 63), q1 = readlane_f(qs[1], j & 63);
+        const int l0 = __builtin_amdgcn_readlane(qsl[0], j & 63), l1 = __builtin_amdgcn_readlane(qsl[1], j & 63);
+        const float q_s = j < 64 ? q0 : q1;
+        const int q_sl = j < 64 ? l0 : l1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pos[u] += static_cast<int>(cand_before(q_s, q_sl, cs[u], csl[u]));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (cv[u] & (pos[u] < cap)) {
+          x_score[pos[u]] = cs[u];
+          x_slot[pos[u]] = csl[u];
+          x_meta[pos[u]] = cm[u];
+          x_ps[pos[u]] = cp[u];
+        }
+      }
+#pragma unroll
       for (int r = 0; r < 2; ++r) {
-        if (rest[r] && below[r] < cap) {
+        if (rest[r] & (below[r] < cap)) {
           x_score[below[r]] = qs[r];
           x_slot[below[r]] = qsl[r];
           x_meta[below[r]] = qm[r];
