@@ -11,9 +11,9 @@
 //
 // Two kernels.  draft_topk_kernel: per (sequence, depth) row of draft logits,
 // the log-sum-exp over the vocabulary (fp64) and the K largest logits (ties
-// to the lower token id), in one pass (an HBM stream).  tree_build_kernel: one wave
-// per sequence runs the queue in LDS; a candidate's push counter is its slot
-// in the pool, so "equal scores in push order" is "equal scores, lower slot".
+// to the lower token id), in one pass (an HBM stream).  tree_build_kernel: one
+// wave per sequence runs the queue in registers; a candidate's push counter is
+// its slot, so "equal scores in push order" is "equal scores, lower slot".
 #include "tv_internal.h"
 
 namespace tv {
@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kTopkThreads = 512;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kKMax = TV_TREE_MAX_TOPK;  // per-thread candidate list length
+constexpr int kKMax = TV_TREE_MAX_TOPK;  // longest wave list (lanes 0 .. K - 1)
 
 // order of the top-k selection: larger value first, then lower index
 // (bitwise operators: straight-line compares, no short-circuit branches)
